@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Batch-1 decode throughput of the Llama-architecture decoder step on one MI355X, plus roofline.
+
+Workload (the metric's main line): the Llama-3.1-8B-shaped decoder (random-init bf16 weights, F32
+arithmetic, bf16 KV cache, MaxSeq 8192) with positions 0..7935 pre-filled with seeded random K/V, then
+K greedy decode steps at positions 7936, 7937, ... (K = 256 covers the whole cache).  A step is one
+call of llama_decode_step: embedding, 32 layers, final norm, LM head, argmax; the argmax feeds the next
+step on the device.  The 1.7B shape (F32, 512-token prompt, 512 decode steps) is measured alongside.
+
+Timing: W untimed warm-up steps, then K steps between two HIP events on the library's stream (with a
+device synchronisation on both sides).  A second, profiled pass of the same steps records HIP events
+around every launch (llama_profile_*) and gives the dominant kernel's average launch time for the
+roofline.  The CPU oracle is timed on the host on a bounded sample of the same workload.
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+METRIC = "decode tokens/sec at batch 1 (1.7B & 8B shapes) + % of HBM roofline"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def layer_weight_bytes(cfg):
+    d, kw, f = cfg.dim, cfg.kvw, cfg.f
+    return (2 * d + 2 * d * d + 2 * kw * d + 3 * f * d) * cfg.wbytes
+
+
+def token_bytes(cfg, t):
+    """Algorithmic HBM bytes of one decode step at position t: every layer matrix and gain, the final
+    norm, the LM head (the embedding when tied), one embedding row, K/V rows 0..t-1 read of every layer
+    and the K/V row written at t.  Activations are not counted."""
+    b = cfg.layers * layer_weight_bytes(cfg) + cfg.dim * cfg.wbytes
+    b += cfg.vocab * cfg.dim * cfg.wbytes  # LM head
+    b += cfg.dim * cfg.wbytes  # one embedding row
+    kvrow = cfg.kvw * cfg.kvbytes
+    b += cfg.layers * 2 * kvrow * t  # positions 0..t-1 read (t itself comes from the append)
+    b += cfg.layers * 2 * kvrow  # the append at t
+    return b
+
+
+def kernel_bytes(cfg, cls, t=None):
+    """Algorithmic bytes of one launch of a kernel class (weights + gains + input + output vectors)."""
+    d, kw, f, wb = cfg.dim, cfg.kvw, cfg.f, cfg.wbytes
+    if cls == "gate_up":
+        return 2 * f * d * wb + d * wb + d * 4 + f * 4
+    if cls == "down":
+        return d * f * wb + f * 4 + 2 * d * 4
+    if cls == "qkv":
+        return (d + 2 * kw) * d * wb + d * wb + d * 4 + (d + 2 * kw) * 4
+    if cls == "o_proj":
+        return d * d * wb + d * 4 + 2 * d * 4
+    if cls == "lm_head":
+        return cfg.vocab * d * wb + d * wb + d * 4 + cfg.vocab * 4
+    if cls == "attention":
+        return 2 * kw * cfg.kvbytes * (t + 1) + (d + 2 * kw) * 4 + d * 4
+    raise KeyError(cls)
+
+
+def build_model(cfg, lm, synth, max_seq, fill, keep_host):
+    import numpy as np
+    import torch
+    t0 = time.time()
+    w = synth.make_weights(cfg)
+    log(f"{cfg.name}: weights generated in {time.time() - t0:.1f}s")
+    dec = lm.Decoder(cfg, w, rows=1, max_seq=max_seq)
+    log(f"{cfg.name}: weights on device ({dec.w.nbytes() / 1e9:.2f} GB)")
+    kc = vc = None
+    if fill:
+        kt = np.float32 if cfg.kvdtype == "f32" else np.uint16
+        shape = (cfg.layers, 1, cfg.kv, max_seq, cfg.head)
+        kc = np.zeros(shape, dtype=kt)
+        vc = np.zeros(shape, dtype=kt)
+        synth.fill_cache_rows(cfg, kc, vc, 0, fill)
+        for host, devt in ((kc, dec.kv.k), (vc, dec.kv.v)):
+            if host.dtype == np.uint16:
+                devt.view(torch.int16).copy_(torch.from_numpy(host.view(np.int16)))
+            else:
+                devt.copy_(torch.from_numpy(host))
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: cache rows 0..{fill - 1} filled")
+    if not keep_host:
+        w = None
+    return dec, w, kc, vc
+
+
+def time_decode(dec, cfg, p0, steps, warmup, first_tok, profile=False):
+    import torch
+    lm = sys.modules["llama_architecture_decoder_amd"]
+    tok = torch.tensor([first_tok], dtype=torch.int32, device="cuda")
+    logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        dec.decode(tok, [p0 + i], logits, tok)
+    torch.cuda.synchronize()
+    tok.fill_(first_tok)
+    torch.cuda.synchronize()
+    if profile:
+        lm.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        dec.decode(tok, [p0 + i], logits, tok)
+    e1.record()
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    if dec.status() != 0:
+        raise RuntimeError("device status flag set during the timed steps")
+    prof = {}
+    if profile:
+        for name, cls in lm.KERNEL_CLASSES.items():
+            n, ms = lm.profile_read(cls)
+            prof[name] = (n, ms)
+        lm.profile_enable(False)
+    return e0.elapsed_time(e1), (h1 - h0) * 1e3, prof
+
+
+def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
+    import numpy as np
+    import oracle
+    om = oracle.Model(cfg, w, rows=1, max_seq=kc.shape[3], alloc_cache=False)
+    om.kc, om.vc = kc, vc
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    tok, n, t0 = first_tok, 0, time.perf_counter()
+    while True:
+        tok, _, _, _ = om.decode(tok, p0 + n)
+        n += 1
+        el = time.perf_counter() - t0
+        log(f"oracle step {n} at position {p0 + n - 1}: {el:.1f}s")
+        if el >= budget_s:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg.name}: first {n} greedy decode steps at positions {p0}..{p0 + n - 1} "
+                      f"(same weights and pre-filled cache as the GPU run), {el:.1f}s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures the single-GPU decode step "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import llama_architecture_decoder_amd as lm
+    import synth
+    from synth import configs
+
+    torch.cuda.set_device(0)
+    cfg = configs.LLAMA31_8B
+    p0 = cfg.kv_fill
+    steps = max(1, min(args.steps, cfg.max_seq - p0))
+    want_cpu = not args.no_cpu_baseline
+    dec, w, kc, vc = build_model(cfg, lm, synth, cfg.max_seq, p0, keep_host=want_cpu)
+    first = int(synth.tokens(cfg, "bench/first", 1)[0])
+
+    log(f"timed: {steps} steps at positions {p0}..{p0 + steps - 1} after {args.warmup} warm-up steps")
+    ev_ms, host_ms, _ = time_decode(dec, cfg, p0, steps, args.warmup, first)
+    ms_step = ev_ms / steps
+    tok_s = 1e3 / ms_step
+    log(f"{tok_s:.1f} tok/s ({ms_step:.3f} ms/step; host clock {host_ms / steps:.3f} ms/step)")
+    log("profiled pass (events around every launch)")
+    pev_ms, _, prof = time_decode(dec, cfg, p0, steps, 0, first, profile=True)
+    mean_t = p0 + (steps - 1) / 2.0
+    bytes_tok = sum(token_bytes(cfg, p0 + i) for i in range(steps)) / steps
+    hbm_frac = bytes_tok / (ms_step * 1e-3) / HBM_PEAK
+
+    kernels = {}
+    for name, (n, ms) in prof.items():
+        if n == 0:
+            continue
+        per = ms / n
+        kb = kernel_bytes(cfg, name, int(mean_t)) if name != "embed" else None
+        kernels[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(ms / pev_ms, 4),
+                         "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
+    dom = "gate_up"
+    n, ms = prof[dom]
+    avg_s = ms / n * 1e-3
+    ach = kernel_bytes(cfg, dom) / avg_s
+    roofline = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK, 4), "traffic": None, "kernel": "k_gemv<bf16, SwiGLU> (gate+up)",
+                "bytes_per_launch": kernel_bytes(cfg, dom), "avg_launch_us": round(avg_s * 1e6, 3)}
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama31_8b-shaped decode, batch 1, bf16 weights and KV, F32 arithmetic, "
+                               f"positions {p0}..{p0 + steps - 1} of MaxSeq {cfg.max_seq} (0..{p0 - 1} "
+                               f"pre-filled random)", "batch": 1, "positions": [p0, p0 + steps - 1],
+                   "max_seq": cfg.max_seq, "hidden": cfg.dim, "layers": cfg.layers, "vocab": cfg.vocab},
+        "hbm_fraction": round(hbm_frac, 4), "bytes_per_token": int(bytes_tok),
+        "host_ms_per_step": round(host_ms / steps, 4),
+        "roofline": roofline, "kernels": kernels,
+    }
+    del dec
+    torch.cuda.empty_cache()
+
+    if want_cpu:
+        log(f"cpu baseline: oracle on {cfg.name}, ~{args.cpu_seconds:.0f}s sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, kc, vc, p0, first, args.cpu_seconds)
+    w = kc = vc = None
+
+    if not args.no_secondary:
+        c3 = configs.SMOLLM2_1_7B
+        dec3, _, _, _ = build_model(c3, lm, synth, c3.max_seq, 0, keep_host=False)
+        prompt = torch.from_numpy(synth.tokens(c3, "bench/prompt", c3.prompt_len)).cuda()
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        dec3.prefill(prompt, pos0=0, next_tok=nxt)
+        torch.cuda.synchronize()
+        s3 = c3.decode_steps
+        ev3, _, _ = time_decode(dec3, c3, c3.prompt_len, s3, args.warmup, int(nxt.item()))
+        ms3 = ev3 / s3
+        b3 = sum(token_bytes(c3, c3.prompt_len + i) for i in range(s3)) / s3
+        result["secondary"] = {"workload": f"smollm2_1_7b-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
+                                           f"then {s3} steps at positions {c3.prompt_len}..{c3.prompt_len + s3 - 1}",
+                               "value": round(1e3 / ms3, 2), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
+                               "dtype": "f32", "hbm_fraction": round(b3 / (ms3 * 1e-3) / HBM_PEAK, 4),
+                               "bytes_per_token": int(b3)}
+        log(f"1.7B: {1e3 / ms3:.1f} tok/s")
+        del dec3
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

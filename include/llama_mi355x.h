@@ -1,0 +1,203 @@
+/*
+ * llama_mi355x.h — C ABI of the MI355X (gfx950) Llama-architecture decoder step.
+ *
+ * What it computes.  One decoder step of a Llama-architecture model: per layer RMSNorm, the Q/K/V
+ * projections, RoPE (a head of 2*half numbers, number i rotated with number i + half, with optional
+ * llama3 three-band frequency rescaling), a KV-cache append at the token's position, causal
+ * grouped-query attention over positions 0..t (query head j*g + i reads key/value head j), the O
+ * projection with its residual, RMSNorm, a SwiGLU MLP with its residual; then the final RMSNorm, the
+ * tied or untied LM head and a greedy argmax (first index of the largest logit).
+ *   Sources: bend-ml-llama@0.2.1.0 main.bend — "The configuration" (Cfg), "The numeric pieces"
+ *   (rmsnorm, inv_freq, rope, silu), "The key/value cache in flat arrays" (KV.push), "Grouped-query
+ *   attention" (gqa_head, causal), "A layer" (block), "The model" (forward, forward_pre, argmax);
+ *   the Llama 3.1 8B Instruct model card (nest) — README (llama3 rope rule, untied head, entries
+ *   decode / prefill / decode_rows) and rope.linnet `tables`.
+ *
+ * Conventions for every call.
+ *   - Pointers are DEVICE pointers unless the name ends in _host.  The caller owns every buffer
+ *     (weights, caches, workspace, outputs) and the stream; the library never allocates or frees
+ *     device memory and keeps no pointer after a call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) unless stated.
+ *   - Host-checkable errors are reported BEFORE anything is enqueued, so on error nothing is
+ *     written (no cache slot, no output).  Token ids that live in device memory are range-checked
+ *     by the kernels: an out-of-range id sets a sticky flag read by llama_status() and that row's
+ *     outputs are not meaningful (its embedding is taken as zeros).
+ *   - Positions: pos is the 0-based position of the token, i.e. the number of positions the cache
+ *     row already holds.  A decode step writes K/V at pos and attends over 0..pos.
+ *   - Not thread-safe for concurrent calls that share a workspace or a cache row.
+ */
+#ifndef LLAMA_MI355X_H
+#define LLAMA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage types of weights and caches (arithmetic is always F32) */
+enum { LLAMA_F32 = 0, LLAMA_BF16 = 1 };
+
+/* return codes */
+enum {
+  LLAMA_OK = 0,
+  LLAMA_E_CONFIG = -1,      /* a size <= 0, eps or theta <= 0 or not finite, bad rope constants, bad dtype */
+  LLAMA_E_POS = -2,         /* pos < 0, pos >= max_seq, pos0 + S > max_seq (main.bend kv_room) */
+  LLAMA_E_TOKEN = -3,       /* a token id outside [0, vocab) (sticky device flag, see llama_status) */
+  LLAMA_E_SHAPE = -4,       /* B <= 0, B > cache rows or workspace batch, row out of range, S <= 0, cache
+                               bound to another shape, S > workspace prefill capacity */
+  LLAMA_E_NULL = -5,        /* a required pointer is NULL */
+  LLAMA_E_WORKSPACE = -6,   /* workspace too small, not initialised, or initialised for another config */
+  LLAMA_E_HIP = -7,         /* a HIP runtime call or launch failed */
+  LLAMA_E_UNSUPPORTED = -8  /* valid but not built: head not in {64,128}, g not in {1,2,3,4,8}, dim or f not a
+                               multiple of 8 or too wide, max_seq > 131072 */
+};
+
+/*
+ * Model config.  Cfg{kv, g, half, f, layers, vocab, eps, theta} (main.bend "The configuration"):
+ * kv key/value heads, g query heads per key/value head, half = half a head (head = 2*half),
+ * f the MLP inner width.  Derived: heads = kv*g, dim = heads*head, kvw = kv*head.
+ * rope_llama3 = 1 applies the llama3 rescale of the frequency table (nest rope.linnet `tables`):
+ * wavelength > original/low_freq_factor -> frequency/factor; wavelength < original/high_freq_factor ->
+ * unchanged; otherwise the linear blend (1 - s)*f/factor + s*f.  tied_lm_head = 1 uses the
+ * embedding as the LM head (main.bend head_of); 0 uses a separate lm_head matrix (nest card).
+ * Supported: head in {64, 128}; dim and f multiples of 8.
+ */
+typedef struct llama_cfg {
+  int32_t kv, g, half, f, layers, vocab;
+  float eps, theta;
+  int32_t rope_llama3;
+  float rope_factor, rope_low_freq_factor, rope_high_freq_factor;
+  int32_t rope_original_max_pos;
+  int32_t tied_lm_head;
+  int32_t weight_dtype; /* LLAMA_F32 | LLAMA_BF16: every weight, gain, the embedding and the LM head */
+  int32_t kv_dtype;     /* LLAMA_F32 | LLAMA_BF16: the cache (F32 -> bf16 rounds to nearest even) */
+} llama_cfg;
+
+/* One layer's weights (main.bend type LW), row = output as PyTorch stores them:
+ * ln1 [dim], wq [dim][dim], wk [kvw][dim], wv [kvw][dim], wo [dim][dim], ln2 [dim],
+ * w_gate [f][dim], w_up [f][dim], w_down [dim][f].  Rows must start 16-byte aligned (true when
+ * dim and f are multiples of 8 and each matrix starts 16-byte aligned). */
+typedef struct llama_layer_w {
+  const void *ln1, *wq, *wk, *wv, *wo, *ln2, *w_gate, *w_up, *w_down;
+} llama_layer_w;
+
+typedef struct llama_weights {
+  const void *emb;              /* [vocab][dim]; also the LM head when tied */
+  const void *lm_head;          /* [vocab][dim]; NULL iff cfg.tied_lm_head */
+  const void *final_norm;       /* [dim] */
+  const llama_layer_w *layers;  /* HOST array of cfg.layers entries, each holding device pointers */
+} llama_weights;
+
+/*
+ * A KV cache bound to caller memory: one K array and one V array per (layer, row, kv head), position
+ * p of head j at [p*head, (p+1)*head) (main.bend "The key/value cache in flat arrays"; the nest card's
+ * cache_k/cache_v [Batch][KvHeads][MaxSeq][head] per layer).  Layout of k and v:
+ * [layers][rows][kv][max_seq][head] in cfg.kv_dtype.  The cache needs no clearing: decoding never
+ * reads past a row's own position.
+ */
+typedef struct llama_kv {
+  void *k, *v;
+  int32_t rows, max_seq;
+  int32_t layers, kv, head, dtype; /* copied from the config by kv_cache_alloc, checked on use */
+} llama_kv;
+
+/* A workspace bound by llama_workspace_init: device scratch (activations, split-attention partials,
+ * counters, the rope cos/sin table, the status flag) for batches up to max_batch, positions up to
+ * max_seq and prompts up to max_prefill tokens.  Fill it only through llama_workspace_init. */
+typedef struct llama_ws {
+  void *base;
+  size_t bytes;
+  int32_t max_batch, max_seq, max_prefill;
+  uint32_t cfg_key;  /* fingerprint of the config it was initialised for */
+  uint32_t magic;
+} llama_ws;
+
+/* Bytes of ONE of the two cache arrays (K or V) for `rows` rows of max_seq positions; < 0 on error. */
+int64_t llama_kv_cache_bytes(const llama_cfg *c, int32_t rows, int32_t max_seq);
+
+/* Validate caller memory (k_mem, v_mem, each >= llama_kv_cache_bytes) and fill *out.  Writes no device
+ * memory.  Errors: E_NULL, E_CONFIG, E_SHAPE (rows or max_seq <= 0), E_WORKSPACE (bytes_each too small). */
+int kv_cache_alloc(const llama_cfg *c, int32_t rows, int32_t max_seq, void *k_mem, void *v_mem, size_t bytes_each,
+                   llama_kv *out);
+
+/* Bytes of workspace for the given capacities; < 0 on error. */
+int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill);
+
+/* Bind `mem` (>= llama_workspace_bytes) as a workspace: clears its counters and status flag and uploads
+ * the rope cos/sin table for positions 0..max_seq-1 (angle t*inv_freq[i] rounded to F32, then cos, sin;
+ * main.bend rot_at).  Synchronous: returns after the stream has finished the upload. */
+int llama_workspace_init(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill, void *mem,
+                         size_t bytes, void *stream, llama_ws *out);
+
+/*
+ * One decode step for B cache rows (main.bend forward; nest decode / decode_rows): batch entry b takes
+ * token tokens[b] at position pos_host[b] of cache row b (rows 0..B-1).  Writes K/V of every layer at
+ * that position, then (if logits != NULL) logits[b][vocab] F32 and (if next != NULL) next[b] = the
+ * first index of the largest logit.  tokens: device int32 [B]; may alias next (greedy feeding).
+ * Errors (nothing enqueued): E_NULL, E_CONFIG, E_SHAPE (B <= 0, B > kv->rows, B > ws->max_batch,
+ * cache shape differs from the config), E_POS (pos < 0 or >= kv->max_seq or >= ws->max_seq),
+ * E_WORKSPACE, E_HIP.
+ */
+int llama_decode_step(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                      const int32_t *pos_host, int32_t B, float *logits, int32_t *next, const llama_ws *ws,
+                      void *stream);
+
+/*
+ * The same step with a per-layer trace of intermediates for divergence bisection (B = 1 only).
+ * trace: device F32 [layers][4*dim + 2*kvw + f] holding, per layer, in order: q [dim], k [kvw], v [kvw]
+ * (projections before RoPE), attn [dim] (attention output), x1 [dim] (after the O projection and its
+ * residual), m [f] (SwiGLU output), y [dim] (layer output) — main.bend type Act's q, k, v, attn, m, y.
+ * trace_floats must be >= llama_trace_floats(c).
+ */
+int64_t llama_trace_floats(const llama_cfg *c);
+int llama_decode_step_traced(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                             const int32_t *pos_host, float *logits, int32_t *next, const llama_ws *ws,
+                             float *trace, int64_t trace_floats, void *stream);
+
+/*
+ * A prompt of S tokens (device int32 [S]) into cache row `row` at positions pos0..pos0+S-1
+ * (main.bend forward_pre for each prompt position; nest prefill<S>(tokens, pos)), then the final norm,
+ * LM head and argmax after the last token only: logits_last [vocab] and next [1] (each optional).
+ * Decoding continues at pos0 + S.  Errors: E_SHAPE (S <= 0, row outside the cache, S > ws->max_prefill
+ * when the batched path is used), E_POS (pos0 < 0, pos0 + S > max_seq), plus those of decode.
+ */
+int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, int32_t row, const int32_t *tokens,
+                  int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream);
+
+/*
+ * Final RMSNorm + LM head + argmax of B hidden states (device F32 [B][dim], the last layer's output
+ * before the final norm): main.bend head_of and argmax.  logits [B][vocab] optional, argmax [B] required.
+ */
+int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidden, int32_t B, float *logits,
+                   int32_t *argmax, const llama_ws *ws, void *stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, every kernel launch of the calls above is bracketed
+ * by two HIP events recorded on the call's stream, grouped by kernel class; llama_profile_read waits
+ * for the recorded events and returns the number of launches of one class and their summed elapsed
+ * milliseconds since the last llama_profile_enable.  Events are created by the library on first use
+ * and kept until the process ends; no device memory is allocated.  Not thread-safe.
+ */
+enum {
+  LLAMA_K_EMBED = 0, LLAMA_K_QKV = 1, LLAMA_K_ATTN = 2, LLAMA_K_O = 3, LLAMA_K_GATE_UP = 4, LLAMA_K_DOWN = 5,
+  LLAMA_K_LM_HEAD = 6
+};
+int llama_profile_enable(int on);
+int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms);
+
+/* Synchronise `stream` and return the sticky device-side status (LLAMA_OK or LLAMA_E_TOKEN), then clear it. */
+int llama_status(const llama_ws *ws, void *stream);
+
+/* Static description of a return code. */
+const char *llama_strerror(int code);
+
+/* Version of the library ABI (this header): 1. */
+int llama_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLAMA_MI355X_H */

@@ -1,0 +1,650 @@
+// Host side of the C ABI (include/llama_mi355x.h): argument checks, workspace layout, the rope
+// cos/sin table, and the launch sequence of one decoder step.
+//
+// Step order (main.bend "A layer" block and "The model" forward; nest attention.linnet `decode`):
+//   embed -> per layer [ rmsnorm+QKV GEMV -> RoPE+append+attention -> O GEMV + residual ->
+//   rmsnorm+gate/up GEMV + SwiGLU -> down GEMV + residual ] -> rmsnorm + LM head GEMV + argmax.
+// Every check that the host can make happens before the first launch, so an error leaves the caches
+// and outputs untouched (main.bend's room proof before KV.push; needle's validation before use).
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "common.h"
+
+using namespace lm;
+
+namespace {
+
+constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
+
+struct Tun {
+  int gemv_grid = 1024;      // cap on GEMV blocks (they walk row groups with a grid stride)
+  int attn_target = 1024;    // wanted attention blocks per launch (sets the chunk length)
+  Tun() {
+    if (const char *e = getenv("LLAMA_GEMV_GRID")) gemv_grid = atoi(e) > 0 ? atoi(e) : gemv_grid;
+    if (const char *e = getenv("LLAMA_ATTN_BLOCKS")) attn_target = atoi(e) > 0 ? atoi(e) : attn_target;
+  }
+};
+const Tun &tun() {
+  static Tun t;
+  return t;
+}
+
+struct Dims {
+  int64_t head, heads, dim, kvw, f, vocab, layers, kv, g, half;
+  int wb, kb;
+};
+
+Dims dims_of(const llama_cfg *c) {
+  Dims d;
+  d.kv = c->kv;
+  d.g = c->g;
+  d.half = c->half;
+  d.head = 2 * (int64_t)c->half;
+  d.heads = (int64_t)c->kv * c->g;
+  d.dim = d.heads * d.head;
+  d.kvw = (int64_t)c->kv * d.head;
+  d.f = c->f;
+  d.vocab = c->vocab;
+  d.layers = c->layers;
+  d.wb = c->weight_dtype == LLAMA_BF16 ? 2 : 4;
+  d.kb = c->kv_dtype == LLAMA_BF16 ? 2 : 4;
+  return d;
+}
+
+int check_cfg(const llama_cfg *c) {
+  if (!c) return LLAMA_E_NULL;
+  if (c->kv <= 0 || c->g <= 0 || c->half <= 0 || c->f <= 0 || c->layers <= 0 || c->vocab <= 0) return LLAMA_E_CONFIG;
+  if (!(c->eps > 0.f) || !isfinite(c->eps) || !(c->theta > 0.f) || !isfinite(c->theta)) return LLAMA_E_CONFIG;
+  if ((c->weight_dtype != LLAMA_F32 && c->weight_dtype != LLAMA_BF16) ||
+      (c->kv_dtype != LLAMA_F32 && c->kv_dtype != LLAMA_BF16))
+    return LLAMA_E_CONFIG;
+  if (c->rope_llama3 != 0 && c->rope_llama3 != 1) return LLAMA_E_CONFIG;
+  if (c->tied_lm_head != 0 && c->tied_lm_head != 1) return LLAMA_E_CONFIG;
+  if (c->rope_llama3) {
+    if (!(c->rope_factor > 0.f) || !(c->rope_low_freq_factor > 0.f) ||
+        !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_original_max_pos <= 0)
+      return LLAMA_E_CONFIG;
+  }
+  const Dims d = dims_of(c);
+  if (d.dim > (1 << 20) || d.f > (1 << 22) || d.layers > 4096 || d.vocab > (1 << 26)) return LLAMA_E_CONFIG;
+  // what this build implements
+  if (!attention_supported((int)d.head, c->g)) return LLAMA_E_UNSUPPORTED;
+  if (d.dim % 8 || d.f % 8) return LLAMA_E_UNSUPPORTED;
+  if (!gemv_supported(c->weight_dtype, (int)d.dim) || !gemv_supported(c->weight_dtype, (int)d.f))
+    return LLAMA_E_UNSUPPORTED;
+  return LLAMA_OK;
+}
+
+uint32_t cfg_key(const llama_cfg *c) {
+  // FNV-1a over the fields (not the padding)
+  uint32_t h = 0x811c9dc5u;
+  auto mix = [&](const void *p, size_t n) {
+    const unsigned char *b = (const unsigned char *)p;
+    for (size_t i = 0; i < n; ++i) {
+      h ^= b[i];
+      h *= 0x01000193u;
+    }
+  };
+  mix(&c->kv, 6 * sizeof(int32_t));
+  mix(&c->eps, sizeof(float));
+  mix(&c->theta, sizeof(float));
+  mix(&c->rope_llama3, sizeof(int32_t));
+  mix(&c->rope_factor, 3 * sizeof(float));
+  mix(&c->rope_original_max_pos, sizeof(int32_t));
+  mix(&c->tied_lm_head, 3 * sizeof(int32_t));
+  return h;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t status, attn_cnt, lm_cnt, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, total;
+  int nch;
+};
+
+WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill) {
+  (void)max_prefill;
+  const Dims d = dims_of(c);
+  WsLayout L;
+  L.nch = (int)((max_seq + kAttnChunkMin - 1) / kAttnChunkMin);
+  if (L.nch > kAttnMaxChunks) L.nch = kAttnMaxChunks;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.status = take(64);
+  L.attn_cnt = take(sizeof(int) * (size_t)max_batch * d.kv);
+  L.lm_cnt = take(sizeof(int) * (size_t)max_batch);
+  L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
+  L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
+  L.x = take(sizeof(float) * (size_t)max_batch * d.dim);
+  L.qkv = take(sizeof(float) * (size_t)max_batch * (d.dim + 2 * d.kvw));
+  L.attn = take(sizeof(float) * (size_t)max_batch * d.dim);
+  L.m = take(sizeof(float) * (size_t)max_batch * d.f);
+  L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
+  L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
+  L.lm_v = take(sizeof(float) * (size_t)max_batch * kLmGridMax);
+  L.lm_i = take(sizeof(int) * (size_t)max_batch * kLmGridMax);
+  L.total = o;
+  return L;
+}
+
+// inv_freq[i] = 1 / theta^(2i / head) (main.bend inv_freq), then the llama3 band rescale in the order
+// nest rope.linnet `tables` prints it.  Plain F32 host arithmetic, no contraction.
+void host_inv_freq(const llama_cfg *c, float *inv) {
+#pragma clang fp contract(off)
+  const float hd = (float)(2 * c->half);
+  const float PI = 3.14159265f;
+  const float orig = (float)c->rope_original_max_pos;
+  for (int i = 0; i < c->half; ++i) {
+    const float base = 1.0f / powf(c->theta, (float)(2 * i) / hd);
+    if (!c->rope_llama3) {
+      inv[i] = base;
+      continue;
+    }
+    const float wavelen = (2.0f * PI) / base;
+    const float low_wl = orig / c->rope_low_freq_factor;
+    const float high_wl = orig / c->rope_high_freq_factor;
+    const float smooth = (orig / wavelen - c->rope_low_freq_factor) / (c->rope_high_freq_factor - c->rope_low_freq_factor);
+    const float scaled = base / c->rope_factor;
+    const float t1 = (1.0f - smooth) * scaled;
+    const float t2 = smooth * base;
+    const float blended = t1 + t2;
+    inv[i] = (wavelen > low_wl) ? scaled : ((wavelen < high_wl) ? base : blended);
+  }
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? LLAMA_OK : LLAMA_E_HIP; }
+
+// Opt-in kernel timing (llama_profile_enable): HIP events recorded on the caller's stream around
+// every launch of a step, grouped by kernel class, read back by llama_profile_read.
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Prof &prof() {
+  static Prof p;
+  return p;
+}
+struct ProfScope {
+  int cls;
+  hipStream_t s;
+  hipEvent_t e0 = nullptr;
+  ProfScope(int c, hipStream_t st) : cls(c), s(st) {
+    if (prof().on && (e0 = prof().get())) hipEventRecord(e0, s);
+  }
+  ~ProfScope() {
+    if (!e0) return;
+    hipEvent_t e1 = prof().get();
+    if (!e1) return;
+    hipEventRecord(e1, s);
+    prof().marks.push_back({cls, {e0, e1}});
+  }
+};
+
+int check_ws(const llama_cfg *c, const llama_ws *ws) {
+  if (!ws || !ws->base) return LLAMA_E_NULL;
+  if (ws->magic != kWsMagic || ws->cfg_key != cfg_key(c)) return LLAMA_E_WORKSPACE;
+  if (ws->max_batch <= 0 || ws->max_seq <= 0 || ws->max_prefill < 0) return LLAMA_E_WORKSPACE;
+  if (ws_layout(c, ws->max_batch, ws->max_seq, ws->max_prefill).total > ws->bytes) return LLAMA_E_WORKSPACE;
+  return LLAMA_OK;
+}
+
+int check_weights(const llama_cfg *c, const llama_weights *w) {
+  if (!w || !w->emb || !w->final_norm || !w->layers) return LLAMA_E_NULL;
+  if (!c->tied_lm_head && !w->lm_head) return LLAMA_E_NULL;
+  for (int l = 0; l < c->layers; ++l) {
+    const llama_layer_w &L = w->layers[l];
+    if (!L.ln1 || !L.wq || !L.wk || !L.wv || !L.wo || !L.ln2 || !L.w_gate || !L.w_up || !L.w_down) return LLAMA_E_NULL;
+    const void *ps[] = {L.ln1, L.wq, L.wk, L.wv, L.wo, L.ln2, L.w_gate, L.w_up, L.w_down};
+    for (const void *p : ps)
+      if (((uintptr_t)p) & 15u) return LLAMA_E_SHAPE;
+  }
+  if (((uintptr_t)w->emb & 15u) || ((uintptr_t)w->final_norm & 15u)) return LLAMA_E_SHAPE;
+  if (w->lm_head && ((uintptr_t)w->lm_head & 15u)) return LLAMA_E_SHAPE;
+  return LLAMA_OK;
+}
+
+int check_kv(const llama_cfg *c, const llama_kv *kv) {
+  if (!kv || !kv->k || !kv->v) return LLAMA_E_NULL;
+  const Dims d = dims_of(c);
+  if (kv->layers != c->layers || kv->kv != c->kv || kv->head != d.head || kv->dtype != c->kv_dtype ||
+      kv->rows <= 0 || kv->max_seq <= 0)
+    return LLAMA_E_SHAPE;
+  return LLAMA_OK;
+}
+
+struct Ctx {
+  const llama_cfg *c;
+  Dims d;
+  const llama_weights *w;
+  const llama_kv *kv;
+  const llama_ws *ws;
+  WsLayout L;
+  hipStream_t s;
+  char *base;
+  template <typename T>
+  T *at(size_t off) const {
+    return reinterpret_cast<T *>(base + off);
+  }
+};
+
+void *layer_cache(const Ctx &x, void *cache, int l) {
+  const size_t per_layer = (size_t)x.kv->rows * x.d.kv * (size_t)x.kv->max_seq * x.d.head * x.d.kb;
+  return (char *)cache + per_layer * (size_t)l;
+}
+
+// LM head of batch entry b: logits (nullable) and next (nullable) from hidden h
+int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *next) {
+  GemvArgs a = {};
+  a.x = h;
+  a.gain = x.w->final_norm;
+  a.eps = x.c->eps;
+  a.w[0] = x.c->tied_lm_head ? x.w->emb : x.w->lm_head;
+  a.rs[0] = 0;
+  a.rs[1] = a.rs[2] = a.rs[3] = (int)x.d.vocab;
+  a.N = (int)x.d.vocab;
+  a.K = (int)x.d.dim;
+  a.y = logits;
+  a.part_v = x.at<float>(x.L.lm_v) + (size_t)b * kLmGridMax;
+  a.part_i = x.at<int>(x.L.lm_i) + (size_t)b * kLmGridMax;
+  a.counter = x.at<int>(x.L.lm_cnt) + b;
+  a.next = next;
+  ProfScope ps(LLAMA_K_LM_HEAD, x.s);
+  return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().gemv_grid, x.s));
+}
+
+// One step for B rows at positions pos[b] of cache rows row0 + b.  want_head = run the LM head.
+int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int row0, float *logits, int32_t *next,
+             bool want_head, float *trace) {
+  const Dims &d = x.d;
+  const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f;
+  const int wdt = x.c->weight_dtype;
+  float *xs = x.at<float>(x.L.x);
+  float *qkv = x.at<float>(x.L.qkv);
+  float *att = x.at<float>(x.L.attn);
+  float *mm = x.at<float>(x.L.m);
+  const int qkv_stride = H + 2 * KW;
+  int rc;
+  {
+    ProfScope ps(LLAMA_K_EMBED, x.s);
+    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, B, x.at<int>(x.L.status), x.s));
+  }
+  if (rc) return rc;
+
+  // attention chunking: enough blocks to cover the chip, chunks a multiple of 32 positions
+  int tmax = 0;
+  for (int b = 0; b < B; ++b) tmax = pos[b] > tmax ? pos[b] : tmax;
+  const int npos = tmax + 1;
+  int want = (tun().attn_target + B * (int)d.kv - 1) / (B * (int)d.kv);
+  if (want < 1) want = 1;
+  int chunk = (npos + want - 1) / want;
+  chunk = (int)align_up((size_t)(chunk < kAttnChunkMin ? kAttnChunkMin : chunk), kAttnChunkMin);
+  if ((npos + chunk - 1) / chunk > x.L.nch) chunk = (int)align_up((size_t)((npos + x.L.nch - 1) / x.L.nch), kAttnChunkMin);
+  if (chunk > kAttnChunkMax) return LLAMA_E_UNSUPPORTED;
+  const int nch_launch = (npos + chunk - 1) / chunk;
+
+  AttnArgs aa = {};
+  aa.qkv = qkv;
+  aa.qkv_stride = qkv_stride;
+  aa.kv = (int)d.kv;
+  aa.max_seq = x.kv->max_seq;
+  aa.half = (int)d.half;
+  aa.row0 = row0;
+  aa.rope_cs = x.at<float>(x.L.rope_cs);
+  aa.rope_sn = x.at<float>(x.L.rope_sn);
+  aa.out = att;
+  aa.out_stride = H;
+  aa.part_o = x.at<float>(x.L.part_o);
+  aa.part_ml = x.at<float>(x.L.part_ml);
+  aa.counter = x.at<int>(x.L.attn_cnt);
+  aa.nch = x.L.nch;
+  aa.chunk = chunk;
+  aa.scale = 1.0f / sqrtf((float)d.head);
+  for (int b = 0; b < B; ++b) aa.pos[b] = pos[b];
+
+  const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
+  for (int l = 0; l < (int)d.layers; ++l) {
+    const llama_layer_w &lw = x.w->layers[l];
+    for (int b = 0; b < B; ++b) {
+      GemvArgs a = {};
+      a.x = xs + (size_t)b * H;
+      a.gain = lw.ln1;
+      a.eps = x.c->eps;
+      a.w[0] = lw.wq;
+      a.w[1] = lw.wk;
+      a.w[2] = lw.wv;
+      a.rs[0] = 0;
+      a.rs[1] = H;
+      a.rs[2] = H + KW;
+      a.rs[3] = H + 2 * KW;
+      a.N = H + 2 * KW;
+      a.K = H;
+      a.y = qkv + (size_t)b * qkv_stride;
+      ProfScope ps(LLAMA_K_QKV, x.s);
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_STORE, true, a, tun().gemv_grid, x.s)))) return rc;
+    }
+    aa.kc = layer_cache(x, x.kv->k, l);
+    aa.vc = layer_cache(x, x.kv->v, l);
+    {
+      ProfScope ps(LLAMA_K_ATTN, x.s);
+      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
+    }
+    float *tr = trace ? trace + (size_t)l * tstride : nullptr;
+    if (tr) {
+      if ((rc = hip_rc(hipMemcpyAsync(tr, qkv, sizeof(float) * qkv_stride, hipMemcpyDeviceToDevice, x.s)))) return rc;
+      if ((rc = hip_rc(hipMemcpyAsync(tr + qkv_stride, att, sizeof(float) * H, hipMemcpyDeviceToDevice, x.s))))
+        return rc;
+    }
+    for (int b = 0; b < B; ++b) {
+      GemvArgs a = {};
+      a.x = att + (size_t)b * H;
+      a.w[0] = lw.wo;
+      a.rs[0] = 0;
+      a.rs[1] = a.rs[2] = a.rs[3] = H;
+      a.N = H;
+      a.K = H;
+      a.y = xs + (size_t)b * H;
+      a.res = xs + (size_t)b * H;
+      ProfScope ps(LLAMA_K_O, x.s);
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().gemv_grid, x.s)))) return rc;
+    }
+    if (tr && (rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + H, xs, sizeof(float) * H, hipMemcpyDeviceToDevice, x.s))))
+      return rc;
+    for (int b = 0; b < B; ++b) {
+      GemvArgs a = {};
+      a.x = xs + (size_t)b * H;
+      a.gain = lw.ln2;
+      a.eps = x.c->eps;
+      a.w[0] = lw.w_gate;
+      a.w[1] = lw.w_up;
+      a.rs[0] = 0;
+      a.rs[1] = a.rs[2] = a.rs[3] = F;
+      a.N = F;
+      a.K = H;
+      a.y = mm + (size_t)b * F;
+      ProfScope ps(LLAMA_K_GATE_UP, x.s);
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_SWIGLU, true, a, tun().gemv_grid, x.s)))) return rc;
+    }
+    for (int b = 0; b < B; ++b) {
+      GemvArgs a = {};
+      a.x = mm + (size_t)b * F;
+      a.w[0] = lw.w_down;
+      a.rs[0] = 0;
+      a.rs[1] = a.rs[2] = a.rs[3] = H;
+      a.N = H;
+      a.K = F;
+      a.y = xs + (size_t)b * H;
+      a.res = xs + (size_t)b * H;
+      ProfScope ps(LLAMA_K_DOWN, x.s);
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().gemv_grid, x.s)))) return rc;
+    }
+    if (tr) {
+      if ((rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + 2 * H, mm, sizeof(float) * F, hipMemcpyDeviceToDevice, x.s))))
+        return rc;
+      if ((rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + 2 * H + F, xs, sizeof(float) * H, hipMemcpyDeviceToDevice,
+                                      x.s))))
+        return rc;
+    }
+  }
+  if (want_head && (logits || next)) {
+    for (int b = 0; b < B; ++b) {
+      rc = run_lm_head(x, xs + (size_t)b * H, b, logits ? logits + (size_t)b * d.vocab : nullptr,
+                       next ? next + b : nullptr);
+      if (rc) return rc;
+    }
+  }
+  return LLAMA_OK;
+}
+
+int make_ctx(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const llama_ws *ws, void *stream,
+             Ctx *x) {
+  int rc;
+  if ((rc = check_cfg(c))) return rc;
+  if (w && (rc = check_weights(c, w))) return rc;
+  if (!w) return LLAMA_E_NULL;
+  if (kv && (rc = check_kv(c, kv))) return rc;
+  if ((rc = check_ws(c, ws))) return rc;
+  x->c = c;
+  x->d = dims_of(c);
+  x->w = w;
+  x->kv = kv;
+  x->ws = ws;
+  x->L = ws_layout(c, ws->max_batch, ws->max_seq, ws->max_prefill);
+  x->s = (hipStream_t)stream;
+  x->base = (char *)ws->base;
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int llama_abi_version(void) { return 1; }
+
+const char *llama_strerror(int code) {
+  switch (code) {
+    case LLAMA_OK: return "ok";
+    case LLAMA_E_CONFIG: return "invalid config";
+    case LLAMA_E_POS: return "position outside the cache";
+    case LLAMA_E_TOKEN: return "token id outside the vocabulary";
+    case LLAMA_E_SHAPE: return "shape mismatch";
+    case LLAMA_E_NULL: return "required pointer is NULL";
+    case LLAMA_E_WORKSPACE: return "workspace too small or not initialised for this config";
+    case LLAMA_E_HIP: return "HIP runtime error";
+    case LLAMA_E_UNSUPPORTED: return "not supported by this build";
+    default: return "unknown error";
+  }
+}
+
+int64_t llama_kv_cache_bytes(const llama_cfg *c, int32_t rows, int32_t max_seq) {
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if (rows <= 0 || max_seq <= 0) return LLAMA_E_SHAPE;
+  const Dims d = dims_of(c);
+  return (int64_t)d.layers * rows * d.kv * (int64_t)max_seq * d.head * d.kb;
+}
+
+int kv_cache_alloc(const llama_cfg *c, int32_t rows, int32_t max_seq, void *k_mem, void *v_mem, size_t bytes_each,
+                   llama_kv *out) {
+  if (!out || !k_mem || !v_mem) return LLAMA_E_NULL;
+  const int64_t need = llama_kv_cache_bytes(c, rows, max_seq);
+  if (need < 0) return (int)need;
+  if ((size_t)need > bytes_each) return LLAMA_E_WORKSPACE;
+  if (((uintptr_t)k_mem & 15u) || ((uintptr_t)v_mem & 15u)) return LLAMA_E_SHAPE;
+  const Dims d = dims_of(c);
+  out->k = k_mem;
+  out->v = v_mem;
+  out->rows = rows;
+  out->max_seq = max_seq;
+  out->layers = c->layers;
+  out->kv = c->kv;
+  out->head = (int32_t)d.head;
+  out->dtype = c->kv_dtype;
+  return LLAMA_OK;
+}
+
+int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill) {
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if (max_batch <= 0 || max_batch > kMaxBatch || max_seq <= 0 || max_prefill < 0) return LLAMA_E_SHAPE;
+  if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * kAttnChunkMax) return LLAMA_E_UNSUPPORTED;
+  return (int64_t)ws_layout(c, max_batch, max_seq, max_prefill).total;
+}
+
+int llama_workspace_init(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill, void *mem,
+                         size_t bytes, void *stream, llama_ws *out) {
+  if (!mem || !out) return LLAMA_E_NULL;
+  const int64_t need = llama_workspace_bytes(c, max_batch, max_seq, max_prefill);
+  if (need < 0) return (int)need;
+  if ((size_t)need > bytes) return LLAMA_E_WORKSPACE;
+  if ((uintptr_t)mem & 255u) return LLAMA_E_SHAPE;
+  const WsLayout L = ws_layout(c, max_batch, max_seq, max_prefill);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)mem;
+  int rc = hip_rc(launch_zero(base, L.rope_cs, s));  // status word and counters
+  if (rc) return rc;
+  // rope table: angle t * inv_freq[i] rounded to F32, then cos and sin (main.bend rot_at)
+  const int half = c->half;
+  std::vector<float> inv(half), cs((size_t)max_seq * half), sn((size_t)max_seq * half);
+  host_inv_freq(c, inv.data());
+  for (int t = 0; t < max_seq; ++t) {
+    for (int i = 0; i < half; ++i) {
+      const float a = (float)t * inv[i];
+      cs[(size_t)t * half + i] = cosf(a);
+      sn[(size_t)t * half + i] = sinf(a);
+    }
+  }
+  if ((rc = hip_rc(hipMemcpyAsync(base + L.rope_cs, cs.data(), sizeof(float) * cs.size(), hipMemcpyHostToDevice, s))))
+    return rc;
+  if ((rc = hip_rc(hipMemcpyAsync(base + L.rope_sn, sn.data(), sizeof(float) * sn.size(), hipMemcpyHostToDevice, s))))
+    return rc;
+  if ((rc = hip_rc(hipStreamSynchronize(s)))) return rc;
+  out->base = mem;
+  out->bytes = bytes;
+  out->max_batch = max_batch;
+  out->max_seq = max_seq;
+  out->max_prefill = max_prefill;
+  out->cfg_key = cfg_key(c);
+  out->magic = kWsMagic;
+  return LLAMA_OK;
+}
+
+int64_t llama_trace_floats(const llama_cfg *c) {
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  const Dims d = dims_of(c);
+  return d.layers * (4 * d.dim + 2 * d.kvw + d.f);
+}
+
+static int decode_common(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                         const int32_t *pos_host, int32_t B, float *logits, int32_t *next, const llama_ws *ws,
+                         void *stream, float *trace) {
+  if (!kv || !tokens || !pos_host || !w || !ws) return LLAMA_E_NULL;
+  // argument checks first (config, cache shape, batch, positions), then the bound buffers
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if (B <= 0 || B > kv->rows || B > kMaxBatch) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos_host[b] < 0 || pos_host[b] >= kv->max_seq) return LLAMA_E_POS;
+  if (logits && ((uintptr_t)logits & 3u)) return LLAMA_E_SHAPE;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if (B > ws->max_batch) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos_host[b] >= ws->max_seq) return LLAMA_E_POS;
+  return run_step(x, tokens, pos_host, B, 0, logits, next, true, trace);
+}
+
+int llama_decode_step(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                      const int32_t *pos_host, int32_t B, float *logits, int32_t *next, const llama_ws *ws,
+                      void *stream) {
+  return decode_common(c, w, kv, tokens, pos_host, B, logits, next, ws, stream, nullptr);
+}
+
+int llama_decode_step_traced(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                             const int32_t *pos_host, float *logits, int32_t *next, const llama_ws *ws, float *trace,
+                             int64_t trace_floats, void *stream) {
+  if (!trace) return LLAMA_E_NULL;
+  const int64_t need = llama_trace_floats(c);
+  if (need < 0) return (int)need;
+  if (trace_floats < need) return LLAMA_E_SHAPE;
+  return decode_common(c, w, kv, tokens, pos_host, 1, logits, next, ws, stream, trace);
+}
+
+int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, int32_t row, const int32_t *tokens,
+                  int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream) {
+  if (!kv || !tokens || !w || !ws) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if (S <= 0 || row < 0 || row >= kv->rows) return LLAMA_E_SHAPE;
+  if (pos0 < 0 || (int64_t)pos0 + S > kv->max_seq) return LLAMA_E_POS;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if ((int64_t)pos0 + S > ws->max_seq) return LLAMA_E_POS;
+  // one position after another through the decode kernels (main.bend forward_pre per prompt
+  // position); only the last runs the final norm, the LM head and the argmax
+  for (int i = 0; i < S; ++i) {
+    const int32_t p = pos0 + i;
+    const bool last = (i == S - 1);
+    rc = run_step(x, tokens + i, &p, 1, row, last ? logits_last : nullptr, last ? next : nullptr, last, nullptr);
+    if (rc) return rc;
+  }
+  return LLAMA_OK;
+}
+
+int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidden, int32_t B, float *logits,
+                   int32_t *argmax, const llama_ws *ws, void *stream) {
+  if (!hidden || !argmax) return LLAMA_E_NULL;
+  Ctx x;
+  int rc = make_ctx(c, w, nullptr, ws, stream, &x);
+  if (rc) return rc;
+  if (B <= 0 || B > ws->max_batch) return LLAMA_E_SHAPE;
+  if ((uintptr_t)hidden & 15u) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    rc = run_lm_head(x, hidden + (size_t)b * x.d.dim, b, logits ? logits + (size_t)b * x.d.vocab : nullptr, argmax + b);
+    if (rc) return rc;
+  }
+  return LLAMA_OK;
+}
+
+int llama_profile_enable(int on) {
+  Prof &p = prof();
+  p.on = on != 0;
+  p.marks.clear();
+  p.used = 0;
+  return LLAMA_OK;
+}
+
+int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms) {
+  if (!launches || !total_ms) return LLAMA_E_NULL;
+  Prof &p = prof();
+  int64_t n = 0;
+  double ms = 0.0;
+  for (auto &m : p.marks) {
+    if (m.first != kernel_class) continue;
+    if (hipEventSynchronize(m.second.second) != hipSuccess) return LLAMA_E_HIP;
+    float e = 0.f;
+    if (hipEventElapsedTime(&e, m.second.first, m.second.second) != hipSuccess) return LLAMA_E_HIP;
+    ms += e;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return LLAMA_OK;
+}
+
+int llama_status(const llama_ws *ws, void *stream) {
+  if (!ws || !ws->base) return LLAMA_E_NULL;
+  if (ws->magic != kWsMagic) return LLAMA_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int flag = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return LLAMA_E_HIP;
+  if (hipMemcpy(&flag, ws->base, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LLAMA_E_HIP;
+  if (flag) {
+    if (launch_zero(ws->base, 64, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) return LLAMA_E_HIP;
+    return LLAMA_E_TOKEN;
+  }
+  return LLAMA_OK;
+}
+
+}  // extern "C"

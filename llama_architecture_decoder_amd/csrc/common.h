@@ -1,0 +1,153 @@
+// Internal to libllama_mi355x: types, launch descriptors and device helpers shared by the kernels
+// and the host entry points.  Written for gfx950 (CDNA4): 64-lane wavefronts, 256-thread blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/llama_mi355x.h"
+
+namespace lm {
+
+constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
+constexpr int kMaxBatch = 64;   // rows of one decode call (positions travel as a kernel argument)
+constexpr int kAttnChunkMin = 32;
+constexpr int kAttnChunkMax = 512;
+constexpr int kAttnMaxChunks = 256;
+constexpr int kLmGridMax = 2048;
+
+typedef uint16_t bf16_t;  // bf16 kept as its bits; widened by a 16-bit shift (exact)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
+
+// ------------------------------------------------------------------ device helpers ----
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// F32 -> bf16 with round-to-nearest-even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// RoPE of one pair (main.bend rot_lo / rot_hi): lo' = lo*c + (-hi)*s, hi' = hi*c + lo*s, every product
+// and sum rounded on its own (no fused multiply-add), as the F32 reference evaluates it.
+__device__ __forceinline__ float rope_lo(float lo, float hi, float c, float s) {
+#pragma clang fp contract(off)
+  const float a = lo * c;
+  const float b = (-hi) * s;
+  return a + b;
+}
+__device__ __forceinline__ float rope_hi(float lo, float hi, float c, float s) {
+#pragma clang fp contract(off)
+  const float a = hi * c;
+  const float b = lo * s;
+  return a + b;
+}
+
+// 16 bytes of a row: 4 F32 or 8 bf16, widened to F32
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  static constexpr int E = 4;
+  __device__ __forceinline__ static void unpack(const u32x4 &r, float *o) {
+    o[0] = __uint_as_float(r.x);
+    o[1] = __uint_as_float(r.y);
+    o[2] = __uint_as_float(r.z);
+    o[3] = __uint_as_float(r.w);
+  }
+};
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int E = 8;
+  __device__ __forceinline__ static void unpack(const u32x4 &r, float *o) {
+    o[0] = __uint_as_float(r.x << 16);
+    o[1] = __uint_as_float(r.x & 0xffff0000u);
+    o[2] = __uint_as_float(r.y << 16);
+    o[3] = __uint_as_float(r.y & 0xffff0000u);
+    o[4] = __uint_as_float(r.z << 16);
+    o[5] = __uint_as_float(r.z & 0xffff0000u);
+    o[6] = __uint_as_float(r.w << 16);
+    o[7] = __uint_as_float(r.w & 0xffff0000u);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float load_scalar(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float load_scalar<float>(const float *p, size_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_scalar<bf16_t>(const bf16_t *p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// streamed once per step: non-temporal 16-byte load
+__device__ __forceinline__ u32x4 load_stream16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// -------------------------------------------------------------- launch descriptors ----
+
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+
+struct GemvArgs {
+  const float *x;      // input [K] (for the norm epilogues: the raw residual stream)
+  const void *gain;    // RMSNorm gains [K] in the weight type, or nullptr for a plain input
+  float eps;
+  const void *w[3];    // stacked row blocks: row r in [rs[i], rs[i+1]) reads w[i] row (r - rs[i]);
+  int rs[4];           // SWIGLU: w[0] = gate, w[1] = up, both N rows
+  int N, K;
+  float *y;            // output [N] (SWIGLU: silu(gate)*up; ARGMAX: logits, may be nullptr)
+  const float *res;    // EPI_RESID: y = res + W x (res may alias y)
+  int ngroups;         // row groups of R rows
+  // EPI_ARGMAX
+  float *part_v;
+  int *part_i;
+  int *counter;
+  int32_t *next;
+};
+
+struct AttnArgs {
+  const float *qkv;    // [B][qkv_stride]: q [dim], k [kvw], v [kvw] before RoPE
+  int qkv_stride;
+  void *kc, *vc;       // this layer's cache: [rows][kv][max_seq][head]
+  int kv, max_seq, half;
+  int row0;            // cache row of batch entry 0
+  const float *rope_cs, *rope_sn;  // [max_seq][half]
+  float *out;          // [B][dim]
+  int out_stride;
+  float *part_o;       // [B][kv][nch][g][head]
+  float *part_ml;      // [B][kv][nch][g][2]
+  int *counter;        // [B][kv], zero between calls
+  int nch;             // chunk slots per (row, kv head) in the partial arrays
+  int chunk;           // positions per chunk
+  float scale;         // 1/sqrt(head)
+  int pos[kMaxBatch];
+};
+
+// host-side launchers (one per kernel family); return hipSuccess or the launch error
+hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, int grid_cap, hipStream_t s);
+int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is instantiated
+hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int nch_launch, hipStream_t s);
+int attention_supported(int head, int g);
+hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
+                        int *status, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace lm

@@ -1,0 +1,311 @@
+// HBM-streaming matrix-vector products for the batch-1 decode step on gfx950.
+//
+// y = W x with W [N][K] row-major (row = output, main.bend type LW), F32 or bf16 weights, F32
+// arithmetic.  The projections of main.bend "A layer" (block): q/k/v from the attention norm, o with
+// the first residual, gate/up from the MLP norm with SwiGLU (silu(g) * u, silu(z) = z / (1 + e^-z)),
+// down with the second residual; and "The model" head_of: logits = W_lm * rmsnorm(x, lnf) with the
+// argmax of main.bend `argmax` (first index of the largest value).
+//
+// Layout of the work: one 256-thread block owns R consecutive rows at a time (a row group) and the
+// whole block splits K: thread t reads 16-byte chunk j*256 + t of every row of the group, so each
+// block instruction streams 4 KB of contiguous row bytes and a thread's slice of x is the same for
+// every row (x lives in registers, at most 8 chunks = 64 floats).  Blocks walk row groups with a
+// grid stride, so the per-block prologue (loading x and, for the norm variants, its sum of squares)
+// is paid once per block rather than once per group.  Each thread issues R*KCH independent 16-byte
+// loads (~16) before it uses any, which keeps ~64 KB in flight per block.
+//
+// Reduction: the R (or 2R) per-thread partial sums are reduced across the wavefront with a
+// transposing butterfly (R-1 + 6-log2 R shuffles instead of 6R), then across the 4 waves through LDS
+// in a fixed order, so results are deterministic.
+#include "common.h"
+
+namespace lm {
+
+template <int KCH, int PAIRS>
+struct RowsPerGroup {
+  static constexpr int loads = 16;
+  static constexpr int raw = loads / (KCH * PAIRS);
+  static constexpr int value = raw >= 8 ? 8 : raw >= 4 ? 4 : raw >= 2 ? 2 : 1;
+};
+
+// Reduce n = 2^k values per lane across the 64 lanes.  After the call, value index r's wave sum is in
+// v[0] of every lane whose lane id / (64 / n) == r.
+template <int n>
+__device__ __forceinline__ void wave_transpose_sum(float (&v)[n], int lane) {
+  int count = n;
+  int off = 32;
+#pragma unroll
+  for (int step = 0; step < 6; ++step) {
+    if (count > 1) {
+      const int halfc = count / 2;
+      const bool up = (lane & off) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        if (i < halfc) {
+          float send = up ? v[i] : v[i + halfc];
+          float keep = up ? v[i + halfc] : v[i];
+          v[i] = keep + __shfl_xor(send, off);
+        }
+      }
+      count = halfc;
+    } else {
+      v[0] += __shfl_xor(v[0], off);
+    }
+    off >>= 1;
+  }
+}
+template <>
+__device__ __forceinline__ void wave_transpose_sum<1>(float (&v)[1], int lane) {
+  v[0] = wave_sum(v[0]);
+}
+
+template <typename WT>
+__device__ __forceinline__ const WT *row_ptr(const GemvArgs &a, int r) {
+  int blk = (r >= a.rs[1]) + (r >= a.rs[2]);
+  return reinterpret_cast<const WT *>(a.w[blk]) + (size_t)(r - a.rs[blk]) * (size_t)a.K;
+}
+
+template <typename WT, int KCH, int EPI, bool NORM>
+__global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
+  constexpr int E = Vec16<WT>::E;
+  constexpr int PAIRS = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int R = RowsPerGroup<KCH, PAIRS>::value;
+  constexpr int NV = R * PAIRS;  // partial sums per thread per group
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunk = a.K / E;
+
+  __shared__ float red[4][NV];
+  __shared__ float ss_w[4];
+  __shared__ int is_last_s;
+
+  // ---- the input slice of this thread: chunks j*256 + tid
+  float xr[KCH][E];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int ci = j * kThreads + tid;
+    if (ci < nchunk) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        float4 v = *reinterpret_cast<const float4 *>(a.x + (size_t)ci * E + e);
+        xr[j][e + 0] = v.x;
+        xr[j][e + 1] = v.y;
+        xr[j][e + 2] = v.z;
+        xr[j][e + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) xr[j][e] = 0.f;
+    }
+    if (NORM) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += xr[j][e] * xr[j][e];
+    }
+  }
+  if (NORM) {
+    // RMSNorm prologue: g * (x * (1 / sqrt(sum(x^2) / K + eps)))
+    ss = wave_sum(ss);
+    if (lane == 0) ss_w[wave] = ss;
+    __syncthreads();
+    const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
+    const float r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
+    const WT *g = reinterpret_cast<const WT *>(a.gain);
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int ci = j * kThreads + tid;
+      if (ci < nchunk) {
+        float gv[E];
+        Vec16<WT>::unpack(load16(g + (size_t)ci * E), gv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) xr[j][e] = gv[e] * (xr[j][e] * r);
+      }
+    }
+  }
+
+  float best_v = -INFINITY;
+  int best_i = 0x7fffffff;
+
+  for (int grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+    const int row0 = grp * R;
+    u32x4 wv[NV][KCH];
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        const WT *wp = nullptr;
+        if (row < a.N) {
+          wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)row * (size_t)a.K
+                                   : row_ptr<WT>(a, row);
+        }
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+          const int ci = j * kThreads + tid;
+          if (wp != nullptr && ci < nchunk)
+            wv[p * R + r][j] = load_stream16(wp + (size_t)ci * E);
+          else
+            wv[p * R + r][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    float acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < KCH; ++j) {
+        float wf[E];
+        Vec16<WT>::unpack(wv[v][j], wf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = fmaf(wf[e], xr[j][e], s);
+      }
+      acc[v] = s;
+    }
+    wave_transpose_sum<NV>(acc, lane);
+    constexpr int span = 64 / NV;
+    if ((lane % span) == 0) red[wave][lane / span] = acc[0];
+    __syncthreads();
+    if (tid < R) {
+      const int row = row0 + tid;
+      float val[PAIRS];
+#pragma unroll
+      for (int p = 0; p < PAIRS; ++p) {
+        const int v = p * R + tid;
+        val[p] = (red[0][v] + red[1][v]) + (red[2][v] + red[3][v]);
+      }
+      if (row < a.N) {
+        if (EPI == EPI_STORE) {
+          a.y[row] = val[0];
+        } else if (EPI == EPI_RESID) {
+          a.y[row] = a.res[row] + val[0];
+        } else if (EPI == EPI_SWIGLU) {
+          const float gt = val[0], up = val[PAIRS - 1];
+          a.y[row] = (gt / (1.0f + expf(-gt))) * up;
+        } else {  // EPI_ARGMAX
+          if (a.y) a.y[row] = val[0];
+        }
+      }
+      if (EPI == EPI_ARGMAX) red[0][tid] = (row < a.N) ? val[0] : -INFINITY;
+    }
+    if (EPI == EPI_ARGMAX) {
+      __syncthreads();
+      if (tid == 0) {
+        // rows in increasing order, strict >: the first index of the largest value
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float v = red[0][r];
+          if (v > best_v) {
+            best_v = v;
+            best_i = row0 + r;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (EPI == EPI_ARGMAX) {
+    if (tid == 0) {
+      a.part_v[blockIdx.x] = best_v;
+      a.part_i[blockIdx.x] = best_i;
+      __threadfence();
+      const int prev = atomicAdd(a.counter, 1);
+      is_last_s = (prev == (int)gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!is_last_s) return;
+    __threadfence();
+    // last block: reduce the per-block winners (larger value wins, equal values keep the lower index)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = tid; i < (int)gridDim.x; i += kThreads) {
+      const float v = __builtin_nontemporal_load(a.part_v + i);
+      const int ix = __builtin_nontemporal_load(a.part_i + i);
+      if (v > bv || (v == bv && ix < bi)) {
+        bv = v;
+        bi = ix;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      red[wave][0] = bv;
+      reinterpret_cast<int *>(ss_w)[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float fv = red[0][0];
+      int fi = reinterpret_cast<int *>(ss_w)[0];
+      for (int w = 1; w < 4; ++w) {
+        const float v = red[w][0];
+        const int ix = reinterpret_cast<int *>(ss_w)[w];
+        if (v > fv || (v == fv && ix < fi)) {
+          fv = v;
+          fi = ix;
+        }
+      }
+      if (fi == 0x7fffffff) fi = 0;  // every logit NaN: index 0, as an empty list gives
+      if (a.next) *a.next = fi;
+      *a.counter = 0;
+    }
+  }
+}
+
+template <typename WT, int EPI, bool NORM>
+static hipError_t dispatch_kch(int kch, dim3 grid, const GemvArgs &a, hipStream_t s) {
+  switch (kch) {
+#define CASE(k)                                                                        \
+  case k:                                                                              \
+    hipLaunchKernelGGL((k_gemv<WT, k, EPI, NORM>), grid, dim3(kThreads), 0, s, a);     \
+    break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+#undef CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static int rows_per_group(int kch, int pairs) {
+  int raw = 16 / (kch * pairs);
+  return raw >= 8 ? 8 : raw >= 4 ? 4 : raw >= 2 ? 2 : 1;
+}
+
+int gemv_supported(int wdtype, int K) {
+  const int E = wdtype == LLAMA_BF16 ? 8 : 4;
+  if (K <= 0 || K % E) return 0;
+  const int kch = (K / E + kThreads - 1) / kThreads;
+  return kch >= 1 && kch <= 8;
+}
+
+template <typename WT>
+static hipError_t launch_typed(GemvEpi epi, bool norm, GemvArgs a, int grid_cap, hipStream_t s) {
+  const int E = Vec16<WT>::E;
+  const int kch = (a.K / E + kThreads - 1) / kThreads;
+  const int R = rows_per_group(kch, epi == EPI_SWIGLU ? 2 : 1);
+  a.ngroups = (a.N + R - 1) / R;
+  int grid = a.ngroups < grid_cap ? a.ngroups : grid_cap;
+  if (epi == EPI_ARGMAX && grid > kLmGridMax) grid = kLmGridMax;
+  if (grid < 1) grid = 1;
+  const dim3 g(grid);
+  if (epi == EPI_STORE && norm) return dispatch_kch<WT, EPI_STORE, true>(kch, g, a, s);
+  if (epi == EPI_STORE && !norm) return dispatch_kch<WT, EPI_STORE, false>(kch, g, a, s);
+  if (epi == EPI_RESID && !norm) return dispatch_kch<WT, EPI_RESID, false>(kch, g, a, s);
+  if (epi == EPI_SWIGLU && norm) return dispatch_kch<WT, EPI_SWIGLU, true>(kch, g, a, s);
+  if (epi == EPI_ARGMAX && norm) return dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, int grid_cap, hipStream_t s) {
+  if (wdtype == LLAMA_BF16) return launch_typed<bf16_t>(epi, norm, a, grid_cap, s);
+  return launch_typed<float>(epi, norm, a, grid_cap, s);
+}
+
+}  // namespace lm

@@ -1,0 +1,139 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every function the header declares,
+and rejects invalid arguments with the documented codes before any device work (no compute call)."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import llama_architecture_decoder_amd as lm
+from synth import configs
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lm.lib()
+
+
+def test_header_declares_the_boundary():
+    names = set(lm.header_functions())
+    for need in ("llama_decode_step", "llama_prefill", "kv_cache_alloc", "lm_head_argmax", "llama_kv_cache_bytes",
+                 "llama_workspace_bytes", "llama_workspace_init", "llama_status", "llama_strerror",
+                 "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version"):
+        assert need in names, need
+
+
+def test_library_exports_every_header_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", lm.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in lm.header_functions() if n not in exported]
+    assert not missing, missing
+    for n in lm.header_functions():
+        assert hasattr(L, n)
+    assert L.llama_abi_version() == 1
+
+
+def test_strerror_covers_codes(L):
+    for code in range(0, -9, -1):
+        assert L.llama_strerror(code).decode() not in ("", "unknown error")
+    assert L.llama_strerror(-100).decode() == "unknown error"
+
+
+def _c(cfg, **kw):
+    c = lm.make_cfg(cfg)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_kv_cache_bytes_and_config_checks(L):
+    c = _c(configs.LLAMA31_8B)
+    # nest 8B card: 1 GiB of bf16 caches (both) at MaxSeq 8192
+    assert L.llama_kv_cache_bytes(ctypes.byref(c), 1, 8192) == (1 << 30) // 2
+    assert L.llama_kv_cache_bytes(ctypes.byref(c), 0, 8192) == lm.E_SHAPE
+    assert L.llama_kv_cache_bytes(None, 1, 8192) == lm.E_NULL
+    for field, bad in (("kv", 0), ("g", -1), ("half", 0), ("f", 0), ("layers", 0), ("vocab", 0), ("eps", 0.0),
+                       ("theta", -1.0), ("weight_dtype", 7), ("kv_dtype", 2), ("rope_llama3", 2),
+                       ("rope_factor", 0.0), ("tied_lm_head", 3)):
+        assert L.llama_kv_cache_bytes(ctypes.byref(_c(configs.LLAMA31_8B, **{field: bad})), 1, 16) == lm.E_CONFIG, field
+    c = _c(configs.LLAMA31_8B, rope_high_freq_factor=0.5)
+    assert L.llama_kv_cache_bytes(ctypes.byref(c), 1, 16) == lm.E_CONFIG
+    # valid but not built: head 32, g = 5, dim not a multiple of 8
+    assert L.llama_kv_cache_bytes(ctypes.byref(_c(configs.TINY)), 1, 16) == lm.E_UNSUPPORTED
+    assert L.llama_kv_cache_bytes(ctypes.byref(_c(configs.SMOLLM2_135M, g=5)), 1, 16) == lm.E_UNSUPPORTED
+    for name in configs.CONFIGS:
+        assert L.llama_kv_cache_bytes(ctypes.byref(_c(configs.get(name))), 1, 64) > 0, name
+
+
+def test_workspace_bytes(L):
+    c = _c(configs.LLAMA31_8B)
+    n1 = L.llama_workspace_bytes(ctypes.byref(c), 1, 8192, 0)
+    n32 = L.llama_workspace_bytes(ctypes.byref(c), 32, 32768, 0)
+    assert 0 < n1 < n32
+    assert L.llama_workspace_bytes(ctypes.byref(c), 0, 8192, 0) == lm.E_SHAPE
+    assert L.llama_workspace_bytes(ctypes.byref(c), 65, 8192, 0) == lm.E_SHAPE
+    assert L.llama_workspace_bytes(ctypes.byref(c), 1, 1 << 20, 0) == lm.E_UNSUPPORTED
+
+
+def test_kv_cache_alloc_binds_without_touching_memory(L):
+    cfg = configs.SMOLLM2_135M
+    c = _c(cfg)
+    need = L.llama_kv_cache_bytes(ctypes.byref(c), 2, 32)
+    k = np.zeros(need + 16, dtype=np.uint8)
+    v = np.zeros(need + 16, dtype=np.uint8)
+    kp = k.ctypes.data + ((-k.ctypes.data) % 16)
+    vp = v.ctypes.data + ((-v.ctypes.data) % 16)
+    rec = lm.llama_kv()
+    assert L.kv_cache_alloc(ctypes.byref(c), 2, 32, kp, vp, need, ctypes.byref(rec)) == lm.OK
+    assert (rec.rows, rec.max_seq, rec.layers, rec.kv, rec.head, rec.dtype) == (2, 32, cfg.layers, cfg.kv, 64, lm.F32)
+    assert not k.any() and not v.any()
+    assert L.kv_cache_alloc(ctypes.byref(c), 2, 32, kp, vp, need - 1, ctypes.byref(rec)) == lm.E_WORKSPACE
+    assert L.kv_cache_alloc(ctypes.byref(c), 2, 32, None, vp, need, ctypes.byref(rec)) == lm.E_NULL
+    assert L.kv_cache_alloc(ctypes.byref(c), 2, 32, kp + 4, vp, need, ctypes.byref(rec)) == lm.E_SHAPE
+
+
+def test_decode_and_prefill_reject_before_any_device_work(L):
+    """Argument errors come back before the library touches the workspace or a GPU: the fake device
+    pointers below are never dereferenced."""
+    cfg = configs.SMOLLM2_135M
+    c = _c(cfg)
+    fake = 1 << 40
+    kv = lm.llama_kv(fake, fake, 2, 16, cfg.layers, cfg.kv, 64, lm.F32)
+    lw = (lm.llama_layer_w * cfg.layers)()
+    for l in range(cfg.layers):
+        for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "w_gate", "w_up", "w_down"):
+            setattr(lw[l], f, fake)
+    w = lm.llama_weights(fake, None, fake, lw)
+    ws = lm.llama_ws(fake, 1 << 30, 2, 16, 0, 0, 0)  # never initialised: reached only after the checks
+    pos = (ctypes.c_int32 * 3)(0, 0, 0)
+
+    def dec(B, p, cc=c, kvr=kv, tokens=fake):
+        for i, v in enumerate(p):
+            pos[i] = v
+        return L.llama_decode_step(ctypes.byref(cc), ctypes.byref(w), ctypes.byref(kvr), tokens, pos, B, None, None,
+                                   ctypes.byref(ws), None)
+
+    assert dec(1, [16]) == lm.E_POS
+    assert dec(1, [-1]) == lm.E_POS
+    assert dec(2, [3, 16]) == lm.E_POS
+    assert dec(0, [0]) == lm.E_SHAPE
+    assert dec(3, [0, 0, 0]) == lm.E_SHAPE  # more rows than the cache holds
+    assert dec(1, [0], tokens=None) == lm.E_NULL
+    assert dec(1, [0], cc=_c(cfg, eps=-1.0)) == lm.E_CONFIG
+    bad_kv = lm.llama_kv(fake, fake, 2, 16, cfg.layers, cfg.kv + 1, 64, lm.F32)
+    assert dec(1, [0], kvr=bad_kv) == lm.E_SHAPE
+    # valid arguments, uninitialised workspace record
+    assert dec(1, [0]) == lm.E_WORKSPACE
+    # prefill: S <= 0, row outside, pos0 + S > max_seq
+    pf = lambda row, S, p0: L.llama_prefill(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), row, fake, S, p0,
+                                            None, None, ctypes.byref(ws), None)
+    assert pf(0, 0, 0) == lm.E_SHAPE
+    assert pf(2, 4, 0) == lm.E_SHAPE
+    assert pf(0, 4, 13) == lm.E_POS
+    assert pf(0, 4, -1) == lm.E_POS
+    assert pf(0, 4, 12) == lm.E_WORKSPACE
+    # lm_head_argmax: NULL outputs
+    assert L.lm_head_argmax(ctypes.byref(c), ctypes.byref(w), fake, 1, None, None, ctypes.byref(ws), None) == lm.E_NULL
+    # a misaligned weight pointer is refused
+    lw[3].wq = fake + 2
+    assert dec(1, [0]) == lm.E_SHAPE

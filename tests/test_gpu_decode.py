@@ -1,0 +1,255 @@
+"""GPU parity of the decode step through the C ABI against the CPU oracle (same seeded inputs).
+
+Teacher forcing: both sides take the oracle's chosen token at every step, so a legitimate near-tie
+cannot cascade.  Logits: F32 models within max|d| 1e-3 and max|d|/max|ref| 1e-4, bf16-weight models
+within max|d| 2e-2; argmax equal wherever the oracle's top-2 gap exceeds that tolerance.  Cache
+indexing and the RoPE + append arithmetic are bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import configs
+from parity_util import (check_argmax, check_logits, fill_random, gpu_cache, log, weights, widen)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _lm():
+    import llama_architecture_decoder_amd as lm
+    return lm
+
+
+def _dev_tok(t):
+    return torch.tensor([int(t)], dtype=torch.int32, device="cuda")
+
+
+def _pair(cfg, max_seq, rows=1):
+    lm = _lm()
+    w = weights(cfg)
+    om = oracle.Model(cfg, w, rows=rows, max_seq=max_seq)
+    dec = lm.Decoder(cfg, w, rows=rows, max_seq=max_seq)
+    return om, dec
+
+
+def _step(cfg, om, dec, tok, pos, row=0):
+    """One teacher-forced step on both sides; returns (oracle id, oracle logits, gpu id, gpu logits)."""
+    r, ref, _, _ = om.decode(int(tok), pos, row=row)
+    logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    dec.decode(_dev_tok(tok), [pos], logits, nxt)
+    torch.cuda.synchronize()
+    return r, ref, int(nxt.item()), logits[0].cpu().numpy()
+
+
+def _check_written_slots(cfg, om, dec, p0, p1, row=0):
+    gk, gv = gpu_cache(dec)
+    for name, g, o in (("K", gk, om.kc), ("V", gv, om.vc)):
+        a = widen(np.ascontiguousarray(g[:, row, :, p0:p1]))
+        b = widen(np.ascontiguousarray(o[:, row, :, p0:p1]))
+        scale = float(np.abs(b).max())
+        tol = (1e-4 if cfg.kvdtype == "f32" else 1.6e-2) * scale
+        assert float(np.abs(a - b).max()) <= tol, f"{name} slots {p0}..{p1 - 1}"
+
+
+CASES = [
+    # name, layers (None = all), prompt length, random fill before the prompt, decode steps, max_seq
+    ("smollm2_135m", None, 8, 0, 16, 2048),        # the whole workload: prompt 8, 16 decode steps
+    ("smollm2_360m", None, 128, 0, 8, 2048),       # full prompt, first 8 decode steps
+    ("smollm2_1_7b", None, 16, 0, 4, 8192),        # the prefill path at the 1.7B shape
+    ("smollm2_1_7b", None, 0, 1019, 5, 8192),      # the last decode positions of the workload (1019..1023)
+    ("llama31_8b", None, 0, 7936, 4, 8192),        # the workload's first steps (7936..7939)
+    ("llama31_8b", None, 0, 8188, 4, 8192),        # its last steps, up to max_seq - 1
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,layers,prompt,fill,steps,max_seq", CASES,
+                         ids=[f"{c[0]}-p{c[2]}-f{c[3]}-d{c[4]}" for c in CASES])
+def test_decode_parity(name, layers, prompt, fill, steps, max_seq):
+    cfg = configs.get(name)
+    log(f"case {name} prompt={prompt} fill={fill} steps={steps} max_seq={max_seq}")
+    om, dec = _pair(cfg, max_seq)
+    if fill:
+        fill_random(cfg, om, dec, [0], fill)
+    pos = fill
+    tok = int(synth.tokens(cfg, f"first/{fill}", 1)[0])
+    worst = 0.0
+    if prompt:
+        toks = synth.tokens(cfg, "prompt", prompt)
+        r, ref = om.prefill(toks, pos0=pos)
+        logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        dec.prefill(torch.from_numpy(toks).cuda(), pos0=pos, logits=logits[0], next_tok=nxt)
+        torch.cuda.synchronize()
+        got = logits[0].cpu().numpy()
+        d, rel = check_logits(cfg, got, ref, "prefill")
+        check_argmax(cfg, int(nxt.item()), ref, "prefill")
+        worst = max(worst, rel)
+        pos += prompt
+        tok = r
+    for s in range(steps):
+        r, ref, gid, got = _step(cfg, om, dec, tok, pos)
+        d, rel = check_logits(cfg, got, ref, f"step {s} pos {pos}")
+        check_argmax(cfg, gid, ref, f"step {s} pos {pos}")
+        worst = max(worst, rel)
+        pos += 1
+        tok = r  # teacher forcing: the oracle's token
+    _check_written_slots(cfg, om, dec, fill, pos)
+    assert dec.status() == 0
+    log(f"{name}: worst max|d|/max|ref| {worst:.3g} over {steps} steps")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,pos", [("smollm2_135m", 0), ("smollm2_135m", 37), ("smollm2_1_7b", 511),
+                                      ("llama31_8b", 7936), ("llama31_8b", 8191)])
+def test_rope_append_bit_exact_and_indexing(name, pos):
+    """The slot written is (layer, row, kv head, pos) and nothing else; its bits are exactly the F32
+    RoPE of the GPU's own pre-RoPE key (oracle rotation, same cos/sin table), rounded as the cache type,
+    and the value is the pre-RoPE value itself, rounded."""
+    cfg = configs.truncated(configs.get(name), 2)
+    lm = _lm()
+    w = weights(cfg)
+    dec = lm.Decoder(cfg, w, rows=2, max_seq=pos + 8)
+    om = oracle.Model(cfg, w, rows=2, max_seq=pos + 8)
+    fill_random(cfg, om, dec, [1], pos + 8)  # row 1 is a neighbour that must stay untouched
+    fill_random(cfg, om, dec, [0], pos)
+    # a sentinel pattern in row 0 beyond pos
+    sentinel = 0x5A5A if cfg.kvdtype == "bf16" else np.float32(-7.25)
+    kk, vv = gpu_cache(dec)
+    kk[:, 0, :, pos:] = sentinel
+    vv[:, 0, :, pos:] = sentinel
+    _upload(dec, kk, vv)
+    before_k, before_v = kk.copy(), vv.copy()
+    tok = int(synth.tokens(cfg, "bitexact", 1)[0])
+    trace = dec.decode_traced(_dev_tok(tok), pos)
+    tr = dec.split_trace(trace)
+    after_k, after_v = gpu_cache(dec)
+    cs, sn = oracle.rope_cs(cfg, pos)
+    D = cfg.head
+    for l in range(cfg.layers):
+        for j in range(cfg.kv):
+            kr = oracle.rope_head(tr[l]["k"][j * D:(j + 1) * D], cs, sn)
+            vr = tr[l]["v"][j * D:(j + 1) * D]
+            if cfg.kvdtype == "bf16":
+                ek = np.array([oracle.bf16(x) for x in kr], dtype=np.uint16)
+                ev = np.array([oracle.bf16(x) for x in vr], dtype=np.uint16)
+            else:
+                ek, ev = kr, vr
+            np.testing.assert_array_equal(after_k[l, 0, j, pos].view(np.uint16 if cfg.kvdtype == "bf16" else np.uint32),
+                                          ek.view(np.uint16 if cfg.kvdtype == "bf16" else np.uint32))
+            np.testing.assert_array_equal(after_v[l, 0, j, pos].view(np.uint16 if cfg.kvdtype == "bf16" else np.uint32),
+                                          ev.view(np.uint16 if cfg.kvdtype == "bf16" else np.uint32))
+    # everything else is bitwise unchanged
+    mask = np.ones(after_k.shape[:4], dtype=bool)
+    mask[:, 0, :, pos] = False
+    for a, b in ((after_k, before_k), (after_v, before_v)):
+        assert np.array_equal(a[mask].view(np.uint8), b[mask].view(np.uint8))
+
+
+def _upload(dec, k, v):
+    if k.dtype == np.uint16:
+        dec.kv.k.view(torch.int16).copy_(torch.from_numpy(k.view(np.int16)))
+        dec.kv.v.view(torch.int16).copy_(torch.from_numpy(v.view(np.int16)))
+    else:
+        dec.kv.k.copy_(torch.from_numpy(k))
+        dec.kv.v.copy_(torch.from_numpy(v))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,pos", [("smollm2_135m", 100), ("llama31_8b", 5000)])
+def test_causality_and_determinism(name, pos):
+    """Rows after t are never read (NaN there changes no bit), and two runs give the same bits."""
+    cfg = configs.truncated(configs.get(name), 2)
+    lm = _lm()
+    w = weights(cfg)
+    dec = lm.Decoder(cfg, w, rows=1, max_seq=pos + 64)
+    om = oracle.Model(cfg, w, rows=1, max_seq=pos + 64, alloc_cache=True)
+    fill_random(cfg, om, dec, [0], pos + 64)
+    k0, v0 = gpu_cache(dec)
+    tok = _dev_tok(3)
+
+    def run():
+        logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+        dec.decode(tok, [pos], logits, None)
+        torch.cuda.synchronize()
+        return logits.cpu().numpy()
+
+    a = run()
+    _upload(dec, k0, v0)
+    b = run()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "not deterministic"
+    k1, v1 = k0.copy(), v0.copy()
+    nan = 0x7FC0 if cfg.kvdtype == "bf16" else np.float32(np.nan)
+    k1[:, :, :, pos + 1:] = nan
+    v1[:, :, :, pos + 1:] = nan
+    _upload(dec, k1, v1)
+    c = run()
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32)), "read past position t"
+
+
+@pytest.mark.timeout(600)
+def test_batched_rows_each_at_own_position():
+    """decode_rows: B rows, each at its own position of its own cache row (nest decode_rows)."""
+    cfg = configs.truncated(configs.SMOLLM2_135M, 3)
+    lm = _lm()
+    w = weights(cfg)
+    rows = 3
+    om = oracle.Model(cfg, w, rows=rows, max_seq=256)
+    dec = lm.Decoder(cfg, w, rows=rows, max_seq=256)
+    lens = [0, 31, 200]
+    for r, n in enumerate(lens):
+        if n:
+            fill_random(cfg, om, dec, [r], n)
+    toks = synth.tokens(cfg, "rows", rows)
+    logits = torch.empty((rows, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    dec.decode(torch.from_numpy(toks).cuda(), lens, logits, nxt)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    for r in range(rows):
+        rid, ref, _, _ = om.decode(int(toks[r]), lens[r], row=r)
+        check_logits(cfg, got[r], ref, f"row {r}")
+        check_argmax(cfg, int(nxt[r].item()), ref, f"row {r}")
+
+
+@pytest.mark.timeout(300)
+def test_token_out_of_range_sets_status():
+    cfg = configs.truncated(configs.SMOLLM2_135M, 2)
+    lm = _lm()
+    dec = lm.Decoder(cfg, weights(cfg), rows=1, max_seq=16)
+    logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+    dec.decode(_dev_tok(cfg.vocab), [0], logits, None)
+    assert dec.status() == lm.E_TOKEN
+    assert dec.status() == 0  # cleared
+    dec.decode(_dev_tok(5), [1], logits, None)
+    assert dec.status() == 0
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["smollm2_135m", "llama31_8b"])
+def test_lm_head_argmax(name):
+    cfg = configs.truncated(configs.get(name), 1)
+    lm = _lm()
+    w = weights(cfg)
+    dec = lm.Decoder(cfg, w, rows=2, max_seq=16)
+    om = oracle.Model(cfg, w, rows=1, max_seq=16, alloc_cache=False)
+    rng = np.random.default_rng(11)
+    hid = rng.standard_normal((2, cfg.dim)).astype(np.float32)
+    logits = torch.empty((2, cfg.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(2, dtype=torch.int32, device="cuda")
+    dec.lm_head_argmax(torch.from_numpy(hid).cuda(), logits, am)
+    torch.cuda.synchronize()
+    for b in range(2):
+        rid, ref = om.lm_head(hid[b])
+        check_logits(cfg, logits[b].cpu().numpy(), ref, f"row {b}")
+        check_argmax(cfg, int(am[b].item()), ref, f"row {b}")
+    # duplicated maxima: the first index wins (main.bend argmax)
+    x = torch.zeros((1, cfg.dim), dtype=torch.float32, device="cuda")
+    dec.lm_head_argmax(x, None, am[:1])
+    torch.cuda.synchronize()
+    assert int(am[0].item()) == 0  # all logits 0: index 0
