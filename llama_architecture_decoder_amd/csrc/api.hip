@@ -23,10 +23,8 @@ constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 
 struct Tun {
   int gemv_grid = 1024;      // cap on GEMV blocks (they walk row groups with a grid stride)
-  int attn_target = 1024;    // wanted attention blocks per launch (sets the chunk length)
   Tun() {
     if (const char *e = getenv("LLAMA_GEMV_GRID")) gemv_grid = atoi(e) > 0 ? atoi(e) : gemv_grid;
-    if (const char *e = getenv("LLAMA_ATTN_BLOCKS")) attn_target = atoi(e) > 0 ? atoi(e) : attn_target;
   }
 };
 const Tun &tun() {
@@ -103,7 +101,7 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, attn_cnt, lm_cnt, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, total;
+  size_t status, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, total;
   int nch;
 };
 
@@ -111,8 +109,8 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   (void)max_prefill;
   const Dims d = dims_of(c);
   WsLayout L;
-  L.nch = (int)((max_seq + kAttnChunkMin - 1) / kAttnChunkMin);
-  if (L.nch > kAttnMaxChunks) L.nch = kAttnMaxChunks;
+  const int chunk = attention_chunk(c->kv_dtype, (int)d.head);
+  L.nch = (int)((max_seq + chunk - 1) / chunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -120,8 +118,6 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
     return at;
   };
   L.status = take(64);
-  L.attn_cnt = take(sizeof(int) * (size_t)max_batch * d.kv);
-  L.lm_cnt = take(sizeof(int) * (size_t)max_batch);
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * (size_t)max_batch * d.dim);
@@ -188,13 +184,13 @@ struct ProfScope {
   hipStream_t s;
   hipEvent_t e0 = nullptr;
   ProfScope(int c, hipStream_t st) : cls(c), s(st) {
-    if (prof().on && (e0 = prof().get())) hipEventRecord(e0, s);
+    if (prof().on && (e0 = prof().get())) (void)hipEventRecord(e0, s);
   }
   ~ProfScope() {
     if (!e0) return;
     hipEvent_t e1 = prof().get();
     if (!e1) return;
-    hipEventRecord(e1, s);
+    (void)hipEventRecord(e1, s);
     prof().marks.push_back({cls, {e0, e1}});
   }
 };
@@ -265,7 +261,6 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
   a.y = logits;
   a.part_v = x.at<float>(x.L.lm_v) + (size_t)b * kLmGridMax;
   a.part_i = x.at<int>(x.L.lm_i) + (size_t)b * kLmGridMax;
-  a.counter = x.at<int>(x.L.lm_cnt) + b;
   a.next = next;
   ProfScope ps(LLAMA_K_LM_HEAD, x.s);
   return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().gemv_grid, x.s));
@@ -289,17 +284,10 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   }
   if (rc) return rc;
 
-  // attention chunking: enough blocks to cover the chip, chunks a multiple of 32 positions
+  // attention: one block per (chunk of positions, kv head, row)
   int tmax = 0;
   for (int b = 0; b < B; ++b) tmax = pos[b] > tmax ? pos[b] : tmax;
-  const int npos = tmax + 1;
-  int want = (tun().attn_target + B * (int)d.kv - 1) / (B * (int)d.kv);
-  if (want < 1) want = 1;
-  int chunk = (npos + want - 1) / want;
-  chunk = (int)align_up((size_t)(chunk < kAttnChunkMin ? kAttnChunkMin : chunk), kAttnChunkMin);
-  if ((npos + chunk - 1) / chunk > x.L.nch) chunk = (int)align_up((size_t)((npos + x.L.nch - 1) / x.L.nch), kAttnChunkMin);
-  if (chunk > kAttnChunkMax) return LLAMA_E_UNSUPPORTED;
-  const int nch_launch = (npos + chunk - 1) / chunk;
+  const int nch_launch = tmax / attention_chunk(x.c->kv_dtype, (int)d.head) + 1;
 
   AttnArgs aa = {};
   aa.qkv = qkv;
@@ -314,9 +302,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   aa.out_stride = H;
   aa.part_o = x.at<float>(x.L.part_o);
   aa.part_ml = x.at<float>(x.L.part_ml);
-  aa.counter = x.at<int>(x.L.attn_cnt);
   aa.nch = x.L.nch;
-  aa.chunk = chunk;
   aa.scale = 1.0f / sqrtf((float)d.head);
   for (int b = 0; b < B; ++b) aa.pos[b] = pos[b];
 
@@ -485,7 +471,8 @@ int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max
   int rc = check_cfg(c);
   if (rc) return rc;
   if (max_batch <= 0 || max_batch > kMaxBatch || max_seq <= 0 || max_prefill < 0) return LLAMA_E_SHAPE;
-  if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * kAttnChunkMax) return LLAMA_E_UNSUPPORTED;
+  if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * attention_chunk(c->kv_dtype, 2 * c->half))
+    return LLAMA_E_UNSUPPORTED;
   return (int64_t)ws_layout(c, max_batch, max_seq, max_prefill).total;
 }
 
@@ -499,7 +486,7 @@ int llama_workspace_init(const llama_cfg *c, int32_t max_batch, int32_t max_seq,
   const WsLayout L = ws_layout(c, max_batch, max_seq, max_prefill);
   hipStream_t s = (hipStream_t)stream;
   char *base = (char *)mem;
-  int rc = hip_rc(launch_zero(base, L.rope_cs, s));  // status word and counters
+  int rc = hip_rc(launch_zero(base, L.rope_cs, s));  // the status word
   if (rc) return rc;
   // rope table: angle t * inv_freq[i] rounded to F32, then cos and sin (main.bend rot_at)
   const int half = c->half;

@@ -11,9 +11,7 @@ namespace lm {
 
 constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
 constexpr int kMaxBatch = 64;   // rows of one decode call (positions travel as a kernel argument)
-constexpr int kAttnChunkMin = 32;
-constexpr int kAttnChunkMax = 512;
-constexpr int kAttnMaxChunks = 256;
+constexpr int kAttnMaxChunks = 512;  // chunks per (row, kv head): max_seq <= 512 * chunk
 constexpr int kLmGridMax = 2048;
 
 typedef uint16_t bf16_t;  // bf16 kept as its bits; widened by a 16-bit shift (exact)
@@ -43,6 +41,16 @@ __device__ __forceinline__ float rope_hi(float lo, float hi, float c, float s) {
 #pragma clang fp contract(off)
   const float a = hi * c;
   const float b = lo * s;
+  return a + b;
+}
+
+// The same two formulas as one: own*c + (sign*partner)*s, where partner is the number half a head away
+// and sign is -1 in the first half (rot_lo) and +1 in the second (rot_hi).  Negation is exact, so this is
+// bit-identical to rope_lo / rope_hi.
+__device__ __forceinline__ float rope_pair(float own, float signed_partner, float c, float s) {
+#pragma clang fp contract(off)
+  const float a = own * c;
+  const float b = signed_partner * s;
   return a + b;
 }
 
@@ -91,6 +99,20 @@ __device__ __forceinline__ u32x4 load_stream16(const void *p) {
 }
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// n (4 or 8) consecutive F32 from a 16-byte aligned address
+template <int n>
+__device__ __forceinline__ void load_f32(const float *p, float (&o)[n]) {
+  static_assert(n % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+  for (int k = 0; k < n; k += 4) {
+    const float4 v = *reinterpret_cast<const float4 *>(p + k);
+    o[k] = v.x;
+    o[k + 1] = v.y;
+    o[k + 2] = v.z;
+    o[k + 3] = v.w;
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -117,10 +139,9 @@ struct GemvArgs {
   const float *res;    // EPI_RESID: y = res + W x (res may alias y)
   int ngroups;         // row groups of R rows
   // EPI_ARGMAX
-  float *part_v;
+  float *part_v;       // [grid] per-block winners
   int *part_i;
-  int *counter;
-  int32_t *next;
+  int32_t *next;       // nullable: argmax written by a one-block reduce
 };
 
 struct AttnArgs {
@@ -134,9 +155,8 @@ struct AttnArgs {
   int out_stride;
   float *part_o;       // [B][kv][nch][g][head]
   float *part_ml;      // [B][kv][nch][g][2]
-  int *counter;        // [B][kv], zero between calls
   int nch;             // chunk slots per (row, kv head) in the partial arrays
-  int chunk;           // positions per chunk
+  int direct;          // set by the launcher: one chunk per row, outputs written normalised
   float scale;         // 1/sqrt(head)
   int pos[kMaxBatch];
 };
@@ -144,8 +164,9 @@ struct AttnArgs {
 // host-side launchers (one per kernel family); return hipSuccess or the launch error
 hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, int grid_cap, hipStream_t s);
 int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is instantiated
-hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int nch_launch, hipStream_t s);
+hipError_t launch_attention(int kvdtype, int head, int g, AttnArgs a, int B, int nch_launch, hipStream_t s);
 int attention_supported(int head, int g);
+int attention_chunk(int kvdtype, int head);  // positions per attention block (fixed per cache type and head)
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
                         int *status, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);

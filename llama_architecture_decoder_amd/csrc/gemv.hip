@@ -76,7 +76,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 
   __shared__ float red[4][NV];
   __shared__ float ss_w[4];
-  __shared__ int is_last_s;
 
   // ---- the input slice of this thread: chunks j*256 + tid
   float xr[KCH][E];
@@ -204,57 +203,53 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     __syncthreads();
   }
 
-  if (EPI == EPI_ARGMAX) {
-    if (tid == 0) {
-      a.part_v[blockIdx.x] = best_v;
-      a.part_i[blockIdx.x] = best_i;
-      __threadfence();
-      const int prev = atomicAdd(a.counter, 1);
-      is_last_s = (prev == (int)gridDim.x - 1);
+  if (EPI == EPI_ARGMAX && tid == 0) {
+    a.part_v[blockIdx.x] = best_v;
+    a.part_i[blockIdx.x] = best_i;
+  }
+}
+
+// The per-block winners of the LM head, reduced by one block in a second launch: larger value wins,
+// equal values keep the lower index, so the result is the first index of the largest logit whatever
+// the order of the blocks (main.bend argmax).  Every logit NaN: index 0, as an empty list gives.
+__global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, const int *part_i, int n,
+                                                         int32_t *next) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = tid; k < n; k += kThreads) {
+    const float v = part_v[k];
+    const int ix = part_i[k];
+    if (v > bv || (v == bv && ix < bi)) {
+      bv = v;
+      bi = ix;
     }
-    __syncthreads();
-    if (!is_last_s) return;
-    __threadfence();
-    // last block: reduce the per-block winners (larger value wins, equal values keep the lower index)
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = tid; i < (int)gridDim.x; i += kThreads) {
-      const float v = __builtin_nontemporal_load(a.part_v + i);
-      const int ix = __builtin_nontemporal_load(a.part_i + i);
-      if (v > bv || (v == bv && ix < bi)) {
-        bv = v;
-        bi = ix;
-      }
-    }
+  }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float fv = sv[0];
+    int fi = si[0];
+    for (int w = 1; w < 4; ++w)
+      if (sv[w] > fv || (sv[w] == fv && si[w] < fi)) {
+        fv = sv[w];
+        fi = si[w];
       }
-    }
-    if (lane == 0) {
-      red[wave][0] = bv;
-      reinterpret_cast<int *>(ss_w)[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float fv = red[0][0];
-      int fi = reinterpret_cast<int *>(ss_w)[0];
-      for (int w = 1; w < 4; ++w) {
-        const float v = red[w][0];
-        const int ix = reinterpret_cast<int *>(ss_w)[w];
-        if (v > fv || (v == fv && ix < fi)) {
-          fv = v;
-          fi = ix;
-        }
-      }
-      if (fi == 0x7fffffff) fi = 0;  // every logit NaN: index 0, as an empty list gives
-      if (a.next) *a.next = fi;
-      *a.counter = 0;
-    }
+    *next = (fi == 0x7fffffff) ? 0 : fi;
   }
 }
 
@@ -299,7 +294,12 @@ static hipError_t launch_typed(GemvEpi epi, bool norm, GemvArgs a, int grid_cap,
   if (epi == EPI_STORE && !norm) return dispatch_kch<WT, EPI_STORE, false>(kch, g, a, s);
   if (epi == EPI_RESID && !norm) return dispatch_kch<WT, EPI_RESID, false>(kch, g, a, s);
   if (epi == EPI_SWIGLU && norm) return dispatch_kch<WT, EPI_SWIGLU, true>(kch, g, a, s);
-  if (epi == EPI_ARGMAX && norm) return dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s);
+  if (epi == EPI_ARGMAX && norm) {
+    hipError_t e = dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s);
+    if (e != hipSuccess || a.next == nullptr) return e;
+    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, a.part_v, a.part_i, grid, a.next);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
