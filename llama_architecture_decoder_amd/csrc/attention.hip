@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       vt_s[d0 + e] = KvStore<KT>::round_store(Vh + (size_t)t * D + d0 + e, vo[e]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- scores of positions p0..p1-1, scaled after the dot product
 #pragma unroll
@@ -153,16 +153,14 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc = fmaf(q[i][e], kf[e], acc);
-#pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-      s[i] = acc;
+      s[i] = group_sum<LPR>(acc);
     }
     if (li == 0 && p < p1) {
 #pragma unroll
       for (int i = 0; i < G; ++i) s_sc[i][r * PPR + grp] = a.scale * s[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- per head over this chunk: max, exp(s - max), their sum
   const int n = p1 - p0;
@@ -182,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       l_s[i] = l;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- sum_p e_p V[p]
   float o[G][E];
@@ -211,18 +209,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   }
   // position groups inside a wavefront, then the 4 wavefronts
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1)
+  for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[i][e] += __shfl_xor(o[i][e], off);
+    for (int e = 0; e < E; ++e) o[i][e] = strided_sum<LPR>(o[i][e]);
   if (lane < LPR) {
 #pragma unroll
     for (int i = 0; i < G; ++i)
 #pragma unroll
       for (int e = 0; e < E; ++e) o_s[wave][i][li * E + e] = o[i][e];
   }
-  __syncthreads();
+  lds_barrier();
 
   const int o_base = (j * G) * D;
   if (a.direct) {
@@ -254,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 // 4 chunk groups x 64 outputs; the 4 groups' sums are combined in a fixed order.
 template <int G, int D>
 __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) {
+  constexpr int PER = 16;  // partials per thread loaded up front (chunks 0..63); more in a loop
   const int og = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
   const int nact = t / chunk + 1;
@@ -265,28 +262,59 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) 
   const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
   const float *pml0 = a.part_ml + slot * (size_t)(G * 2);
   const float *po0 = a.part_o + slot * (size_t)(G * D);
+  // every load first: this thread's (m, l) of chunks tid, tid + 256 and its output's partial o of
+  // chunks wave, wave + 4, ..., wave + 60 (independent of the maxima: one memory round trip)
+  float mv[2], lv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int cc = min(tid + k * kThreads, nact - 1);
+    mv[k] = pml0[(size_t)cc * G * 2 + 2 * i];
+    lv[k] = pml0[(size_t)cc * G * 2 + 2 * i + 1];
+  }
+  float ov[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int cc = wave + 4 * k;
+    if (cc < nact) ov[k] = po0[(size_t)cc * G * D + i * D + d];
+  }
   float M = -INFINITY;
-  for (int cc = tid; cc < nact; cc += kThreads) M = fmaxf(M, pml0[(size_t)cc * G * 2 + 2 * i]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (tid + k * kThreads < nact) M = fmaxf(M, mv[k]);
   M = wave_max(M);
   if (lane == 0) red[wave] = M;
-  __syncthreads();
+  lds_barrier();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
+  lds_barrier();
   float L = 0.f;
-  for (int cc = tid; cc < nact; cc += kThreads) {
-    const float w = expf(pml0[(size_t)cc * G * 2 + 2 * i] - M);
-    w_s[cc] = w;
-    L = fmaf(w, pml0[(size_t)cc * G * 2 + 2 * i + 1], L);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int cc = tid + k * kThreads;
+    if (cc < nact) {
+      const float w = expf(mv[k] - M);
+      w_s[cc] = w;
+      L = fmaf(w, lv[k], L);
+    }
   }
   L = wave_sum(L);
   if (lane == 0) red[wave] = L;
-  __syncthreads();
+  lds_barrier();
   L = (red[0] + red[1]) + (red[2] + red[3]);
   float acc = 0.f;
-#pragma unroll 8
-  for (int cc = wave; cc < nact; cc += 4) acc = fmaf(w_s[cc], po0[(size_t)cc * G * D + i * D + d], acc);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int cc = wave + 4 * k;
+    if (cc < nact) acc = fmaf(w_s[cc], ov[k], acc);
+  }
+  for (int base = 4 * PER; base < nact; base += 4 * PER) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int cc = base + wave + 4 * k;
+      if (cc < nact) acc = fmaf(w_s[cc], po0[(size_t)cc * G * D + i * D + d], acc);
+    }
+  }
   acc_s[wave][lane] = acc;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const float sum = (acc_s[0][lane] + acc_s[1][lane]) + (acc_s[2][lane] + acc_s[3][lane]);
     a.out[(size_t)b * a.out_stride + (size_t)(j * G + i) * D + d] = sum / L;

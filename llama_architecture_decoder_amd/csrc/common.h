@@ -5,13 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/llama_mi355x.h"
+#include "llama_mi355x.h"
 
 namespace lm {
 
 constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
 constexpr int kMaxBatch = 64;   // rows of one decode call (positions travel as a kernel argument)
-constexpr int kAttnMaxChunks = 512;  // chunks per (row, kv head): max_seq <= 512 * chunk
+constexpr int kAttnMaxChunks = 512;  // chunks per (row, kv head): max_seq <= 512 * chunk (2 per merge thread)
 constexpr int kLmGridMax = 2048;
 
 typedef uint16_t bf16_t;  // bf16 kept as its bits; widened by a 16-bit shift (exact)
@@ -99,6 +99,15 @@ __device__ __forceinline__ u32x4 load_stream16(const void *p) {
 }
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Block barrier that orders LDS only: waves publish LDS writes to each other, while global loads issued
+// before it stay in flight (a full __syncthreads() also waits for every outstanding global access).
+// Used wherever threads of a block exchange data through LDS and nothing through global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // n (4 or 8) consecutive F32 from a 16-byte aligned address
 template <int n>
 __device__ __forceinline__ void load_f32(const float *p, float (&o)[n]) {
@@ -111,6 +120,40 @@ __device__ __forceinline__ void load_f32(const float *p, float (&o)[n]) {
     o[k + 2] = v.z;
     o[k + 3] = v.w;
   }
+}
+
+// ---- cross-lane sums on VALU permutes (DPP within 16-lane rows, permlane swaps across rows)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float xor16_sum(float v) {  // v + v of lane ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {  // v + v of lane ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over each aligned group of N lanes (N = 1, 2, 4, 8, 16, 32, 64); every lane of a group gets it.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if (N >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if (N >= 8) v += dpp_f<0x141>(v);  // row_half_mirror: the other quad of the half row
+  if (N >= 16) v += dpp_f<0x140>(v); // row_mirror: the other half of the row
+  if (N >= 32) v = xor16_sum(v);
+  if (N >= 64) v = xor32_sum(v);
+  return v;
+}
+// Sum over the lanes that share (lane % S), S = 8, 16, 32 or 64: one value per lane position of an
+// S-lane group, summed over the 64/S groups of the wavefront.
+template <int S>
+__device__ __forceinline__ float strided_sum(float v) {
+  if (S <= 8) v += dpp_f<0x128>(v);  // row_ror:8: lane ^ 8 within the row
+  if (S <= 16) v = xor16_sum(v);
+  if (S <= 32) v = xor32_sum(v);
+  return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   constexpr int NV = R * PAIRS;  // partial sums per thread per group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunk = a.K / E;
+  const bool ragged = (nchunk % kThreads) != 0;  // uniform: some threads' last chunk is past K
 
   __shared__ float red[4][NV];
   __shared__ float ss_w[4];
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     // RMSNorm prologue: g * (x * (1 / sqrt(sum(x^2) / K + eps)))
     ss = wave_sum(ss);
     if (lane == 0) ss_w[wave] = ss;
-    __syncthreads();
+    lds_barrier();
     const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
     const float r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
     const WT *g = reinterpret_cast<const WT *>(a.gain);
@@ -132,18 +133,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = row0 + r;
-        const WT *wp = nullptr;
-        if (row < a.N) {
-          wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)row * (size_t)a.K
-                                   : row_ptr<WT>(a, row);
-        }
+        // unconditional loads: a row past N reads row N-1 (its result is never stored) and a chunk past
+        // the row end reads the row's last chunk (zeroed below)
+        const WT *wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)min(row, a.N - 1) * (size_t)a.K
+                                           : row_ptr<WT>(a, min(row, a.N - 1));
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
-          const int ci = j * kThreads + tid;
-          if (wp != nullptr && ci < nchunk)
-            wv[p * R + r][j] = load_stream16(wp + (size_t)ci * E);
-          else
-            wv[p * R + r][j] = u32x4{0u, 0u, 0u, 0u};
+          const int ci = min(j * kThreads + tid, nchunk - 1);
+          wv[p * R + r][j] = load_stream16(wp + (size_t)ci * E);
+        }
+        if (ragged) {  // a chunk past the row end contributes exact zeros, whatever was stored there
+#pragma unroll
+          for (int j = 0; j < KCH; ++j)
+            if (j * kThreads + tid >= nchunk) wv[p * R + r][j] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     wave_transpose_sum<NV>(acc, lane);
     constexpr int span = 64 / NV;
     if ((lane % span) == 0) red[wave][lane / span] = acc[0];
-    __syncthreads();
+    lds_barrier();
     if (tid < R) {
       const int row = row0 + tid;
       float val[PAIRS];
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       if (EPI == EPI_ARGMAX) red[0][tid] = (row < a.N) ? val[0] : -INFINITY;
     }
     if (EPI == EPI_ARGMAX) {
-      __syncthreads();
+      lds_barrier();
       if (tid == 0) {
         // rows in increasing order, strict >: the first index of the largest value
 #pragma unroll
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (EPI == EPI_ARGMAX && tid == 0) {
@@ -219,12 +221,20 @@ __global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, 
   __shared__ int si[4];
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int k = tid; k < n; k += kThreads) {
-    const float v = part_v[k];
-    const int ix = part_i[k];
-    if (v > bv || (v == bv && ix < bi)) {
-      bv = v;
-      bi = ix;
+  constexpr int PER = kLmGridMax / kThreads;  // every partial loaded before any compare
+  float vv[PER];
+  int iv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int ix = min(tid + k * kThreads, n - 1);
+    vv[k] = part_v[ix];
+    iv[k] = part_i[ix];
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (tid + k * kThreads < n && (vv[k] > bv || (vv[k] == bv && iv[k] < bi))) {
+      bv = vv[k];
+      bi = iv[k];
     }
   }
 #pragma unroll
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, 
     sv[wave] = bv;
     si[wave] = bi;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     float fv = sv[0];
     int fi = si[0];

@@ -1,8 +1,9 @@
 // Embedding gather and workspace clearing.
 //
 // Embedding (main.bend forward: the embedding row of the token, Bands.read_row; bf16 rows widened
-// exactly, bf16 being the upper half of an F32): x[b] = emb[tokens[b]].  Token ids live in device
-// memory (the previous step's argmax may feed them), so the range check happens here: an id outside
+// exactly, bf16 being the upper half of an F32): x[b] = emb[tokens[b]], one 16-byte slice per thread.
+// Token ids live in device memory (the previous step's argmax may feed them), so the range check
+// happens here: an id outside
 // [0, vocab) sets the sticky status flag and the row's input becomes zeros, so no out-of-bounds read
 // can happen.
 #include "common.h"
@@ -12,16 +13,23 @@ namespace lm {
 template <typename WT>
 __global__ __launch_bounds__(kThreads) void k_embed(const int32_t *tokens, const WT *emb, int dim, int vocab,
                                                     float *x, int *status) {
-  const int b = blockIdx.x;
+  // block (s, b): 16-byte slices s*256 + tid of row b (dim is a multiple of 8)
+  constexpr int E = Vec16<WT>::E;
+  const int b = blockIdx.y;
   const int tok = tokens[b];
-  float *xb = x + (size_t)b * dim;
+  const int ci = blockIdx.x * kThreads + threadIdx.x;
+  if (ci * E >= dim) return;
+  float *xb = x + (size_t)b * dim + (size_t)ci * E;
+  float v[E];
   if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) atomicOr(status, 1);
-    for (int i = threadIdx.x; i < dim; i += kThreads) xb[i] = 0.f;
-    return;
+    if (ci == 0) atomicOr(status, 1);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = 0.f;
+  } else {
+    Vec16<WT>::unpack(load16(emb + (size_t)tok * dim + (size_t)ci * E), v);
   }
-  const WT *row = emb + (size_t)tok * dim;
-  for (int i = threadIdx.x; i < dim; i += kThreads) xb[i] = load_scalar<WT>(row, i);
+#pragma unroll
+  for (int e = 0; e < E; e += 4) *reinterpret_cast<float4 *>(xb + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
 }
 
 __global__ void k_zero(uint32_t *p, size_t n) {
@@ -30,11 +38,13 @@ __global__ void k_zero(uint32_t *p, size_t n) {
 
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
                         int *status, hipStream_t s) {
+  const int E = wdtype == LLAMA_BF16 ? 8 : 4;
+  const dim3 grid((dim / E + kThreads - 1) / kThreads, B);
   if (wdtype == LLAMA_BF16)
-    hipLaunchKernelGGL((k_embed<bf16_t>), dim3(B), dim3(kThreads), 0, s, tokens,
-                       reinterpret_cast<const bf16_t *>(emb), dim, vocab, x, status);
+    hipLaunchKernelGGL((k_embed<bf16_t>), grid, dim3(kThreads), 0, s, tokens, reinterpret_cast<const bf16_t *>(emb),
+                       dim, vocab, x, status);
   else
-    hipLaunchKernelGGL((k_embed<float>), dim3(B), dim3(kThreads), 0, s, tokens, reinterpret_cast<const float *>(emb),
+    hipLaunchKernelGGL((k_embed<float>), grid, dim3(kThreads), 0, s, tokens, reinterpret_cast<const float *>(emb),
                        dim, vocab, x, status);
   return hipGetLastError();
 }
