@@ -13,11 +13,13 @@
 // head j and all g query heads of the group, so each K/V byte is read from HBM once for g heads.
 // 256 threads = 256/LPR position groups of LPR lanes, LPR lanes covering one 16-byte slice each of a
 // head row (head*bytes/16 lanes), so every load instruction of a wave reads whole contiguous rows.
-// Every K and V load of a thread (8 rows each) is issued before any is used.  Scores go to LDS; per head
-// the chunk max and exp-sum; then the exp-weighted V sum.  Each chunk writes an unnormalised partial
-// (o, m, l); a second small kernel merges the chunks of each (row, kv head) in chunk order, so results
-// do not depend on block timing.  When one chunk covers every row's positions the attention kernel
-// normalises directly and no merge runs.
+// Every K and V load of a thread (8 rows each) is issued before any is used.  The query heads, the
+// cos/sin row and the appended key/value are staged once per block in LDS.  Each wavefront keeps its
+// scores in registers and forms its own softmax pieces (max, exp-sum, exp-weighted V sum) with
+// cross-lane permutes; the 4 wavefronts are combined through LDS.  Each chunk writes an unnormalised
+// partial (o, m, l); a second small kernel merges the chunks of each (row, kv head) in chunk order,
+// so results do not depend on block timing.  When one chunk covers every row's positions the
+// attention kernel normalises directly and no merge runs.
 #include "common.h"
 
 namespace lm {
@@ -54,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   using S = AttnShape<KT, D>;
   constexpr int E = S::E, LPR = S::LPR, PPR = S::PPR, NR = S::NR, CHUNK = S::CHUNK;
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row must fit a wavefront");
+  constexpr int HALF = D / 2;
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
   const int nact = t / CHUNK + 1;  // chunks covering 0..t
@@ -62,44 +65,42 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   const int li = tid % LPR, grp = tid / LPR;
   const int p0 = c * CHUNK;
   const int p1 = min(p0 + CHUNK, t + 1);
-  const int half = a.half;
+  const bool owner = (c == nact - 1);
 
-  __shared__ float s_sc[G][CHUNK];
-  __shared__ float kt_s[D], vt_s[D];
-  __shared__ float m_s[G], l_s[G];
-  __shared__ float o_s[4][G][D];
+  __shared__ float q_s[G][D];                // raw query heads of the group
+  __shared__ float cs_s[HALF], sn_s[HALF];   // cos / sin of position t
+  __shared__ float kr_s[D], vr_s[D];         // raw key / value of kv head j at t (owner block)
+  __shared__ float kt_s[D], vt_s[D];         // the appended key (rotated) and value, as stored
+  __shared__ float m_s[4][G];
+  __shared__ float l_g[kThreads / LPR][G];
+  __shared__ float o_g[kThreads / LPR][G][D];
 
   const size_t head_off = ((size_t)(a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
   KT *Kh = reinterpret_cast<KT *>(a.kc) + head_off;
   KT *Vh = reinterpret_cast<KT *>(a.vc) + head_off;
   const float *qkv = a.qkv + (size_t)b * a.qkv_stride;
   const int dim = a.kv * G * D;
-  const float *cs = a.rope_cs + (size_t)t * half;
-  const float *sn = a.rope_sn + (size_t)t * half;
 
-  // (1) the small inputs first, so that waiting for them does not wait for the K/V stream: this lane's
-  // query slices [li*E, li*E + E) of the g heads and the slices half a head away, the cos/sin slice,
-  // and (for the append) the raw key/value slices of kv head j
-  const int d0 = li * E;                      // first number of this lane's slice
-  const int dp = d0 < half ? d0 + half : d0 - half;  // partner slice
-  const int ic = d0 < half ? d0 : d0 - half;  // frequency index of the slice
-  const float sgn = d0 < half ? -1.f : 1.f;
-  float qo[G][E], qp[G][E], cv[E], sv[E], ko[E], kp[E], vo[E];
+  // (1) small inputs, once per block, as 16-byte units: units [0, NQ) the query heads, [NQ, NQ+NC) the
+  // cos/sin slices, then (owner block) the raw key and value of head j.  A thread takes units tid and
+  // tid + 256.
+  constexpr int NQ = G * D / 4, NC = HALF / 4, NK = D / 4, NU = NQ + NC + NK;
+  static_assert(NU <= 2 * kThreads, "two staging units per thread");
+  float4 sm[2][2];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const float *qh = qkv + (size_t)(j * G + i) * D;
-    load_f32(qh + d0, qo[i]);
-    load_f32(qh + dp, qp[i]);
-  }
-  load_f32(cs + ic, cv);
-  load_f32(sn + ic, sv);
-  const bool owner = (c == nact - 1);
-  const float *kh = qkv + dim + (size_t)j * D;
-  const float *vh = qkv + dim + (size_t)a.kv * D + (size_t)j * D;
-  if (owner && grp == 0) {
-    load_f32(kh + d0, ko);
-    load_f32(kh + dp, kp);
-    load_f32(vh + d0, vo);
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + k * kThreads;
+    sm[k][0] = sm[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (u < NQ) {
+      sm[k][0] = *reinterpret_cast<const float4 *>(qkv + (size_t)j * G * D + u * 4);
+    } else if (u < NQ + NC) {
+      sm[k][0] = *reinterpret_cast<const float4 *>(a.rope_cs + (size_t)t * HALF + (u - NQ) * 4);
+      sm[k][1] = *reinterpret_cast<const float4 *>(a.rope_sn + (size_t)t * HALF + (u - NQ) * 4);
+    } else if (owner && u < NU) {
+      const int w = u - NQ - NC;
+      sm[k][0] = *reinterpret_cast<const float4 *>(qkv + dim + (size_t)j * D + w * 4);
+      sm[k][1] = *reinterpret_cast<const float4 *>(qkv + dim + (size_t)a.kv * D + (size_t)j * D + w * 4);
+    }
   }
 
   // (2) every K and V row of this thread's positions, in flight together.  Loads are unconditional: a
@@ -114,132 +115,145 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     vraw[r] = load_stream16(Vh + (size_t)p * D + li * E);
   }
 
-  // (3) rotated query slices (rot_lo / rot_hi)
-  float q[G][E];
 #pragma unroll
-  for (int i = 0; i < G; ++i)
-#pragma unroll
-    for (int e = 0; e < E; ++e) q[i][e] = rope_pair(qo[i][e], sgn * qp[i][e], cv[e], sv[e]);
-
-  // (4) the block whose chunk holds t appends this position's rotated key and its value (lanes of the
-  // first position group, one slice each); the scores read them back from LDS as stored
-  if (owner && grp == 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float kr = rope_pair(ko[e], sgn * kp[e], cv[e], sv[e]);
-      kt_s[d0 + e] = KvStore<KT>::round_store(Kh + (size_t)t * D + d0 + e, kr);
-      vt_s[d0 + e] = KvStore<KT>::round_store(Vh + (size_t)t * D + d0 + e, vo[e]);
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + k * kThreads;
+    if (u < NQ) {
+      *reinterpret_cast<float4 *>(&q_s[0][0] + u * 4) = sm[k][0];
+    } else if (u < NQ + NC) {
+      *reinterpret_cast<float4 *>(cs_s + (u - NQ) * 4) = sm[k][0];
+      *reinterpret_cast<float4 *>(sn_s + (u - NQ) * 4) = sm[k][1];
+    } else if (owner && u < NU) {
+      const int w = u - NQ - NC;
+      *reinterpret_cast<float4 *>(kr_s + w * 4) = sm[k][0];
+      *reinterpret_cast<float4 *>(vr_s + w * 4) = sm[k][1];
     }
   }
   lds_barrier();
 
-  // ---- scores of positions p0..p1-1, scaled after the dot product
+  // (3) the owner appends position t: the rotated key (rot_lo / rot_hi) and the value, rounded as
+  // stored; the scores use the stored values
+  if (owner && tid < D) {
+    const int d = tid, ic = d < HALF ? d : d - HALF;
+    const float partner = d < HALF ? -kr_s[d + HALF] : kr_s[d - HALF];
+    const float kr = rope_pair(kr_s[d], partner, cs_s[ic], sn_s[ic]);
+    kt_s[d] = KvStore<KT>::round_store(Kh + (size_t)t * D + d, kr);
+    vt_s[d] = KvStore<KT>::round_store(Vh + (size_t)t * D + d, vr_s[d]);
+  }
+  // rotated query slices [li*E, li*E + E) of the g heads
+  const int d0 = li * E;
+  const int dp = d0 < HALF ? d0 + HALF : d0 - HALF;
+  const int ic0 = d0 < HALF ? d0 : d0 - HALF;
+  const float sgn = d0 < HALF ? -1.f : 1.f;
+  float q[G][E];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[i][e] = rope_pair(q_s[i][d0 + e], sgn * q_s[i][dp + e], cs_s[ic0 + e], sn_s[ic0 + e]);
+  if (owner) {
+    lds_barrier();  // kt_s / vt_s
+    // the position-t row comes from this step's append: put its stored bits where a cache load would
+    // have put them, so every round takes the same path
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (p0 + r * PPR + grp == t) {
+        kraw[r] = Vec16<KT>::pack(&kt_s[d0]);
+        vraw[r] = Vec16<KT>::pack(&vt_s[d0]);
+      }
+    }
+  }
+
+  // (4) scores of this thread's positions in base 2: s2 = (q . k) * (scale * log2 e), so that
+  // exp(s - m) = exp2(s2 - m2); every lane of a position group gets the full dot product
+  const float scale2 = a.scale * 1.4426950408889634f;
+  float sc[NR][G];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int p = p0 + r * PPR + grp;
     float kf[E];
-    if (p < t) {
-      Vec16<KT>::unpack(kraw[r], kf);
-    } else if (p == t) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) kf[e] = kt_s[li * E + e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) kf[e] = 0.f;
-    }
-    float s[G];
+    Vec16<KT>::unpack(kraw[r], kf);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc = fmaf(q[i][e], kf[e], acc);
-      s[i] = group_sum<LPR>(acc);
-    }
-    if (li == 0 && p < p1) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) s_sc[i][r * PPR + grp] = a.scale * s[i];
+      const float dot = group_sum<LPR>(acc);  // every lane takes part in the row permutes
+      sc[r][i] = (p < p1) ? dot * scale2 : -INFINITY;
     }
   }
-  lds_barrier();
-
-  // ---- per head over this chunk: max, exp(s - max), their sum
-  const int n = p1 - p0;
-  for (int i = wave; i < G; i += 4) {
-    float m = -INFINITY;
-    for (int p = lane; p < n; p += 64) m = fmaxf(m, s_sc[i][p]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int p = lane; p < n; p += 64) {
-      const float e = expf(s_sc[i][p] - m);
-      s_sc[i][p] = e;
-      l += e;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      m_s[i] = m;
-      l_s[i] = l;
-    }
-  }
-  lds_barrier();
-
-  // ---- sum_p e_p V[p]
-  float o[G][E];
+  // (5) softmax pieces of this wavefront per head: max over its positions, 2^(s2 - max), their sum,
+  // and sum_p e_p V[p] (per position group; the groups are summed through LDS below)
+  float mw[G], lw[G], o[G][E];
 #pragma unroll
-  for (int i = 0; i < G; ++i)
+  for (int i = 0; i < G; ++i) {
+    float m = sc[0][i];
+#pragma unroll
+    for (int r = 1; r < NR; ++r) m = fmaxf(m, sc[r][i]);
+    mw[i] = strided_max<LPR < 16 ? 16 : LPR>(LPR < 16 ? fmaxf(m, dpp_f<0x128>(m)) : m);
+    lw[i] = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[i][e] = 0.f;
+  }
+  // exponent reference: the wavefront max, or 0 when none of its positions is in the chunk (every
+  // score is then -inf and every weight 0; -inf - -inf would be NaN)
+  float mref[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) mref[i] = (mw[i] == -INFINITY) ? 0.f : mw[i];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int p = p0 + r * PPR + grp;
-    if (p < p1) {
-      float vf[E];
-      if (p < t) {
-        Vec16<KT>::unpack(vraw[r], vf);
-      } else {
+    float vf[E];
+    Vec16<KT>::unpack(vraw[r], vf);
 #pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = vt_s[li * E + e];
-      }
+    for (int i = 0; i < G; ++i) {
+      const float w = __builtin_amdgcn_exp2f(sc[r][i] - mref[i]);  // -inf (masked) gives 0
+      lw[i] += w;
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float w = s_sc[i][r * PPR + grp];
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[i][e] = fmaf(w, vf[e], o[i][e]);
-      }
+      for (int e = 0; e < E; ++e) o[i][e] = fmaf(w, vf[e], o[i][e]);
     }
   }
-  // position groups inside a wavefront, then the 4 wavefronts
+  // per position group: (l, o) to LDS; the wavefront max is the same for its groups
+  constexpr int NG = kThreads / LPR;  // position groups per block
 #pragma unroll
-  for (int i = 0; i < G; ++i)
+  for (int i = 0; i < G; ++i) {
+    if (li == 0) l_g[grp][i] = lw[i];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[i][e] = strided_sum<LPR>(o[i][e]);
-  if (lane < LPR) {
+    for (int e = 0; e < E; ++e) o_g[grp][i][d0 + e] = o[i][e];
+  }
+  if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-      for (int e = 0; e < E; ++e) o_s[wave][i][li * E + e] = o[i][e];
+    for (int i = 0; i < G; ++i) m_s[wave][i] = mw[i];
   }
   lds_barrier();
 
-  const int o_base = (j * G) * D;
-  if (a.direct) {
-    // a single chunk covers 0..t (every row of the launch): normalise here, no merge pass
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int i = idx / D, d = idx % D;
-      const float sum = (o_s[0][i][d] + o_s[1][i][d]) + (o_s[2][i][d] + o_s[3][i][d]);
-      a.out[(size_t)b * a.out_stride + o_base + idx] = sum / l_s[i];
-    }
-    return;
-  }
+  // (6) the position groups combined (a wavefront with no position of the chunk has max -inf,
+  // weight 0); groups are summed in a fixed order
+  constexpr int GPW = NG / 4;  // position groups per wavefront
   const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
-  float *po = a.part_o + (slot + c) * (size_t)(G * D);
-  float *pml = a.part_ml + (slot + c) * (size_t)(G * 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int i = idx / D, d = idx % D;
-    po[idx] = (o_s[0][i][d] + o_s[1][i][d]) + (o_s[2][i][d] + o_s[3][i][d]);
-  }
-  if (tid < G) {
-    pml[2 * tid] = m_s[tid];
-    pml[2 * tid + 1] = l_s[tid];
+    const float M = fmaxf(fmaxf(m_s[0][i], m_s[1][i]), fmaxf(m_s[2][i], m_s[3][i]));
+    float acc = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (m_s[w][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][i] - M);
+      float ow = 0.f, lsum = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < GPW; ++g2) {
+        ow += o_g[w * GPW + g2][i][d];
+        lsum += l_g[w * GPW + g2][i];
+      }
+      acc = fmaf(f, ow, acc);
+      L = fmaf(f, lsum, L);
+    }
+    if (a.direct) {
+      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+    } else {
+      a.part_o[(slot + c) * (size_t)(G * D) + idx] = acc;
+      if (d == 0) {
+        a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * i] = M;
+        a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * i + 1] = L;
+      }
+    }
   }
 }
 
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) 
   for (int k = 0; k < 2; ++k) {
     const int cc = tid + k * kThreads;
     if (cc < nact) {
-      const float w = expf(mv[k] - M);
+      const float w = __builtin_amdgcn_exp2f(mv[k] - M);  // maxima are in base 2
       w_s[cc] = w;
       L = fmaf(w, lv[k], L);
     }

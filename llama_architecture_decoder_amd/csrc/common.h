@@ -60,6 +60,10 @@ struct Vec16;
 template <>
 struct Vec16<float> {
   static constexpr int E = 4;
+  // the 16 bytes of 4 F32 values
+  __device__ __forceinline__ static u32x4 pack(const float *v) {
+    return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  }
   __device__ __forceinline__ static void unpack(const u32x4 &r, float *o) {
     o[0] = __uint_as_float(r.x);
     o[1] = __uint_as_float(r.y);
@@ -70,6 +74,15 @@ struct Vec16<float> {
 template <>
 struct Vec16<bf16_t> {
   static constexpr int E = 8;
+  // the 16 bytes of 8 values that are bf16 numbers widened to F32 (their low 16 bits are zero)
+  __device__ __forceinline__ static u32x4 pack(const float *v) {
+    u32x4 r;
+    r.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+    r.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
+    r.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xffff0000u);
+    r.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xffff0000u);
+    return r;
+  }
   __device__ __forceinline__ static void unpack(const u32x4 &r, float *o) {
     o[0] = __uint_as_float(r.x << 16);
     o[1] = __uint_as_float(r.x & 0xffff0000u);
@@ -134,6 +147,22 @@ __device__ __forceinline__ float xor16_sum(float v) {  // v + v of lane ^ 16
 __device__ __forceinline__ float xor32_sum(float v) {  // v + v of lane ^ 32
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Max over the lanes that share (lane % S), S = 16, 32 or 64 (whole rows or half-waves).
+template <int S>
+__device__ __forceinline__ float strided_max(float v) {
+  static_assert(S >= 16, "row-aligned groups");
+  if (S <= 16) v = xor16_max(v);
+  if (S <= 32) v = xor32_max(v);
+  return v;
 }
 // Sum over each aligned group of N lanes (N = 1, 2, 4, 8, 16, 32, 64); every lane of a group gets it.
 template <int N>
