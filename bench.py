@@ -8,9 +8,11 @@ call of llama_decode_step: embedding, 32 layers, final norm, LM head, argmax; th
 step on the device.  The 1.7B shape (F32, 512-token prompt, 512 decode steps) is measured alongside.
 
 Timing: W untimed warm-up steps, then K steps between two HIP events on the library's stream (with a
-device synchronisation on both sides).  A second, profiled pass of the same steps records HIP events
-around every launch (llama_profile_*) and gives the dominant kernel's average launch time for the
-roofline.  The CPU oracle is timed on the host on a bounded sample of the same workload.
+device synchronisation on both sides).  A second, profiled pass of the same steps has every kernel
+launch record a pair of HIP events from its own dispatch packet (llama_profile_*), which gives the
+dominant kernel's (the gate/up GEMV's) average duration for the roofline; `traffic` is the HBM bytes
+per launch that rocprofv3 counters measured for the same sources (profiles/decode_8b_hbm_traffic.*).
+The CPU oracle is timed on the host on a bounded sample of the same workload.
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -64,6 +66,25 @@ def kernel_bytes(cfg, cls, t=None):
     if cls == "attention":
         return 2 * kw * cfg.kvbytes * (t + 1) + (d + 2 * kw) * 4 + d * 4
     raise KeyError(cls)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled
+    by a plain copy of known size; None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        h = hashlib.sha256()
+        for p in rec["sources"]:
+            h.update(open(os.path.join(ROOT, p), "rb").read())
+        if h.hexdigest()[:16] != rec["sources_sha256_16"]:
+            return None
+        return int(rec["per_launch"][kernel]["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def build_model(cfg, lm, synth, max_seq, fill, keep_host):
@@ -152,6 +173,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
+                         "copy kernel of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the single-GPU decode step "
@@ -195,7 +219,8 @@ def main():
     avg_s = ms / n * 1e-3
     ach = kernel_bytes(cfg, dom) / avg_s
     roofline = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK, 4), "traffic": None, "kernel": "k_gemv<bf16, SwiGLU> (gate+up)",
+                "frac": round(ach / HBM_PEAK, 4), "traffic": measured_traffic("gate_up"),
+                "kernel": "k_gemv<bf16, SwiGLU> (gate+up)",
                 "bytes_per_launch": kernel_bytes(cfg, dom), "avg_launch_us": round(avg_s * 1e6, 3)}
 
     result = {
@@ -212,6 +237,17 @@ def main():
     }
     del dec
     torch.cuda.empty_cache()
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+        del src, dst
+        torch.cuda.empty_cache()
 
     if want_cpu:
         log(f"cpu baseline: oracle on {cfg.name}, ~{args.cpu_seconds:.0f}s sample")

@@ -125,7 +125,7 @@ int kv_cache_alloc(const llama_cfg *c, int32_t rows, int32_t max_seq, void *k_me
 /* Bytes of workspace for the given capacities; < 0 on error. */
 int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill);
 
-/* Bind `mem` (>= llama_workspace_bytes) as a workspace: clears its counters and status flag and uploads
+/* Bind `mem` (>= llama_workspace_bytes) as a workspace: clears its status flag and uploads
  * the rope cos/sin table for positions 0..max_seq-1 (angle t*inv_freq[i] rounded to F32, then cos, sin;
  * main.bend rot_at).  Synchronous: returns after the stream has finished the upload. */
 int llama_workspace_init(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill, void *mem,

@@ -180,17 +180,30 @@ Prof &prof() {
   return p;
 }
 struct ProfScope {
+  // events handed to the launches of this scope (recorded by their dispatch packets); if no launch
+  // used them, they are recorded on the stream around the scope instead
   int cls;
   hipStream_t s;
-  hipEvent_t e0 = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   ProfScope(int c, hipStream_t st) : cls(c), s(st) {
-    if (prof().on && (e0 = prof().get())) (void)hipEventRecord(e0, s);
+    if (!prof().on) return;
+    e0 = prof().get();
+    e1 = prof().get();
+    if (!e0 || !e1) {
+      e0 = e1 = nullptr;
+      return;
+    }
+    LaunchEvents &ev = launch_events();
+    ev.start = e0;
+    ev.stop = e1;
+    ev.used = false;
   }
   ~ProfScope() {
     if (!e0) return;
-    hipEvent_t e1 = prof().get();
-    if (!e1) return;
-    (void)hipEventRecord(e1, s);
+    LaunchEvents &ev = launch_events();
+    const bool used = ev.used;
+    ev = LaunchEvents();
+    if (!used) return;  // nothing was launched (an error path): drop the pair
     prof().marks.push_back({cls, {e0, e1}});
   }
 };

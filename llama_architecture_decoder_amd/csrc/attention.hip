@@ -348,12 +348,11 @@ template <typename KT, int D>
 static hipError_t launch_d(int g, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
   const int chunk = AttnShape<KT, D>::CHUNK;
   switch (g) {
-#define CASE(G)                                                                                        \
-  case G:                                                                                              \
-    hipLaunchKernelGGL((k_attn<KT, D, G>), grid, dim3(kThreads), 0, s, a);                             \
-    if (merge)                                                                                         \
-      hipLaunchKernelGGL((k_attn_merge<G, D>), dim3(G * D / 64, grid.y, grid.z), dim3(kThreads), 0, s, \
-                         a, chunk);                                                                    \
+#define CASE(G)                                                                                     \
+  case G:                                                                                           \
+    launch(k_attn<KT, D, G>, grid, dim3(kThreads), s, true, !merge, a);                             \
+    if (merge) launch(k_attn_merge<G, D>, dim3(G * D / 64, grid.y, grid.z), dim3(kThreads), s, false, \
+                      true, a, chunk);                                                              \
     break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(8)
 #undef CASE

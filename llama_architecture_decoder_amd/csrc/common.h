@@ -2,6 +2,7 @@
 // and the host entry points.  Written for gfx950 (CDNA4): 64-lane wavefronts, 256-thread blocks.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -232,6 +233,27 @@ struct AttnArgs {
   float scale;         // 1/sqrt(head)
   int pos[kMaxBatch];
 };
+
+// Kernel timing: when the host sets `start`/`stop`, the next launch records them from its own dispatch
+// packet (hipExtLaunchKernel), so they bracket exactly the kernel's execution; a launcher that issues
+// several kernels gives `start` to the first and `stop` to the last.  Cleared once used.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents &launch_events();
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, bool first, bool last, Args... args) {
+  LaunchEvents &ev = launch_events();
+  hipEvent_t e0 = first ? ev.start : nullptr, e1 = last ? ev.stop : nullptr;
+  if (e0 || e1) {
+    ev.used = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
 
 // host-side launchers (one per kernel family); return hipSuccess or the launch error
 hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, int grid_cap, hipStream_t s);

@@ -264,11 +264,11 @@ __global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, 
 }
 
 template <typename WT, int EPI, bool NORM>
-static hipError_t dispatch_kch(int kch, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t dispatch_kch(int kch, dim3 grid, const GemvArgs &a, hipStream_t s, bool last) {
   switch (kch) {
 #define CASE(k)                                                                        \
   case k:                                                                              \
-    hipLaunchKernelGGL((k_gemv<WT, k, EPI, NORM>), grid, dim3(kThreads), 0, s, a);     \
+    launch(k_gemv<WT, k, EPI, NORM>, grid, dim3(kThreads), s, true, last, a);          \
     break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
@@ -300,14 +300,16 @@ static hipError_t launch_typed(GemvEpi epi, bool norm, GemvArgs a, int grid_cap,
   if (epi == EPI_ARGMAX && grid > kLmGridMax) grid = kLmGridMax;
   if (grid < 1) grid = 1;
   const dim3 g(grid);
-  if (epi == EPI_STORE && norm) return dispatch_kch<WT, EPI_STORE, true>(kch, g, a, s);
-  if (epi == EPI_STORE && !norm) return dispatch_kch<WT, EPI_STORE, false>(kch, g, a, s);
-  if (epi == EPI_RESID && !norm) return dispatch_kch<WT, EPI_RESID, false>(kch, g, a, s);
-  if (epi == EPI_SWIGLU && norm) return dispatch_kch<WT, EPI_SWIGLU, true>(kch, g, a, s);
+  if (epi == EPI_STORE && norm) return dispatch_kch<WT, EPI_STORE, true>(kch, g, a, s, true);
+  if (epi == EPI_STORE && !norm) return dispatch_kch<WT, EPI_STORE, false>(kch, g, a, s, true);
+  if (epi == EPI_RESID && !norm) return dispatch_kch<WT, EPI_RESID, false>(kch, g, a, s, true);
+  if (epi == EPI_SWIGLU && norm) return dispatch_kch<WT, EPI_SWIGLU, true>(kch, g, a, s, true);
   if (epi == EPI_ARGMAX && norm) {
-    hipError_t e = dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s);
-    if (e != hipSuccess || a.next == nullptr) return e;
-    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, a.part_v, a.part_i, grid, a.next);
+    const bool reduce = a.next != nullptr;
+    hipError_t e = dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s, !reduce);
+    if (e != hipSuccess || !reduce) return e;
+    launch(k_argmax_final, dim3(1), dim3(kThreads), s, false, true, (const float *)a.part_v, (const int *)a.part_i,
+           grid, a.next);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

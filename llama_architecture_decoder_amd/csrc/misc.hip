@@ -41,12 +41,17 @@ hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int 
   const int E = wdtype == LLAMA_BF16 ? 8 : 4;
   const dim3 grid((dim / E + kThreads - 1) / kThreads, B);
   if (wdtype == LLAMA_BF16)
-    hipLaunchKernelGGL((k_embed<bf16_t>), grid, dim3(kThreads), 0, s, tokens, reinterpret_cast<const bf16_t *>(emb),
-                       dim, vocab, x, status);
+    launch(k_embed<bf16_t>, grid, dim3(kThreads), s, true, true, tokens, reinterpret_cast<const bf16_t *>(emb), dim,
+           vocab, x, status);
   else
-    hipLaunchKernelGGL((k_embed<float>), grid, dim3(kThreads), 0, s, tokens, reinterpret_cast<const float *>(emb),
-                       dim, vocab, x, status);
+    launch(k_embed<float>, grid, dim3(kThreads), s, true, true, tokens, reinterpret_cast<const float *>(emb), dim,
+           vocab, x, status);
   return hipGetLastError();
+}
+
+LaunchEvents &launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
 }
 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
