@@ -101,8 +101,10 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, total;
+  size_t status, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, total;
   int nch;
+  int lm_ld;  // per-row stride of the LM head's block winners
+  int mpad;   // token rows of the split operands (max_batch rounded up to 16)
 };
 
 WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill) {
@@ -126,8 +128,14 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.m = take(sizeof(float) * (size_t)max_batch * d.f);
   L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
   L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
-  L.lm_v = take(sizeof(float) * (size_t)max_batch * kLmGridMax);
-  L.lm_i = take(sizeof(int) * (size_t)max_batch * kLmGridMax);
+  L.lm_ld = kLmGridMax;
+  if (max_batch > 1 && gemm_skinny_blocks((int)d.vocab) > L.lm_ld) L.lm_ld = gemm_skinny_blocks((int)d.vocab);
+  L.lm_v = take(sizeof(float) * (size_t)max_batch * L.lm_ld);
+  L.lm_i = take(sizeof(int) * (size_t)max_batch * L.lm_ld);
+  L.mpad = max_batch > 1 ? (max_batch + 15) / 16 * 16 : 0;
+  const int64_t kmax = d.dim > d.f ? d.dim : d.f;
+  L.xhi = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
+  L.xlo = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
   L.total = o;
   return L;
 }
@@ -279,6 +287,98 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
   return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().gemv_grid, x.s));
 }
 
+// Several token rows with bf16 weights: each projection is one matrix-core product over all rows (the
+// weights stream once per step instead of once per row); operands are split into bf16 hi/lo first.
+int run_step_rows(const Ctx &x, AttnArgs aa, int nch_launch, int B, float *logits, int32_t *next, bool want_head) {
+  const Dims &d = x.d;
+  const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f, V = (int)d.vocab;
+  const int mpad = (B + 15) / 16 * 16;
+  float *xs = x.at<float>(x.L.x);
+  float *qkv = x.at<float>(x.L.qkv);
+  float *att = x.at<float>(x.L.attn);
+  float *mm = x.at<float>(x.L.m);
+  bf16_t *xhi = x.at<bf16_t>(x.L.xhi), *xlo = x.at<bf16_t>(x.L.xlo);
+  const int wdt = x.c->weight_dtype;
+  const int qkv_stride = H + 2 * KW;
+  auto split = [&](const float *in, int ldin, const void *gain, int K) {
+    SplitArgs sa = {};
+    sa.x = in;
+    sa.ldin = ldin;
+    sa.gain = gain;
+    sa.eps = x.c->eps;
+    sa.K = K;
+    sa.M = B;
+    sa.xhi = xhi;
+    sa.xlo = xlo;
+    sa.ldx = K;
+    return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
+  };
+  auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
+                  int ldy, const float *res, bool last) {
+    GemmArgs ga = {};
+    ga.xhi = xhi;
+    ga.xlo = xlo;
+    ga.ldx = K;
+    ga.w[0] = w0;
+    ga.w[1] = w1;
+    ga.w[2] = w2;
+    ga.rs[0] = 0;
+    ga.rs[1] = r1;
+    ga.rs[2] = r2;
+    ga.rs[3] = N;
+    ga.N = N;
+    ga.K = K;
+    ga.M = B;
+    ga.y = y;
+    ga.ldy = ldy;
+    ga.res = res;
+    ga.ldres = ldy;
+    ga.part_v = x.at<float>(x.L.lm_v);
+    ga.part_i = x.at<int>(x.L.lm_i);
+    ga.part_ld = x.L.lm_ld;
+    return hip_rc(launch_gemm_skinny(epi, ga, x.s, last));
+  };
+  int rc;
+  for (int l = 0; l < (int)d.layers; ++l) {
+    const llama_layer_w &lw = x.w->layers[l];
+    {
+      ProfScope ps(LLAMA_K_QKV, x.s);
+      if ((rc = split(xs, H, lw.ln1, H))) return rc;
+      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, true))) return rc;
+    }
+    aa.kc = layer_cache(x, x.kv->k, l);
+    aa.vc = layer_cache(x, x.kv->v, l);
+    {
+      ProfScope ps(LLAMA_K_ATTN, x.s);
+      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_O, x.s);
+      if ((rc = split(att, H, nullptr, H))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, true))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_GATE_UP, x.s);
+      if ((rc = split(xs, H, lw.ln2, H))) return rc;
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr, true))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_DOWN, x.s);
+      if ((rc = split(mm, F, nullptr, F))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true))) return rc;
+    }
+  }
+  if (!want_head || (!logits && !next)) return LLAMA_OK;
+  ProfScope ps(LLAMA_K_LM_HEAD, x.s);
+  if ((rc = split(xs, H, x.w->final_norm, H))) return rc;
+  const void *wl = x.c->tied_lm_head ? x.w->emb : x.w->lm_head;
+  if ((rc = gemm(EPI_ARGMAX, wl, wl, wl, V, V, V, H, logits, V, nullptr, next == nullptr))) return rc;
+  if (next)
+    return hip_rc(launch_argmax_final(x.at<float>(x.L.lm_v), x.at<int>(x.L.lm_i), gemm_skinny_blocks(V), x.L.lm_ld, B,
+                                      next, x.s));
+  return LLAMA_OK;
+}
+
 // One step for B rows at positions pos[b] of cache rows row0 + b.  want_head = run the LM head.
 int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int row0, float *logits, int32_t *next,
              bool want_head, float *trace) {
@@ -318,6 +418,9 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   aa.nch = x.L.nch;
   aa.scale = 1.0f / sqrtf((float)d.head);
   for (int b = 0; b < B; ++b) aa.pos[b] = pos[b];
+
+  if (B > 1 && gemm_skinny_supported(wdt, H, B) && gemm_skinny_supported(wdt, F, B) && !trace)
+    return run_step_rows(x, aa, nch_launch, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
   for (int l = 0; l < (int)d.layers; ++l) {

@@ -217,6 +217,32 @@ struct GemvArgs {
   int32_t *next;       // nullable: argmax written by a one-block reduce
 };
 
+// several token rows at once (matrix cores): operands split into bf16 hi/lo by k_split
+struct SplitArgs {
+  const float *x;      // [M][ldin] F32 rows
+  int ldin;
+  const void *gain;    // RMSNorm gains [K] (weight type) when normalising
+  float eps;
+  int K, M;            // row length, real rows (rows M..mpad-1 are written as zeros)
+  bf16_t *xhi, *xlo;   // [mpad][ldx]
+  int ldx;
+};
+
+struct GemmArgs {
+  const bf16_t *xhi, *xlo;  // [mpad][ldx] operands from k_split
+  int ldx;
+  const void *w[3];    // as GemvArgs: stacked row blocks (rs), or w[0] = gate, w[1] = up
+  int rs[4];
+  int N, K, M;
+  float *y;            // [M][ldy]
+  int ldy;
+  const float *res;    // EPI_RESID: y = res + X W^T
+  int ldres;
+  float *part_v;       // EPI_ARGMAX: [M][part_ld] per-block winners
+  int *part_i;
+  int part_ld;
+};
+
 struct AttnArgs {
   const float *qkv;    // [B][qkv_stride]: q [dim], k [kvw], v [kvw] before RoPE
   int qkv_stride;
@@ -261,6 +287,15 @@ int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is in
 hipError_t launch_attention(int kvdtype, int head, int g, AttnArgs a, int B, int nch_launch, hipStream_t s);
 int attention_supported(int head, int g);
 int attention_chunk(int kvdtype, int head);  // positions per attention block (fixed per cache type and head)
+int gemm_skinny_supported(int wdtype, int K, int M);
+int gemm_skinny_blocks(int N);
+// a split is always followed by its product: the split takes a timing scope's start event, the
+// product (and, for the LM head, the argmax reduce) its stop event
+hipError_t launch_split(int gdtype, bool norm, const SplitArgs &a, int mpad, hipStream_t s);
+hipError_t launch_gemm_skinny(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
+// argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]
+hipError_t launch_argmax_final(const float *part_v, const int *part_i, int n, int ld, int rows, int32_t *next,
+                               hipStream_t s);
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
                         int *status, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);

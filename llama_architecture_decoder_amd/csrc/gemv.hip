@@ -214,27 +214,31 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 // The per-block winners of the LM head, reduced by one block in a second launch: larger value wins,
 // equal values keep the lower index, so the result is the first index of the largest logit whatever
 // the order of the blocks (main.bend argmax).  Every logit NaN: index 0, as an empty list gives.
-__global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, const int *part_i, int n,
+__global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, const int *part_i, int n, int ld,
                                                          int32_t *next) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  part_v += (size_t)blockIdx.x * ld;
+  part_i += (size_t)blockIdx.x * ld;
   __shared__ float sv[4];
   __shared__ int si[4];
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  constexpr int PER = kLmGridMax / kThreads;  // every partial loaded before any compare
-  float vv[PER];
-  int iv[PER];
+  constexpr int PER = 8;  // partials per thread per pass, loaded before any compare
+  for (int base = 0; base < n; base += PER * kThreads) {
+    float vv[PER];
+    int iv[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int ix = min(tid + k * kThreads, n - 1);
-    vv[k] = part_v[ix];
-    iv[k] = part_i[ix];
-  }
+    for (int k = 0; k < PER; ++k) {
+      const int ix = min(base + tid + k * kThreads, n - 1);
+      vv[k] = part_v[ix];
+      iv[k] = part_i[ix];
+    }
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    if (tid + k * kThreads < n && (vv[k] > bv || (vv[k] == bv && iv[k] < bi))) {
-      bv = vv[k];
-      bi = iv[k];
+    for (int k = 0; k < PER; ++k) {
+      if (base + tid + k * kThreads < n && (vv[k] > bv || (vv[k] == bv && iv[k] < bi))) {
+        bv = vv[k];
+        bi = iv[k];
+      }
     }
   }
 #pragma unroll
@@ -259,8 +263,14 @@ __global__ __launch_bounds__(kThreads) void k_argmax_final(const float *part_v, 
         fv = sv[w];
         fi = si[w];
       }
-    *next = (fi == 0x7fffffff) ? 0 : fi;
+    next[blockIdx.x] = (fi == 0x7fffffff) ? 0 : fi;
   }
+}
+
+hipError_t launch_argmax_final(const float *part_v, const int *part_i, int n, int ld, int rows, int32_t *next,
+                               hipStream_t s) {
+  launch(k_argmax_final, dim3(rows), dim3(kThreads), s, false, true, part_v, part_i, n, ld, next);
+  return hipGetLastError();
 }
 
 template <typename WT, int EPI, bool NORM>
@@ -308,9 +318,7 @@ static hipError_t launch_typed(GemvEpi epi, bool norm, GemvArgs a, int grid_cap,
     const bool reduce = a.next != nullptr;
     hipError_t e = dispatch_kch<WT, EPI_ARGMAX, true>(kch, g, a, s, !reduce);
     if (e != hipSuccess || !reduce) return e;
-    launch(k_argmax_final, dim3(1), dim3(kThreads), s, false, true, (const float *)a.part_v, (const int *)a.part_i,
-           grid, a.next);
-    return hipGetLastError();
+    return launch_argmax_final(a.part_v, a.part_i, grid, grid, 1, a.next, s);
   }
   return hipErrorInvalidValue;
 }
