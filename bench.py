@@ -146,6 +146,59 @@ def time_decode(dec, cfg, p0, steps, warmup, first_tok, profile=False):
     return e0.elapsed_time(e1), (h1 - h0) * 1e3, prof
 
 
+def batched_step_bytes(cfg, positions):
+    """Algorithmic HBM bytes of one batched decode step: the weights once, one embedding row per row,
+    and every row's K/V reads (positions 0..t-1) and append."""
+    b = token_bytes(cfg, 0) - cfg.dim * cfg.wbytes - cfg.layers * 2 * cfg.kvw * cfg.kvbytes
+    kvrow = cfg.kvw * cfg.kvbytes
+    for t in positions:
+        b += cfg.dim * cfg.wbytes + cfg.layers * 2 * kvrow * (int(t) + 1)
+    return b
+
+
+def time_batched(cfg, lm, synth, dev_weights, steps, warmup):
+    """Batch-`cfg.batch` decode: every row pre-filled (on the device) to its own random length, then
+    `steps` greedy steps of all rows together."""
+    import numpy as np
+    import torch
+    B = cfg.batch
+    lens = synth.row_lengths(cfg).astype(np.int64)
+    dec = lm.Decoder(cfg, None, rows=B, max_seq=cfg.max_seq, weights=dev_weights)
+    log(f"{cfg.name}: cache {2 * dec.kv.k.numel() * dec.kv.k.element_size() / 1e9:.1f} GB; filling rows to "
+        f"lengths {int(lens.min())}..{int(lens.max())}")
+    t0 = time.time()
+    synth.fill_cache_device(cfg, dec.kv.k.data_ptr(), dec.kv.v.data_ptr(), B, cfg.max_seq, lens,
+                            stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: filled in {time.time() - t0:.1f}s")
+    first = torch.from_numpy(synth.tokens(cfg, "bench/rows", B)).cuda()
+    tok = first.clone()
+    for i in range(warmup):
+        dec.decode(tok, [int(p) + i for p in lens], None, tok)
+    torch.cuda.synchronize()
+    tok.copy_(first)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        dec.decode(tok, [int(p) + i for p in lens], None, tok)
+    e1.record()
+    torch.cuda.synchronize()
+    if dec.status() != 0:
+        raise RuntimeError("device status flag set during the batched steps")
+    ms = e0.elapsed_time(e1) / steps
+    bytes_step = sum(batched_step_bytes(cfg, lens + i) for i in range(steps)) / steps
+    out = {"workload": f"{cfg.name}: llama31_8b-shaped decode, batch {B} rows, bf16 weights and KV, MaxSeq "
+                       f"{cfg.max_seq}, row lengths uniform in [{cfg.len_lo}, {cfg.len_hi}] (pre-filled random), "
+                       f"{steps} steps", "value": round(B * 1e3 / ms, 2), "unit": "tokens/s",
+           "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup, "dtype": "bf16",
+           "hbm_fraction": round(bytes_step / (ms * 1e-3) / HBM_PEAK, 4), "bytes_per_step": int(bytes_step),
+           "row_lengths": [int(lens.min()), int(lens.max())]}
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
     import numpy as np
     import oracle
@@ -235,6 +288,10 @@ def main():
         "host_ms_per_step": round(host_ms / steps, 4),
         "roofline": roofline, "kernels": kernels,
     }
+    if not args.no_secondary:
+        c5 = configs.LLAMA31_8B_LONG
+        result["batched"] = time_batched(c5, lm, synth, dec.w, c5.decode_steps, args.warmup)
+        log(f"batch {c5.batch}: {result['batched']['value']:.1f} tok/s, hbm {result['batched']['hbm_fraction']:.3f}")
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:

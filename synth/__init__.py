@@ -185,6 +185,51 @@ def fill_cache_rows(cfg: Cfg, kc: np.ndarray, vc: np.ndarray, row: int, length: 
             kv_fill_head(cfg, l, row, "v", j, 0, length, base_seed, out=vc[l, cr, j, :length])
 
 
+_dev_lib = None
+
+
+def _load_dev():
+    global _dev_lib
+    if _dev_lib is not None:
+        return _dev_lib
+    from . import build as _b
+    if not os.path.exists(_b.DEV_LIB):
+        raise RuntimeError(f"{_b.DEV_LIB} is not built (python synth/build.py)")
+    lib = ctypes.CDLL(_b.DEV_LIB)
+    lib.synth_dev_fill_kv.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.synth_dev_fill_kv.restype = ctypes.c_int
+    _dev_lib = lib
+    return lib
+
+
+def fill_cache_device(cfg: Cfg, k_ptr: int, v_ptr: int, rows: int, max_seq: int, lengths, layers=None,
+                      base_seed: int = 0, stream: int = 0, row_keys=None) -> None:
+    """Device-side fill of device caches laid out [layers][rows][kv][max_seq][head]: positions
+    0..lengths[r]-1 of cache row r get the bytes fill_cache_rows writes for row key row_keys[r]
+    (default r).  Asynchronous on `stream` (a hipStream_t as an int, 0 = the null stream)."""
+    lib = _load_dev()
+    D, kv = cfg.head, cfg.kv
+    esize = 4 if cfg.kvdtype == "f32" else 2
+    step = kv_step(cfg)
+    nl = cfg.layers if layers is None else layers
+    seeds = (ctypes.c_uint32 * kv)()
+    for l in range(nl):
+        for r in range(rows):
+            key = r if row_keys is None else int(row_keys[r])
+            n = int(lengths[r]) * D
+            if n == 0:
+                continue
+            off = ((l * rows + r) * kv) * max_seq * D * esize
+            for which, base in (("k", k_ptr), ("v", v_ptr)):
+                for j in range(kv):
+                    seeds[j] = hash32(stream_seed(f"{cfg.weights_key}/kvfill/r{key}/L{l}/{which}/h{j}", base_seed))
+                rc = lib.synth_dev_fill_kv(seeds, kv, base + off, max_seq * D, n, step, int(cfg.kvdtype != "f32"),
+                                           stream)
+                if rc != 0:
+                    raise RuntimeError(f"synth_dev_fill_kv failed ({rc}) at layer {l} row {r} {which}")
+
+
 __all__ = ["configs", "Cfg", "make_weights", "make_layer", "tokens", "row_lengths", "kv_fill_head",
            "fill_cache_rows", "normal", "stream_seed", "hash32", "uniform", "LAYER_TENSORS", "layer_shapes",
-           "np_kv_dtype", "kv_step", "int_range"]
+           "np_kv_dtype", "kv_step", "int_range", "fill_cache_device"]

@@ -75,3 +75,62 @@ def test_batched_rows_parity(name, layers, rows, max_seq):
         toks = new  # teacher forcing
     assert dec.status() == 0
     log(f"{name} B={rows}: worst max|d| {worst:.3g}")
+
+
+@pytest.mark.timeout(300)
+def test_device_fill_matches_host_fill():
+    """The device cache filler writes the host generator's bytes (sampled layers, rows and heads)."""
+    cfg = configs.truncated(configs.LLAMA31_8B_LONG, 2)
+    rows, max_seq = 3, 1024
+    lens = [1000, 0, 17]
+    k = torch.full((cfg.layers, rows, cfg.kv, max_seq, cfg.head), 7.0, dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, -3.0)
+    synth.fill_cache_device(cfg, k.data_ptr(), v.data_ptr(), rows, max_seq, lens, row_keys=[5, 6, 7])
+    torch.cuda.synchronize()
+    gk = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for l in range(cfg.layers):
+        for r, n in enumerate(lens):
+            for j in (0, cfg.kv - 1):
+                hk = synth.kv_fill_head(cfg, l, 5 + r, "k", j, 0, n)
+                hv = synth.kv_fill_head(cfg, l, 5 + r, "v", j, 0, n)
+                assert np.array_equal(gk[l, r, j, :n], hk), (l, r, j)
+                assert np.array_equal(gv[l, r, j, :n], hv), (l, r, j)
+                # positions past the length are untouched
+                assert (gk[l, r, j, n:] == 0x40E0).all() and (gv[l, r, j, n:] == 0xC040).all()
+
+
+@pytest.mark.timeout(900)
+def test_long_context_batch32_sampled_rows():
+    """The batch-32 long-context workload at its full size (32 layers, MaxSeq 32768, lengths uniform in
+    [8192, 32000]) in the launch configuration the benchmark times; sampled rows are recomputed alone by
+    the oracle (rows are independent)."""
+    import llama_architecture_decoder_amd as lm
+    cfg = configs.LLAMA31_8B_LONG
+    B = cfg.batch
+    lens = synth.row_lengths(cfg).astype(np.int64)
+    w = weights(configs.LLAMA31_8B)  # the same weight streams (one family)
+    dec = lm.Decoder(cfg, w, rows=B, max_seq=cfg.max_seq)
+    log(f"long batch: lengths {int(lens.min())}..{int(lens.max())}")
+    synth.fill_cache_device(cfg, dec.kv.k.data_ptr(), dec.kv.v.data_ptr(), B, cfg.max_seq, lens,
+                            stream=torch.cuda.current_stream().cuda_stream)
+    toks = synth.tokens(cfg, "bench/rows", B)
+    logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    dec.decode(torch.from_numpy(toks).cuda(), [int(p) for p in lens], logits, nxt)
+    torch.cuda.synchronize()
+    assert dec.status() == 0
+    got = logits.cpu().numpy()
+    gid = nxt.cpu().numpy()
+    sample = [int(np.argmax(lens)), int(np.argmin(lens))]
+    for r in sample:
+        n = int(lens[r])
+        om = oracle.Model(cfg, w, rows=1, max_seq=n + 1)
+        synth.fill_cache_rows(cfg, om.kc, om.vc, r, n, cache_row=0)
+        rid, ref, _, _ = om.decode(int(toks[r]), n, row=0)
+        d, rel = check_logits(cfg, got[r], ref, f"row {r} pos {n}")
+        check_argmax(cfg, int(gid[r]), ref, f"row {r} pos {n}")
+        log(f"long batch row {r} at {n}: max|d| {d:.3g} rel {rel:.3g}")
+        del om
+    del dec
+    torch.cuda.empty_cache()
