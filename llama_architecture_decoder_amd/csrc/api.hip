@@ -107,9 +107,18 @@ struct WsLayout {
   int mpad;   // token rows of the split operands (max_batch rounded up to 16)
 };
 
+// the matrix-core prefill: bf16 weights and cache, head 64 or 128, K of every product a multiple of 32
+bool prefill_tiled_ok(const llama_cfg *c) {
+  return c->weight_dtype == LLAMA_BF16 && c->kv_dtype == LLAMA_BF16 && (c->half == 32 || c->half == 64) &&
+         gemm_skinny_supported(LLAMA_BF16, (int)(2 * c->half * c->kv * c->g), 1) &&
+         gemm_skinny_supported(LLAMA_BF16, c->f, 1);
+}
+
 WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill) {
-  (void)max_prefill;
   const Dims d = dims_of(c);
+  // activation rows: a decode call's batch, or a prefill chunk when the matrix-core prefill runs
+  const int32_t prows = prefill_tiled_ok(c) ? max_prefill : 0;
+  const size_t rows = (size_t)(max_batch > prows ? max_batch : prows);
   WsLayout L;
   const int chunk = attention_chunk(c->kv_dtype, (int)d.head);
   L.nch = (int)((max_seq + chunk - 1) / chunk);
@@ -122,10 +131,10 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.status = take(64);
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
-  L.x = take(sizeof(float) * (size_t)max_batch * d.dim);
-  L.qkv = take(sizeof(float) * (size_t)max_batch * (d.dim + 2 * d.kvw));
-  L.attn = take(sizeof(float) * (size_t)max_batch * d.dim);
-  L.m = take(sizeof(float) * (size_t)max_batch * d.f);
+  L.x = take(sizeof(float) * rows * d.dim);
+  L.qkv = take(sizeof(float) * rows * (d.dim + 2 * d.kvw));
+  L.attn = take(sizeof(float) * rows * d.dim);
+  L.m = take(sizeof(float) * rows * d.f);
   L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
   L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
   L.lm_ld = kLmGridMax;
@@ -133,6 +142,7 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.lm_v = take(sizeof(float) * (size_t)max_batch * L.lm_ld);
   L.lm_i = take(sizeof(int) * (size_t)max_batch * L.lm_ld);
   L.mpad = max_batch > 1 ? (max_batch + 15) / 16 * 16 : 0;
+  if (prows > 0 && gemm_tiled_rows(prows) > L.mpad) L.mpad = gemm_tiled_rows(prows);
   const int64_t kmax = d.dim > d.f ? d.dim : d.f;
   L.xhi = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
   L.xlo = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
@@ -379,6 +389,112 @@ int run_step_rows(const Ctx &x, AttnArgs aa, int nch_launch, int B, float *logit
   return LLAMA_OK;
 }
 
+// Prompt positions pos0 .. pos0+S-1 of cache row `row`, all S at once per layer (S <= the workspace's
+// max_prefill): matrix-core products over the S rows, RoPE + append of the S positions, causal
+// attention over the cache.  The LM head runs on the last position only when want_head.
+int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int row, float *logits, int32_t *next,
+                     bool want_head) {
+  const Dims &d = x.d;
+  const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f;
+  const int mpad = gemm_tiled_rows(S);
+  float *xs = x.at<float>(x.L.x);
+  float *qkv = x.at<float>(x.L.qkv);
+  float *att = x.at<float>(x.L.attn);
+  float *mm = x.at<float>(x.L.m);
+  bf16_t *xhi = x.at<bf16_t>(x.L.xhi), *xlo = x.at<bf16_t>(x.L.xlo);
+  const int wdt = x.c->weight_dtype;
+  const int qkv_stride = H + 2 * KW;
+  int rc;
+  {
+    ProfScope ps(LLAMA_K_EMBED, x.s);
+    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, S, x.at<int>(x.L.status), x.s));
+  }
+  if (rc) return rc;
+  auto split = [&](const float *in, const void *gain, int K) {
+    SplitArgs sa = {};
+    sa.x = in;
+    sa.ldin = K;
+    sa.gain = gain;
+    sa.eps = x.c->eps;
+    sa.K = K;
+    sa.M = S;
+    sa.xhi = xhi;
+    sa.xlo = xlo;
+    sa.ldx = K;
+    return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
+  };
+  auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
+                  int ldy, const float *res) {
+    GemmArgs ga = {};
+    ga.xhi = xhi;
+    ga.xlo = xlo;
+    ga.ldx = K;
+    ga.w[0] = w0;
+    ga.w[1] = w1;
+    ga.w[2] = w2;
+    ga.rs[0] = 0;
+    ga.rs[1] = r1;
+    ga.rs[2] = r2;
+    ga.rs[3] = N;
+    ga.N = N;
+    ga.K = K;
+    ga.M = S;
+    ga.y = y;
+    ga.ldy = ldy;
+    ga.res = res;
+    ga.ldres = ldy;
+    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true));
+  };
+  PrefillArgs pa = {};
+  pa.qkv = qkv;
+  pa.qkv_stride = qkv_stride;
+  pa.kv = (int)d.kv;
+  pa.g = (int)d.g;
+  pa.heads = (int)(d.kv * d.g);
+  pa.half = (int)d.half;
+  pa.max_seq = x.kv->max_seq;
+  pa.row = row;
+  pa.pos0 = pos0;
+  pa.S = S;
+  pa.rope_cs = x.at<float>(x.L.rope_cs);
+  pa.rope_sn = x.at<float>(x.L.rope_sn);
+  pa.out = att;
+  pa.out_stride = H;
+  pa.scale = 1.0f / sqrtf((float)d.head);
+  for (int l = 0; l < (int)d.layers; ++l) {
+    const llama_layer_w &lw = x.w->layers[l];
+    {
+      ProfScope ps(LLAMA_K_QKV, x.s);
+      if ((rc = split(xs, lw.ln1, H))) return rc;
+      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr))) return rc;
+    }
+    pa.kc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->k, l));
+    pa.vc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->v, l));
+    {
+      ProfScope ps(LLAMA_K_ATTN, x.s);
+      if ((rc = hip_rc(launch_rope_rows(pa, x.s, true, false)))) return rc;
+      if ((rc = hip_rc(launch_attn_prefill(pa, x.s, false, true)))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_O, x.s);
+      if ((rc = split(att, nullptr, H))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_GATE_UP, x.s);
+      if ((rc = split(xs, lw.ln2, H))) return rc;
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr))) return rc;
+    }
+    {
+      ProfScope ps(LLAMA_K_DOWN, x.s);
+      if ((rc = split(mm, nullptr, F))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs))) return rc;
+    }
+  }
+  if (!want_head || (!logits && !next)) return LLAMA_OK;
+  return run_lm_head(x, xs + (size_t)(S - 1) * H, 0, logits, next);
+}
+
 // One step for B rows at positions pos[b] of cache rows row0 + b.  want_head = run the LM head.
 int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int row0, float *logits, int32_t *next,
              bool want_head, float *trace) {
@@ -589,6 +705,7 @@ int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max
   if (max_batch <= 0 || max_batch > kMaxBatch || max_seq <= 0 || max_prefill < 0) return LLAMA_E_SHAPE;
   if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * attention_chunk(c->kv_dtype, 2 * c->half))
     return LLAMA_E_UNSUPPORTED;
+  if (max_prefill > 65535) return LLAMA_E_UNSUPPORTED;  // one grid row per prompt position
   return (int64_t)ws_layout(c, max_batch, max_seq, max_prefill).total;
 }
 
@@ -684,6 +801,17 @@ int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv
   Ctx x;
   if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
   if ((int64_t)pos0 + S > ws->max_seq) return LLAMA_E_POS;
+  if (prefill_tiled_ok(c) && ws->max_prefill >= 2 && S >= 2) {
+    // chunks of at most max_prefill positions, each attending to everything before it in the cache
+    for (int32_t c0 = 0; c0 < S; c0 += ws->max_prefill) {
+      const int32_t n = S - c0 < ws->max_prefill ? S - c0 : ws->max_prefill;
+      const bool last = c0 + n == S;
+      rc = run_prefill_rows(x, tokens + c0, n, pos0 + c0, row, last ? logits_last : nullptr, last ? next : nullptr,
+                            last);
+      if (rc) return rc;
+    }
+    return LLAMA_OK;
+  }
   // one position after another through the decode kernels (main.bend forward_pre per prompt
   // position); only the last runs the final norm, the LM head and the argmax
   for (int i = 0; i < S; ++i) {

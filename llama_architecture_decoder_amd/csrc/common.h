@@ -260,6 +260,18 @@ struct AttnArgs {
   int pos[kMaxBatch];
 };
 
+// Prefill of S positions of one cache row (bf16 cache): RoPE + append and causal attention
+struct PrefillArgs {
+  float *qkv;          // [S][qkv_stride]: q [dim] (rotated in place), k [kvw], v [kvw]
+  int qkv_stride;
+  bf16_t *kc, *vc;     // this layer's cache: [rows][kv][max_seq][head]
+  int kv, g, heads, half, max_seq, row, pos0, S;
+  const float *rope_cs, *rope_sn;  // [max_seq][half]
+  float *out;          // [S][out_stride] attention output, heads concatenated
+  int out_stride;
+  float scale;         // 1/sqrt(head)
+};
+
 // Kernel timing: when the host sets `start`/`stop`, the next launch records them from its own dispatch
 // packet (hipExtLaunchKernel), so they bracket exactly the kernel's execution; a launcher that issues
 // several kernels gives `start` to the first and `stop` to the last.  Cleared once used.
@@ -293,6 +305,11 @@ int gemm_skinny_blocks(int N);
 // product (and, for the LM head, the argmax reduce) its stop event
 hipError_t launch_split(int gdtype, bool norm, const SplitArgs &a, int mpad, hipStream_t s);
 hipError_t launch_gemm_skinny(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
+// many token rows (prefill): 128 x 128 tiles; the operands need gemm_tiled_rows(M) rows (zero-padded)
+int gemm_tiled_rows(int M);
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
+hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last);
+hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 // argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]
 hipError_t launch_argmax_final(const float *part_v, const int *part_i, int n, int ld, int rows, int32_t *next,
                                hipStream_t s);

@@ -1,0 +1,405 @@
+// Prefill of S prompt positions at once (bf16 weights and cache) on gfx950 matrix cores.
+//
+// The prompt is the decode step applied to positions pos0 .. pos0+S-1 in order, where position i sees
+// cache positions 0 .. pos0+i (main.bend forward_pre per prompt position; nest prefill.linnet states the
+// same pass with the causal `seen` mask).  All S positions of a layer are done together:
+//   * projections: Y[S][N] = X[S][K] W[N][K]^T as tiled MFMA products (X = bf16 hi + lo of the F32
+//     activations, so the products carry about 16 significant bits of X and W is exact);
+//   * RoPE + cache append for all S positions (the decode kernels' arithmetic, element for element);
+//   * causal grouped-query attention over the cache, flash style: key tiles of 64 positions stream
+//     through LDS once per (32-position query tile, kv head) and serve the g query heads of the group;
+//     scores and probabilities stay in registers (softmax with a running maximum, base 2).
+#include "common.h"
+
+namespace lm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_32x32x16_bf16: A (32 x 16) lane l holds A[l%32][8(l/32) .. +8]; B (16 x 32) lane l holds
+// B[8(l/32) .. +8][l%32]; C (32 x 32) lane l holds C[8(r/4) + 4(l/32) + r%4][l%32], r < 16.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------ tiled product ----
+// Block: 128 token rows x 128 weight rows (SwiGLU: 64 gate rows + the same 64 up rows), K in steps of
+// 32 through double-buffered LDS.  Wave (wm, wn) owns 64 x 64 of the block as 2 x 2 tiles of 32 x 32.
+constexpr int kTM = 128, kTN = 128, kTK = 32;
+constexpr int kRowA = kTK + 8;  // LDS row of a tile: 40 bf16 = 80 bytes (16-byte reads of 16 rows hit distinct banks)
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  __shared__ __attribute__((aligned(16))) bf16_t s_a[2][2][kTM * kRowA];  // [buffer][hi, lo]
+  __shared__ __attribute__((aligned(16))) bf16_t s_b[2][kTN * kRowA];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kTM;
+  const int n0 = blockIdx.x * (SW ? kTN / 2 : kTN);
+
+  // staging: 16-byte chunk c = tid + 256 i of a 128 x 32 tile is row c / 4, columns 8 (c % 4) .. +8
+  const bf16_t *ga_hi[2], *ga_lo[2], *gb[2];
+  int lds_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i, r = c >> 2, cc = (c & 3) * 8;
+    lds_off[i] = r * kRowA + cc;
+    ga_hi[i] = a.xhi + (size_t)(m0 + r) * a.ldx + cc;
+    ga_lo[i] = a.xlo + (size_t)(m0 + r) * a.ldx + cc;
+    const bf16_t *base;
+    int n;
+    if (SW) {
+      n = min(n0 + (r & 63), a.N - 1);
+      base = reinterpret_cast<const bf16_t *>(r < 64 ? a.w[0] : a.w[1]) + (size_t)n * a.K;
+    } else {
+      n = min(n0 + r, a.N - 1);
+      const int seg = n >= a.rs[2] ? 2 : (n >= a.rs[1] ? 1 : 0);
+      base = reinterpret_cast<const bf16_t *>(a.w[seg]) + (size_t)(n - a.rs[seg]) * a.K;
+    }
+    gb[i] = base + cc;
+  }
+
+  u32x4 rh[2], rl[2], rb[2];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rh[i] = load16(ga_hi[i] + k0);
+      rl[i] = load16(ga_lo[i] + k0);
+      rb[i] = load16(gb[i] + k0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4 *>(&s_a[buf][0][lds_off[i]]) = rh[i];
+      *reinterpret_cast<u32x4 *>(&s_a[buf][1][lds_off[i]]) = rl[i];
+      *reinterpret_cast<u32x4 *>(&s_b[buf][lds_off[i]]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nst = a.K / kTK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int l32 = lane & 31, hsel = (lane >> 5) * 8;
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nst) fetch((s + 1) * kTK);
+#pragma unroll
+    for (int kk = 0; kk < kTK / 16; ++kk) {
+      const int ko = kk * 16 + hsel;
+      u32x4 ah[2], al[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + l32;
+        ah[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][0][row * kRowA + ko]);
+        al[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][1][row * kRowA + ko]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int brow = SW ? (wn * 32 + j * 64 + l32) : (wn * 64 + j * 32 + l32);
+        b[j] = *reinterpret_cast<const u32x4 *>(&s_b[buf][brow * kRowA + ko]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
+          acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+        }
+    }
+    if (s + 1 < nst) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (t >= a.M) continue;
+      if (SW) {
+        const int n = n0 + wn * 32 + l32;
+        if (n < a.N) {
+          const float gt = acc[i][0][r], up = acc[i][1][r];
+          a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 64 + j * 32 + l32;
+          if (n >= a.N) continue;
+          float *y = a.y + (size_t)t * a.ldy + n;
+          if (EPI == EPI_RESID)
+            *y = a.res[(size_t)t * a.ldres + n] + acc[i][j][r];
+          else
+            *y = acc[i][j][r];
+        }
+      }
+    }
+}
+
+int gemm_tiled_rows(int M) { return (M + kTM - 1) / kTM * kTM; }
+
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last) {
+  if (a.K % kTK != 0 || a.M <= 0) return hipErrorInvalidValue;
+  const int mt = (a.M + kTM - 1) / kTM;
+  switch (epi) {
+    case EPI_STORE:
+      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt), dim3(kThreads), s, false, last, a);
+      break;
+    case EPI_RESID:
+      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt), dim3(kThreads), s, false, last, a);
+      break;
+    case EPI_SWIGLU:
+      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt), dim3(kThreads), s, false, last, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RoPE + cache append ----
+// Block i = prompt position pos0 + i: the query heads are rotated in place in the qkv rows; the key
+// heads are rotated and, with the value heads, stored at that position of the cache (bf16 with
+// round-to-nearest-even).  Each pair (d, d + half) uses rot_lo / rot_hi (main.bend rope) with the
+// position's cos/sin from the table.
+__global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
+  const int i = blockIdx.x, p = a.pos0 + i;
+  const int half = a.half, D = 2 * half;
+  float *row = a.qkv + (size_t)i * a.qkv_stride;
+  const float *cs = a.rope_cs + (size_t)p * half, *sn = a.rope_sn + (size_t)p * half;
+  const int nq = a.heads * half, nk = a.kv * half;
+  for (int k = threadIdx.x; k < nq + nk; k += kThreads) {
+    const bool isq = k < nq;
+    const int kk = isq ? k : k - nq;
+    const int h = kk / half, d = kk - h * half;
+    float *src = isq ? row + h * D : row + a.heads * D + h * D;
+    const float lo = src[d], hi = src[d + half], c = cs[d], s = sn[d];
+    const float nlo = rope_pair(lo, -hi, c, s), nhi = rope_pair(hi, lo, c, s);
+    if (isq) {
+      src[d] = nlo;
+      src[d + half] = nhi;
+    } else {
+      bf16_t *kd = a.kc + ((size_t)(a.row * a.kv + h) * a.max_seq + p) * D;
+      kd[d] = f32_to_bf16(nlo);
+      kd[d + half] = f32_to_bf16(nhi);
+    }
+  }
+  const float *v = row + a.heads * D + a.kv * D;
+  for (int k = threadIdx.x; k < a.kv * D; k += kThreads) {
+    const int h = k / D, d = k - h * D;
+    a.vc[((size_t)(a.row * a.kv + h) * a.max_seq + p) * D + d] = f32_to_bf16(v[k]);
+  }
+}
+
+// ------------------------------------------------------------------ causal attention ----
+// Block (query tile qt of 32 positions, kv head j, head quarter z): wave w takes query head
+// j*g + 4z + w (idle when that is >= g; it still helps stage the tiles).  Per key tile of 64 positions:
+//   S^T[key][q] = K Q^T (K from LDS as the A operand, the wave's rotated queries as bf16 hi + lo B
+//   fragments held in registers), so each lane owns one query column: 32 of the tile's 64 scores, the
+//   other 32 in lane ^ 32.  Softmax with a running maximum in base 2 (scores times scale * log2(e)).
+//   O^T[d][q] += V^T P^T: P^T is the score accumulator itself, split into bf16 hi + lo; the 16 keys a
+//   B fragment covers are taken in the order the accumulator holds them (a sum does not care), and
+//   V^T fragments are read from an LDS copy of V stored transposed, in the same key order.
+constexpr int kQT = 32;   // query positions per block
+constexpr int kKT = 64;   // key positions per tile
+
+template <int D>
+struct FlashShape {
+  static constexpr int KROW = D + 8;        // LDS row of K (bf16): 16-byte reads of 16 rows hit distinct banks
+  static constexpr int VROW = kKT + 4;      // LDS row of V^T (bf16): one d, 64 keys
+  static constexpr int KS = D / 16;         // k16 steps of a score product
+  static constexpr int DT = D / 32;         // 32-row tiles of O^T
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
+  using F = FlashShape<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t s_k[kKT * F::KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t s_vt[D * F::VROW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nqt = gridDim.x;
+  const int qt = nqt - 1 - (int)blockIdx.x;  // the longest tiles first
+  const int j = blockIdx.y;
+  const int hi_in_group = blockIdx.z * 4 + wave;
+  const bool active = hi_in_group < a.g;
+  const int head = j * a.g + (active ? hi_in_group : 0);
+  const int l32 = lane & 31, hsel = lane >> 5;
+  const int q_i = qt * kQT + l32;                 // prompt index of this lane's query
+  const int q_pos = a.pos0 + min(q_i, a.S - 1);   // its cache position (tail lanes repeat the last)
+  const int last_pos = a.pos0 + min(qt * kQT + kQT - 1, a.S - 1);
+  const bf16_t *Kh = a.kc + (size_t)(a.row * a.kv + j) * a.max_seq * D;
+  const bf16_t *Vh = a.vc + (size_t)(a.row * a.kv + j) * a.max_seq * D;
+
+  // the wave's rotated queries as B fragments: lane holds q[q_i][16 ks + 8 hsel .. +8], hi and lo
+  u32x4 qh[F::KS], ql[F::KS];
+  {
+    const float *q = a.qkv + (size_t)min(q_i, a.S - 1) * a.qkv_stride + head * D;
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks) {
+      const float4 v0 = *reinterpret_cast<const float4 *>(q + ks * 16 + hsel * 8);
+      const float4 v1 = *reinterpret_cast<const float4 *>(q + ks * 16 + hsel * 8 + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t h4[4], l4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
+        const uint16_t r0 = f32_to_bf16(f[2 * e] - bf16_to_f32(h0)), r1 = f32_to_bf16(f[2 * e + 1] - bf16_to_f32(h1));
+        h4[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        l4[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+      }
+      qh[ks] = u32x4{h4[0], h4[1], h4[2], h4[3]};
+      ql[ks] = u32x4{l4[0], l4[1], l4[2], l4[3]};
+    }
+  }
+
+  f32x16 o[F::DT];
+#pragma unroll
+  for (int t = 0; t < F::DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale * 1.4426950408889634f;
+
+  const int ntiles = last_pos / kKT + 1;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int k0 = tile * kKT;
+    // stage K (row-major) and V (transposed) of positions k0 .. k0+63 (past last_pos: clamped, masked)
+    constexpr int KCH = kKT * D / 8;  // 16-byte chunks of the K tile
+    for (int c = tid; c < KCH; c += kThreads) {
+      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
+      const int p = min(k0 + r, last_pos);
+      *reinterpret_cast<u32x4 *>(&s_k[r * F::KROW + cc]) = load16(Kh + (size_t)p * D + cc);
+    }
+    // V: thread takes 4 consecutive keys x 8 consecutive d and writes 8 rows of 4 keys of V^T
+    constexpr int VCH = (kKT / 4) * (D / 8);
+    for (int c = tid; c < VCH; c += kThreads) {
+      const int dc = c % (D / 8), kq = c / (D / 8);
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load16(Vh + (size_t)min(k0 + 4 * kq + u, last_pos) * D + dc * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1, sh = (e & 1) * 16;
+        const uint32_t b0 = (v[0][w] >> sh) & 0xffffu, b1 = (v[1][w] >> sh) & 0xffffu;
+        const uint32_t b2 = (v[2][w] >> sh) & 0xffffu, b3 = (v[3][w] >> sh) & 0xffffu;
+        *reinterpret_cast<u32x2 *>(&s_vt[(dc * 8 + e) * F::VROW + 4 * kq]) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      }
+    }
+    __syncthreads();
+
+    if (active) {
+      // scores S^T for keys k0 + 32 mt + (8(r/4) + 4 hsel + r%4), query q_i
+      f32x16 s[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ++ks) {
+          const u32x4 kf = *reinterpret_cast<const u32x4 *>(&s_k[(mt * 32 + l32) * F::KROW + ks * 16 + hsel * 8]);
+          s[mt] = mfma32(kf, qh[ks], s[mt]);
+          s[mt] = mfma32(kf, ql[ks], s[mt]);
+        }
+      }
+      float mt_max = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+          const float v = key <= q_pos ? s[mt][r] * sc : -INFINITY;
+          s[mt][r] = v;
+          mt_max = fmaxf(mt_max, v);
+        }
+      mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32));
+      const float m_new = fmaxf(m_run, mt_max);  // finite: key 0 is visible to every query
+      const float alpha = exp2f(m_run - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = exp2f(s[mt][r] - m_new);
+          s[mt][r] = pr;
+          lsum += pr;
+        }
+      lsum += __shfl_xor(lsum, 32);
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < F::DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      // O^T += V^T P^T over the tile's 4 groups of 16 keys
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int mt = kk >> 1, r0 = (kk & 1) * 8;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f0 = s[mt][r0 + 2 * e], f1 = s[mt][r0 + 2 * e + 1];
+          const uint16_t h0 = f32_to_bf16(f0), h1 = f32_to_bf16(f1);
+          const uint16_t q0 = f32_to_bf16(f0 - bf16_to_f32(h0)), q1 = f32_to_bf16(f1 - bf16_to_f32(h1));
+          ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          pl[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+        }
+        const u32x4 pfh = u32x4{ph[0], ph[1], ph[2], ph[3]}, pfl = u32x4{pl[0], pl[1], pl[2], pl[3]};
+        // keys of slot e of half hsel within the 16-group: 8(e/4) + 4 hsel + e%4
+        const int kb = kk * 16 + 4 * hsel;
+#pragma unroll
+        for (int t = 0; t < F::DT; ++t) {
+          const bf16_t *vr = &s_vt[(t * 32 + l32) * F::VROW + kb];
+          const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(vr);
+          const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(vr + 8);
+          const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+          o[t] = mfma32(vf, pfh, o[t]);
+          o[t] = mfma32(vf, pfl, o[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (active && q_i < a.S) {
+    const float inv = 1.0f / l_run;
+    float *out = a.out + (size_t)q_i * a.out_stride + head * D;
+#pragma unroll
+    for (int t = 0; t < F::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[t * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3)] = o[t][r] * inv;
+  }
+}
+
+hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last) {
+  launch(k_rope_rows, dim3(a.S), dim3(kThreads), s, first, last, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last) {
+  const dim3 g((a.S + kQT - 1) / kQT, a.kv, (a.g + 3) / 4);
+  if (a.half == 64)
+    launch(k_attn_prefill<128>, g, dim3(kThreads), s, first, last, a);
+  else if (a.half == 32)
+    launch(k_attn_prefill<64>, g, dim3(kThreads), s, first, last, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lm
