@@ -199,6 +199,72 @@ def time_batched(cfg, lm, synth, dev_weights, steps, warmup):
     return out
 
 
+def prefill_flops(cfg, S, pos0=0):
+    """Algorithmic FLOPs of a prefill of S positions: 2 per multiply-add of every layer product for every
+    position, causal attention (scores and weighted sum, 4 * head per visible key per query head), and
+    the LM head of the last position."""
+    d, kw, f = cfg.dim, cfg.kvw, cfg.f
+    mats = 2 * d * d + 2 * kw * d + 3 * f * d
+    keys = sum(pos0 + i + 1 for i in range(S))
+    att = 4 * cfg.head * cfg.heads * keys
+    return cfg.layers * (2 * S * mats + att) + 2 * cfg.vocab * d
+
+
+MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core peak, FLOP/s
+
+
+def time_prefill(cfg, lm, synth, dev_weights, reps, warmup):
+    """Prefill of a `cfg.prompt_len`-position random prompt into a fresh cache row (MaxSeq cfg.max_seq)."""
+    import torch
+    S = cfg.prompt_len
+    dec = lm.Decoder(cfg, None, rows=1, max_seq=cfg.max_seq, max_prefill=S, weights=dev_weights)
+    toks = torch.from_numpy(synth.tokens(cfg, "bench/prompt", S)).cuda()
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        dec.prefill(toks, pos0=0, next_tok=nxt)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dec.prefill(toks, pos0=0, next_tok=nxt)
+    e1.record()
+    torch.cuda.synchronize()
+    if dec.status() != 0:
+        raise RuntimeError("device status flag set during the prefill")
+    ms = e0.elapsed_time(e1) / reps
+    lm.profile_enable(True)
+    dec.prefill(toks, pos0=0, next_tok=nxt)
+    torch.cuda.synchronize()
+    kernels = {}
+    for name, cls in lm.KERNEL_CLASSES.items():
+        n, kms = lm.profile_read(cls)
+        if n:
+            kernels[name] = {"launches": n, "ms": round(kms, 3), "share": round(kms / ms, 4)}
+    lm.profile_enable(False)
+    fl = prefill_flops(cfg, S)
+    # the products: the largest share of the time; matrix-core work per launch counted algorithmically
+    d, kw, f = cfg.dim, cfg.kvw, cfg.f
+    gu = kernels.get("gate_up")
+    gu_flops = 2 * S * 2 * f * d
+    out = {"workload": f"{cfg.name}: prefill of a {S}-position random prompt at positions 0..{S - 1} of a fresh "
+                       f"cache row (MaxSeq {cfg.max_seq}), bf16 weights and KV, F32 activations",
+           "value": round(S * 1e3 / ms, 1), "unit": "tokens/s", "ms_per_prefill": round(ms, 3), "reps": reps,
+           "warmup": warmup, "dtype": "bf16", "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "mfma_fraction": round(fl / (ms * 1e-3) / MFMA_BF16_PEAK, 4), "kernels": kernels}
+    if gu:
+        per = gu["ms"] / gu["launches"] * 1e-3
+        out["roofline"] = {"bound": "mfma", "kernel": "split + k_gemm_tiled<SwiGLU> (gate+up)",
+                           "achieved": round(gu_flops / per / 1e12, 1), "peak": MFMA_BF16_PEAK / 1e12,
+                           "unit": "TFLOP/s", "frac": round(gu_flops / per / MFMA_BF16_PEAK, 4),
+                           "flops_per_launch": gu_flops, "avg_launch_us": round(per * 1e6, 1),
+                           "note": "algorithmic FLOPs; the products run twice (bf16 hi and lo of the F32 "
+                                   "activations), so executed matrix-core work is 2x"}
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
     import numpy as np
     import oracle
@@ -225,6 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the 4096-position prefill (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
@@ -245,6 +313,11 @@ def main():
     p0 = cfg.kv_fill
     steps = max(1, min(args.steps, cfg.max_seq - p0))
     want_cpu = not args.no_cpu_baseline
+    if args.prefill_only:
+        dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
+        c5 = configs.LLAMA31_8B_LONG
+        print(json.dumps({"prefill": time_prefill(c5, lm, synth, dec.w, 2, 1)}), flush=True)
+        return
     dec, w, kc, vc = build_model(cfg, lm, synth, cfg.max_seq, p0, keep_host=want_cpu)
     first = int(synth.tokens(cfg, "bench/first", 1)[0])
 
@@ -292,6 +365,9 @@ def main():
         c5 = configs.LLAMA31_8B_LONG
         result["batched"] = time_batched(c5, lm, synth, dec.w, c5.decode_steps, args.warmup)
         log(f"batch {c5.batch}: {result['batched']['value']:.1f} tok/s, hbm {result['batched']['hbm_fraction']:.3f}")
+        result["prefill"] = time_prefill(c5, lm, synth, dec.w, 3, 1)
+        log(f"prefill {c5.prompt_len}: {result['prefill']['ms_per_prefill']:.1f} ms, "
+            f"{result['prefill']['tflops']:.0f} TFLOP/s")
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:

@@ -21,10 +21,24 @@ namespace {
 
 constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 
+// Caps on GEMV blocks per projection (blocks walk row groups with a grid stride).  Fewer blocks read
+// the input vector fewer times (each block loads all of it); more blocks keep more loads in flight.
+// Defaults measured on MI355X at the 8B shape; LLAMA_GEMV_GRID sets all, LLAMA_GEMV_GRID_<NAME> one.
 struct Tun {
-  int gemv_grid = 1024;      // cap on GEMV blocks (they walk row groups with a grid stride)
+  int qkv = 1024, o = 512, gate_up = 2048, down = 768, lm = 512;
+  static void env(const char *name, int &v) {
+    if (const char *e = getenv(name))
+      if (atoi(e) > 0) v = atoi(e);
+  }
   Tun() {
-    if (const char *e = getenv("LLAMA_GEMV_GRID")) gemv_grid = atoi(e) > 0 ? atoi(e) : gemv_grid;
+    int all = 0;
+    env("LLAMA_GEMV_GRID", all);
+    if (all > 0) qkv = o = gate_up = down = lm = all;
+    env("LLAMA_GEMV_GRID_QKV", qkv);
+    env("LLAMA_GEMV_GRID_O", o);
+    env("LLAMA_GEMV_GRID_GATE_UP", gate_up);
+    env("LLAMA_GEMV_GRID_DOWN", down);
+    env("LLAMA_GEMV_GRID_LM", lm);
   }
 };
 const Tun &tun() {
@@ -101,7 +115,7 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, rope_cs, rope_sn, x, qkv, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, total;
+  size_t status, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, total;
   int nch;
   int lm_ld;  // per-row stride of the LM head's block winners
   int mpad;   // token rows of the split operands (max_batch rounded up to 16)
@@ -120,7 +134,7 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   const int32_t prows = prefill_tiled_ok(c) ? max_prefill : 0;
   const size_t rows = (size_t)(max_batch > prows ? max_batch : prows);
   WsLayout L;
-  const int chunk = attention_chunk(c->kv_dtype, (int)d.head);
+  const int chunk = attention_chunk(c->kv_dtype, (int)d.head, (int)d.g);
   L.nch = (int)((max_seq + chunk - 1) / chunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -133,6 +147,7 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * rows * d.dim);
   L.qkv = take(sizeof(float) * rows * (d.dim + 2 * d.kvw));
+  L.qrot = take(sizeof(float) * (size_t)max_batch * d.dim);
   L.attn = take(sizeof(float) * rows * d.dim);
   L.m = take(sizeof(float) * rows * d.f);
   L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
@@ -294,12 +309,13 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
   a.part_i = x.at<int>(x.L.lm_i) + (size_t)b * kLmGridMax;
   a.next = next;
   ProfScope ps(LLAMA_K_LM_HEAD, x.s);
-  return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().gemv_grid, x.s));
+  return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().lm, x.s));
 }
 
 // Several token rows with bf16 weights: each projection is one matrix-core product over all rows (the
 // weights stream once per step instead of once per row); operands are split into bf16 hi/lo first.
-int run_step_rows(const Ctx &x, AttnArgs aa, int nch_launch, int B, float *logits, int32_t *next, bool want_head) {
+int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int nch_launch, int B, float *logits, int32_t *next,
+                  bool want_head) {
   const Dims &d = x.d;
   const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f, V = (int)d.vocab;
   const int mpad = (B + 15) / 16 * 16;
@@ -346,18 +362,19 @@ int run_step_rows(const Ctx &x, AttnArgs aa, int nch_launch, int B, float *logit
     ga.part_v = x.at<float>(x.L.lm_v);
     ga.part_i = x.at<int>(x.L.lm_i);
     ga.part_ld = x.L.lm_ld;
+    if (epi == EPI_ROPE) ga.ra = ra;
     return hip_rc(launch_gemm_skinny(epi, ga, x.s, last));
   };
   int rc;
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
+    aa.kc = ra.kc = layer_cache(x, x.kv->k, l);
+    aa.vc = ra.vc = layer_cache(x, x.kv->v, l);
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
       if ((rc = split(xs, H, lw.ln1, H))) return rc;
-      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, true))) return rc;
+      if ((rc = gemm(EPI_ROPE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, true))) return rc;
     }
-    aa.kc = layer_cache(x, x.kv->k, l);
-    aa.vc = layer_cache(x, x.kv->v, l);
     {
       ProfScope ps(LLAMA_K_ATTN, x.s);
       if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
@@ -516,17 +533,14 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   // attention: one block per (chunk of positions, kv head, row)
   int tmax = 0;
   for (int b = 0; b < B; ++b) tmax = pos[b] > tmax ? pos[b] : tmax;
-  const int nch_launch = tmax / attention_chunk(x.c->kv_dtype, (int)d.head) + 1;
+  const int nch_launch = tmax / attention_chunk(x.c->kv_dtype, (int)d.head, (int)d.g) + 1;
 
   AttnArgs aa = {};
-  aa.qkv = qkv;
-  aa.qkv_stride = qkv_stride;
+  aa.q = x.at<float>(x.L.qrot);
   aa.kv = (int)d.kv;
   aa.max_seq = x.kv->max_seq;
   aa.half = (int)d.half;
   aa.row0 = row0;
-  aa.rope_cs = x.at<float>(x.L.rope_cs);
-  aa.rope_sn = x.at<float>(x.L.rope_sn);
   aa.out = att;
   aa.out_stride = H;
   aa.part_o = x.at<float>(x.L.part_o);
@@ -535,14 +549,34 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   aa.scale = 1.0f / sqrtf((float)d.head);
   for (int b = 0; b < B; ++b) aa.pos[b] = pos[b];
 
+  // the q|k|v epilogue: RoPE and the cache append at each row's position
+  RopeAppend ra = {};
+  ra.qrot = x.at<float>(x.L.qrot);
+  ra.kv_bf16 = x.c->kv_dtype == LLAMA_BF16;
+  ra.max_seq = x.kv->max_seq;
+  ra.half = (int)d.half;
+  ra.hshift = d.half == 64 ? 6 : 5;
+  ra.dim = H;
+  ra.kvw = KW;
+  ra.row0 = row0;
+  ra.rope_cs = x.at<float>(x.L.rope_cs);
+  ra.rope_sn = x.at<float>(x.L.rope_sn);
+  for (int b = 0; b < B; ++b) ra.pos[b] = pos[b];
+
   if (B > 1 && gemm_skinny_supported(wdt, H, B) && gemm_skinny_supported(wdt, F, B) && !trace)
-    return run_step_rows(x, aa, nch_launch, B, logits, next, want_head);
+    return run_step_rows(x, aa, ra, nch_launch, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
+    aa.kc = ra.kc = layer_cache(x, x.kv->k, l);
+    aa.vc = ra.vc = layer_cache(x, x.kv->v, l);
     for (int b = 0; b < B; ++b) {
       GemvArgs a = {};
+      a.ra = ra;
+      a.ra.qrot = ra.qrot + (size_t)b * H;
+      a.ra.row0 = row0 + b;
+      a.ra.pos[0] = pos[b];
       a.x = xs + (size_t)b * H;
       a.gain = lw.ln1;
       a.eps = x.c->eps;
@@ -557,10 +591,8 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.K = H;
       a.y = qkv + (size_t)b * qkv_stride;
       ProfScope ps(LLAMA_K_QKV, x.s);
-      if ((rc = hip_rc(launch_gemv(wdt, EPI_STORE, true, a, tun().gemv_grid, x.s)))) return rc;
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_ROPE, true, a, tun().qkv, x.s)))) return rc;
     }
-    aa.kc = layer_cache(x, x.kv->k, l);
-    aa.vc = layer_cache(x, x.kv->v, l);
     {
       ProfScope ps(LLAMA_K_ATTN, x.s);
       if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
@@ -582,7 +614,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.y = xs + (size_t)b * H;
       a.res = xs + (size_t)b * H;
       ProfScope ps(LLAMA_K_O, x.s);
-      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().gemv_grid, x.s)))) return rc;
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().o, x.s)))) return rc;
     }
     if (tr && (rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + H, xs, sizeof(float) * H, hipMemcpyDeviceToDevice, x.s))))
       return rc;
@@ -599,7 +631,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.K = H;
       a.y = mm + (size_t)b * F;
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
-      if ((rc = hip_rc(launch_gemv(wdt, EPI_SWIGLU, true, a, tun().gemv_grid, x.s)))) return rc;
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_SWIGLU, true, a, tun().gate_up, x.s)))) return rc;
     }
     for (int b = 0; b < B; ++b) {
       GemvArgs a = {};
@@ -612,7 +644,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.y = xs + (size_t)b * H;
       a.res = xs + (size_t)b * H;
       ProfScope ps(LLAMA_K_DOWN, x.s);
-      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().gemv_grid, x.s)))) return rc;
+      if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().down, x.s)))) return rc;
     }
     if (tr) {
       if ((rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + 2 * H, mm, sizeof(float) * F, hipMemcpyDeviceToDevice, x.s))))
@@ -703,7 +735,7 @@ int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max
   int rc = check_cfg(c);
   if (rc) return rc;
   if (max_batch <= 0 || max_batch > kMaxBatch || max_seq <= 0 || max_prefill < 0) return LLAMA_E_SHAPE;
-  if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * attention_chunk(c->kv_dtype, 2 * c->half))
+  if ((int64_t)max_seq > (int64_t)kAttnMaxChunks * attention_chunk(c->kv_dtype, 2 * c->half, c->g))
     return LLAMA_E_UNSUPPORTED;
   if (max_prefill > 65535) return LLAMA_E_UNSUPPORTED;  // one grid row per prompt position
   return (int64_t)ws_layout(c, max_batch, max_seq, max_prefill).total;

@@ -1,46 +1,29 @@
-// Causal grouped-query decode attention on gfx950, with RoPE and the KV-cache append fused in.
+// Causal grouped-query decode attention on gfx950.
 //
 // What it computes (main.bend "Grouped-query attention over the arrays", head_att / group_att /
 // attention; nest attention.linnet `decode` / `decode_rows`): for cache row b at position t, query
 // head h = j*g + i reads key/value head j (gqa_head); scores s_p = (q_h . K_j[p]) * (1/sqrt(head)) for
-// p = 0..t exactly (causal / read_len), softmax over them, o_h = sum_p w_p V_j[p].  Before that, the
-// position's rotated key and its value are written at slot t of head j (KV.push): RoPE pairs number i
-// with number i + half of a head, lo' = lo*c - hi*s, hi' = hi*c + lo*s (rot_lo / rot_hi), each product
-// and sum rounded on its own; bf16 caches round to nearest even.  The position-t key and value that
-// the scores use are the stored (rounded) ones, as a cache read would give.
+// p = 0..t exactly (causal / read_len), softmax over them, o_h = sum_p w_p V_j[p].  The rotated queries
+// and the position-t key and value were produced by the q/k/v projection's epilogue (RoPE and the
+// cache append, KV.push), so every position 0..t is read from the cache as stored.
 //
 // Work split (split-K over positions): block (c, j, b) takes chunk c of `chunk` positions of row b's
 // head j and all g query heads of the group, so each K/V byte is read from HBM once for g heads.
-// 256 threads = 256/LPR position groups of LPR lanes, LPR lanes covering one 16-byte slice each of a
-// head row (head*bytes/16 lanes), so every load instruction of a wave reads whole contiguous rows.
-// Every K and V load of a thread (8 rows each) is issued before any is used.  The query heads, the
-// cos/sin row and the appended key/value are staged once per block in LDS.  Each wavefront keeps its
-// scores in registers and forms its own softmax pieces (max, exp-sum, exp-weighted V sum) with
-// cross-lane permutes; the 4 wavefronts are combined through LDS.  Each chunk writes an unnormalised
-// partial (o, m, l); a second small kernel merges the chunks of each (row, kv head) in chunk order,
-// so results do not depend on block timing.  When one chunk covers every row's positions the
-// attention kernel normalises directly and no merge runs.
+// Two kernels: k_attn_mfma (bf16 caches) forms the scores on the matrix cores and the weighted V sum
+// on the vector units; k_attn (any cache type) does both on the vector units.  Each chunk writes an
+// unnormalised partial (o, m, l); a second small kernel merges the chunks of each (row, kv head) in
+// chunk order, so results do not depend on block timing.  When one chunk covers every row's positions
+// the attention kernel normalises directly and no merge runs.
+//
+// k_attn: 256 threads = 256/LPR position groups of LPR lanes, LPR lanes covering one 16-byte slice each
+// of a head row (head*bytes/16 lanes), so every load instruction of a wave reads whole contiguous rows.
+// Every K and V load of a thread (8 rows each) is issued before any is used.  The query heads are
+// staged once per block in LDS.  Each wavefront keeps its scores in registers and forms its own
+// softmax pieces (max, exp-sum, exp-weighted V sum) with cross-lane permutes; the 4 wavefronts are
+// combined through LDS.
 #include "common.h"
 
 namespace lm {
-
-template <typename KT>
-struct KvStore;
-template <>
-struct KvStore<float> {
-  __device__ __forceinline__ static float round_store(float *p, float v) {
-    *p = v;
-    return v;
-  }
-};
-template <>
-struct KvStore<bf16_t> {
-  __device__ __forceinline__ static float round_store(bf16_t *p, float v) {
-    const uint16_t b = f32_to_bf16(v);
-    *p = b;
-    return bf16_to_f32(b);
-  }
-};
 
 template <typename KT, int D>
 struct AttnShape {
@@ -56,7 +39,6 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   using S = AttnShape<KT, D>;
   constexpr int E = S::E, LPR = S::LPR, PPR = S::PPR, NR = S::NR, CHUNK = S::CHUNK;
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row must fit a wavefront");
-  constexpr int HALF = D / 2;
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
   const int nact = t / CHUNK + 1;  // chunks covering 0..t
@@ -65,103 +47,42 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   const int li = tid % LPR, grp = tid / LPR;
   const int p0 = c * CHUNK;
   const int p1 = min(p0 + CHUNK, t + 1);
-  const bool owner = (c == nact - 1);
 
-  __shared__ float q_s[G][D];                // raw query heads of the group
-  __shared__ float cs_s[HALF], sn_s[HALF];   // cos / sin of position t
-  __shared__ float kr_s[D], vr_s[D];         // raw key / value of kv head j at t (owner block)
-  __shared__ float kt_s[D], vt_s[D];         // the appended key (rotated) and value, as stored
+  __shared__ float q_s[G][D];                // rotated query heads of the group
   __shared__ float m_s[4][G];
   __shared__ float l_g[kThreads / LPR][G];
   __shared__ float o_g[kThreads / LPR][G][D];
 
   const size_t head_off = ((size_t)(a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
-  KT *Kh = reinterpret_cast<KT *>(a.kc) + head_off;
-  KT *Vh = reinterpret_cast<KT *>(a.vc) + head_off;
-  const float *qkv = a.qkv + (size_t)b * a.qkv_stride;
-  const int dim = a.kv * G * D;
+  const KT *Kh = reinterpret_cast<const KT *>(a.kc) + head_off;
+  const KT *Vh = reinterpret_cast<const KT *>(a.vc) + head_off;
+  const float *qg = a.q + (size_t)b * (a.kv * G * D) + (size_t)j * G * D;
 
-  // (1) small inputs, once per block, as 16-byte units: units [0, NQ) the query heads, [NQ, NQ+NC) the
-  // cos/sin slices, then (owner block) the raw key and value of head j.  A thread takes units tid and
-  // tid + 256.
-  constexpr int NQ = G * D / 4, NC = HALF / 4, NK = D / 4, NU = NQ + NC + NK;
-  static_assert(NU <= 2 * kThreads, "two staging units per thread");
-  float4 sm[2][2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = tid + k * kThreads;
-    sm[k][0] = sm[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (u < NQ) {
-      sm[k][0] = *reinterpret_cast<const float4 *>(qkv + (size_t)j * G * D + u * 4);
-    } else if (u < NQ + NC) {
-      sm[k][0] = *reinterpret_cast<const float4 *>(a.rope_cs + (size_t)t * HALF + (u - NQ) * 4);
-      sm[k][1] = *reinterpret_cast<const float4 *>(a.rope_sn + (size_t)t * HALF + (u - NQ) * 4);
-    } else if (owner && u < NU) {
-      const int w = u - NQ - NC;
-      sm[k][0] = *reinterpret_cast<const float4 *>(qkv + dim + (size_t)j * D + w * 4);
-      sm[k][1] = *reinterpret_cast<const float4 *>(qkv + dim + (size_t)a.kv * D + (size_t)j * D + w * 4);
-    }
-  }
+  // (1) the group's query heads, one 16-byte unit per thread, staged in LDS
+  constexpr int NQ = G * D / 4;
+  static_assert(NQ <= kThreads, "one staging unit per thread");
+  float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < NQ) qv = *reinterpret_cast<const float4 *>(qg + tid * 4);
 
   // (2) every K and V row of this thread's positions, in flight together.  Loads are unconditional: a
-  // position at or after t reads row min(p, t - 1) (row 0 when t = 0), which is inside the cache, and
-  // its value is never used (position t comes from this step's append).
+  // position after t reads row t (inside the cache), and its value is never used.
   u32x4 kraw[NR], vraw[NR];
-  const int plast = t > 0 ? t - 1 : 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int p = min(p0 + r * PPR + grp, plast);
+    const int p = min(p0 + r * PPR + grp, t);
     kraw[r] = load_stream16(Kh + (size_t)p * D + li * E);
     vraw[r] = load_stream16(Vh + (size_t)p * D + li * E);
   }
-
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = tid + k * kThreads;
-    if (u < NQ) {
-      *reinterpret_cast<float4 *>(&q_s[0][0] + u * 4) = sm[k][0];
-    } else if (u < NQ + NC) {
-      *reinterpret_cast<float4 *>(cs_s + (u - NQ) * 4) = sm[k][0];
-      *reinterpret_cast<float4 *>(sn_s + (u - NQ) * 4) = sm[k][1];
-    } else if (owner && u < NU) {
-      const int w = u - NQ - NC;
-      *reinterpret_cast<float4 *>(kr_s + w * 4) = sm[k][0];
-      *reinterpret_cast<float4 *>(vr_s + w * 4) = sm[k][1];
-    }
-  }
+  if (tid < NQ) *reinterpret_cast<float4 *>(&q_s[0][0] + tid * 4) = qv;
   lds_barrier();
 
-  // (3) the owner appends position t: the rotated key (rot_lo / rot_hi) and the value, rounded as
-  // stored; the scores use the stored values
-  if (owner && tid < D) {
-    const int d = tid, ic = d < HALF ? d : d - HALF;
-    const float partner = d < HALF ? -kr_s[d + HALF] : kr_s[d - HALF];
-    const float kr = rope_pair(kr_s[d], partner, cs_s[ic], sn_s[ic]);
-    kt_s[d] = KvStore<KT>::round_store(Kh + (size_t)t * D + d, kr);
-    vt_s[d] = KvStore<KT>::round_store(Vh + (size_t)t * D + d, vr_s[d]);
-  }
-  // rotated query slices [li*E, li*E + E) of the g heads
+  // (3) this thread's query slices [li*E, li*E + E) of the g heads
   const int d0 = li * E;
-  const int dp = d0 < HALF ? d0 + HALF : d0 - HALF;
-  const int ic0 = d0 < HALF ? d0 : d0 - HALF;
-  const float sgn = d0 < HALF ? -1.f : 1.f;
   float q[G][E];
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int e = 0; e < E; ++e) q[i][e] = rope_pair(q_s[i][d0 + e], sgn * q_s[i][dp + e], cs_s[ic0 + e], sn_s[ic0 + e]);
-  if (owner) {
-    lds_barrier();  // kt_s / vt_s
-    // the position-t row comes from this step's append: put its stored bits where a cache load would
-    // have put them, so every round takes the same path
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (p0 + r * PPR + grp == t) {
-        kraw[r] = Vec16<KT>::pack(&kt_s[d0]);
-        vraw[r] = Vec16<KT>::pack(&vt_s[d0]);
-      }
-    }
-  }
+    for (int e = 0; e < E; ++e) q[i][e] = q_s[i][d0 + e];
 
   // (4) scores of this thread's positions in base 2: s2 = (q . k) * (scale * log2 e), so that
   // exp(s - m) = exp2(s2 - m2); every lane of a position group gets the full dot product
@@ -257,6 +178,222 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ matrix-core scores ----
+// k_attn_mfma (bf16 cache): each wavefront takes chunk/4 consecutive positions, in groups of 16.
+//   Scores: S[q][p] = Q K^T with v_mfma_f32_16x16x32_bf16, A = the group's query heads (rows q < g of
+//   16; the F32 queries as bf16 hi + lo, so the products are those of the F32 values to ~2^-17) and
+//   B = K^T, whose lane layout (lane l: position l%16, 8 consecutive numbers at 8(l/16) of a 32-wide
+//   slice) is a plain 16-byte load of a key row.  Lane l then holds S[4(l/16) + r][l%16].
+//   Softmax pieces per head over the wave's positions (max by DPP within 16-lane rows), the weights go
+//   through LDS to the layout of the V loads (lane l: position l/LPR of PPI rows, numbers 8(l%LPR) .. +8),
+//   and the weighted V sum runs on the vector units.  The wave's lane groups and the 4 waves are combined
+//   through LDS in a fixed order, as in k_attn.
+typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
+typedef float af32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ af32x4 mfma16(u32x4 a, u32x4 b, af32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8, a), __builtin_bit_cast(abf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// 8 F32 -> bf16 hi (RNE) and lo = bf16(x - hi) (x - hi is exact), packed as MFMA operands
+__device__ __forceinline__ void split8(const float (&f)[8], u32x4 &hi, u32x4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16x2(f[2 * e], f[2 * e + 1], h[e], l[e]);
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+#ifndef LLAMA_ATTN_MFMA_NPW
+#define LLAMA_ATTN_MFMA_NPW 32
+#endif
+template <int D, int G>
+struct MfmaAttnShape {
+  static constexpr int NPW = LLAMA_ATTN_MFMA_NPW;  // positions per wavefront
+  static constexpr int CHUNK = 4 * NPW;   // positions per block
+  static constexpr int NGI = NPW / 16;    // 16-position score groups per wavefront
+  static constexpr int KS = D / 32;       // 32-wide steps of a score
+  static constexpr int LPR = D / 8;       // lanes per V row (16 bytes each)
+  static constexpr int PPI = 64 / LPR;    // V rows per wavefront load
+  static constexpr int NV = NPW / PPI;    // V loads per lane
+  static constexpr int GP = G <= 4 ? 4 : 8;  // weights per position in LDS (padded)
+  static constexpr int NG = kThreads / LPR;  // lane groups per block
+  static constexpr size_t LDS = sizeof(float) * (4 * NPW * GP + 8 * G + (size_t)NG * G * D);
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
+  using S = MfmaAttnShape<D, G>;
+  constexpr int CHUNK = S::CHUNK, NPW = S::NPW, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
+  constexpr int GP = S::GP, NG = S::NG;
+  static_assert(G <= 8, "at most 8 query heads per kv head (two rows of the 16-row tile)");
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int t = a.pos[b];
+  const int nact = t / CHUNK + 1;
+  if (c >= nact) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pw0 = c * CHUNK + wave * NPW;  // this wavefront's first position
+  const int p1 = min(c * CHUNK + CHUNK, t + 1);
+
+  __shared__ __attribute__((aligned(16))) float p_s[4][NPW][GP];
+  __shared__ float m_s[4][G], l_s[4][G];
+  __shared__ __attribute__((aligned(16))) float o_g[NG][G][D];
+
+  const size_t head_off = ((size_t)(a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
+  const bf16_t *Kh = reinterpret_cast<const bf16_t *>(a.kc) + head_off;
+  const bf16_t *Vh = reinterpret_cast<const bf16_t *>(a.vc) + head_off;
+
+  // (1) loads, oldest first: the queries (lane l: head l%16 of the group, numbers 32 ks + 8(l/16) .. +8),
+  // the keys in the B layout, the values in row slices.  Positions after t read row t (never used).
+  const int qrow = lane & 15, qh8 = (lane >> 4) * 8;
+  const float *qp = a.q + (size_t)b * (a.kv * G * D) + ((size_t)j * G + min(qrow, G - 1)) * D;
+  float4 qv[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qv[ks][0] = *reinterpret_cast<const float4 *>(qp + 32 * ks + qh8);
+    qv[ks][1] = *reinterpret_cast<const float4 *>(qp + 32 * ks + qh8 + 4);
+  }
+  u32x4 kf[NGI][KS], vr[NV];
+#pragma unroll
+  for (int gi = 0; gi < NGI; ++gi) {
+    const int p = min(pw0 + 16 * gi + qrow, t);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[gi][ks] = load_stream16(Kh + (size_t)p * D + 32 * ks + qh8);
+  }
+  const int vl = lane % LPR, vg = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int p = min(pw0 + PPI * i + vg, t);
+    vr[i] = load_stream16(Vh + (size_t)p * D + 8 * vl);
+  }
+
+  // (2) query fragments: rows q >= g are zero
+  u32x4 qhi[KS], qlo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float f[8] = {qv[ks][0].x, qv[ks][0].y, qv[ks][0].z, qv[ks][0].w,
+                  qv[ks][1].x, qv[ks][1].y, qv[ks][1].z, qv[ks][1].w};
+    if (qrow >= G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    }
+    split8(f, qhi[ks], qlo[ks]);
+  }
+
+  // (3) scores, base 2: s2 = (q . k) * scale * log2 e; lane holds head 4(lane/16) + r, position
+  // pw0 + 16 gi + lane%16
+  const float scale2 = a.scale * 1.4426950408889634f;
+  float sc[NGI][4];
+#pragma unroll
+  for (int gi = 0; gi < NGI; ++gi) {
+    af32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mfma16(qhi[ks], kf[gi][ks], acc);
+      acc = mfma16(qlo[ks], kf[gi][ks], acc);
+    }
+    const int p = pw0 + 16 * gi + qrow;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[gi][r] = (p < p1) ? acc[r] * scale2 : -INFINITY;
+  }
+  // (4) per head: the wave's max, weights 2^(s2 - max) (reference 0 when the wave has no position of
+  // the chunk: every weight is then 0), their sum
+  const int qbase = 4 * (lane >> 4);  // heads held by this lane: qbase + r
+  float mw[4], lw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float m = sc[0][r];
+#pragma unroll
+    for (int gi = 1; gi < NGI; ++gi) m = fmaxf(m, sc[gi][r]);
+    mw[r] = row16_max(m);
+    const float mref = (mw[r] == -INFINITY) ? 0.f : mw[r];
+    float l = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < NGI; ++gi) {
+      const float w = __builtin_amdgcn_exp2f(sc[gi][r] - mref);
+      sc[gi][r] = w;
+      l += w;
+    }
+    lw[r] = group_sum<16>(l);
+  }
+  if (qbase < G) {
+#pragma unroll
+    for (int gi = 0; gi < NGI; ++gi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (qbase + r < GP) p_s[wave][16 * gi + qrow][qbase + r] = sc[gi][r];
+    if (qrow == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (qbase + r < G) {
+          m_s[wave][qbase + r] = mw[r];
+          l_s[wave][qbase + r] = lw[r];
+        }
+    }
+  }
+  lds_barrier();
+
+  // (5) o[q][e] = sum over this lane's positions of w[q] * V[p][8 vl + e]
+  float o[G][8];
+#pragma unroll
+  for (int q = 0; q < G; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[q][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float w[GP];
+#pragma unroll
+    for (int k = 0; k < GP; k += 4) {
+      const float4 w4 = *reinterpret_cast<const float4 *>(&p_s[wave][PPI * i + vg][k]);
+      w[k] = w4.x;
+      w[k + 1] = w4.y;
+      w[k + 2] = w4.z;
+      w[k + 3] = w4.w;
+    }
+    float vf[8];
+    Vec16<bf16_t>::unpack(vr[i], vf);
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] = fmaf(w[q], vf[e], o[q][e]);
+  }
+  const int grp = tid / LPR;  // lane group of the block: wave * PPI + vg
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    *reinterpret_cast<float4 *>(&o_g[grp][q][8 * vl]) = make_float4(o[q][0], o[q][1], o[q][2], o[q][3]);
+    *reinterpret_cast<float4 *>(&o_g[grp][q][8 * vl + 4]) = make_float4(o[q][4], o[q][5], o[q][6], o[q][7]);
+  }
+  lds_barrier();
+
+  // (6) the waves combined (factor 2^(m_w - M), 0 for a wave without positions), lane groups summed in
+  // a fixed order
+  const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int q = idx / D, d = idx % D;
+    const float M = fmaxf(fmaxf(m_s[0][q], m_s[1][q]), fmaxf(m_s[2][q], m_s[3][q]));
+    float acc = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (m_s[w][q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][q] - M);
+      float ow = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < PPI; ++g2) ow += o_g[w * PPI + g2][q][d];
+      acc = fmaf(f, ow, acc);
+      L = fmaf(f, l_s[w][q], L);
+    }
+    if (a.direct) {
+      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+    } else {
+      a.part_o[(slot + c) * (size_t)(G * D) + idx] = acc;
+      if (d == 0) {
+        a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * q] = M;
+        a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * q + 1] = L;
+      }
+    }
+  }
+}
+
 // Merge of the chunk partials of one (row, kv head), in chunk order (a separate launch: the kernel
 // boundary makes the partials visible without cache-wide fences inside the attention kernel).
 // Block (og, j, b) produces 64 consecutive outputs of query head i = og*64/head of group j:
@@ -335,22 +472,53 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) 
   }
 }
 
-int attention_chunk(int kvdtype, int head) {
-  if (kvdtype == LLAMA_BF16) return head == 64 ? AttnShape<bf16_t, 64>::CHUNK : AttnShape<bf16_t, 128>::CHUNK;
-  return head == 64 ? AttnShape<float, 64>::CHUNK : AttnShape<float, 128>::CHUNK;
+template <typename KT, int D, int G>
+constexpr bool use_mfma() {
+  return sizeof(KT) == 2 && MfmaAttnShape<D, G>::LDS <= 64 * 1024;
+}
+template <typename KT, int D, int G>
+constexpr int chunk_of() {
+  if constexpr (use_mfma<KT, D, G>())
+    return MfmaAttnShape<D, G>::CHUNK;
+  else
+    return AttnShape<KT, D>::CHUNK;
+}
+template <typename KT, int D>
+static int chunk_d(int g) {
+  switch (g) {
+    case 1: return chunk_of<KT, D, 1>();
+    case 2: return chunk_of<KT, D, 2>();
+    case 3: return chunk_of<KT, D, 3>();
+    case 4: return chunk_of<KT, D, 4>();
+    case 8: return chunk_of<KT, D, 8>();
+  }
+  return AttnShape<KT, D>::CHUNK;
+}
+
+int attention_chunk(int kvdtype, int head, int g) {
+  if (kvdtype == LLAMA_BF16) return head == 64 ? chunk_d<bf16_t, 64>(g) : chunk_d<bf16_t, 128>(g);
+  return head == 64 ? chunk_d<float, 64>(g) : chunk_d<float, 128>(g);
 }
 
 int attention_supported(int head, int g) {
   return (head == 64 || head == 128) && (g == 1 || g == 2 || g == 3 || g == 4 || g == 8);
 }
 
+template <typename KT, int D, int G>
+static void launch_attn_kernel(const AttnArgs &a, dim3 grid, bool last, hipStream_t s) {
+  if constexpr (use_mfma<KT, D, G>())
+    launch(k_attn_mfma<D, G>, grid, dim3(kThreads), s, true, last, a);
+  else
+    launch(k_attn<KT, D, G>, grid, dim3(kThreads), s, true, last, a);
+}
+
 template <typename KT, int D>
 static hipError_t launch_d(int g, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
-  const int chunk = AttnShape<KT, D>::CHUNK;
+  const int chunk = chunk_d<KT, D>(g);
   switch (g) {
 #define CASE(G)                                                                                     \
   case G:                                                                                           \
-    launch(k_attn<KT, D, G>, grid, dim3(kThreads), s, true, !merge, a);                             \
+    launch_attn_kernel<KT, D, G>(a, grid, !merge, s);                                               \
     if (merge) launch(k_attn_merge<G, D>, dim3(G * D / 64, grid.y, grid.z), dim3(kThreads), s, false, \
                       true, a, chunk);                                                              \
     break;

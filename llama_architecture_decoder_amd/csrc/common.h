@@ -22,6 +22,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Two F32 -> two bf16 (round to nearest even) in one instruction (v_cvt_pk_bf16_f32), a in the low half
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Matrix-core operands of two F32: hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in F32), so
+// hi + lo carries x to about 2^-17 relative
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // F32 -> bf16 with round-to-nearest-even; NaN stays NaN
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -176,6 +189,14 @@ __device__ __forceinline__ float group_sum(float v) {
   if (N >= 64) v = xor32_sum(v);
   return v;
 }
+// Max over each aligned group of 16 lanes (a DPP row); every lane of the row gets it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
 // Sum over the lanes that share (lane % S), S = 8, 16, 32 or 64: one value per lane position of an
 // S-lane group, summed over the 64/S groups of the wavefront.
 template <int S>
@@ -199,7 +220,64 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // -------------------------------------------------------------- launch descriptors ----
 
-enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_ROPE = 4 };
+
+// EPI_ROPE, the q|k|v projection's epilogue: y gets the projections as computed (before RoPE); the
+// query heads are rotated into qrot and the key heads rotated and, with the value heads, stored at the
+// token's position of its cache row (rounded to the cache type).  The weight rows are visited in an
+// order that puts the two numbers of every RoPE pair (i, i + half of a head) side by side, so one
+// thread holds both.
+struct RopeAppend {
+  float *qrot;                     // [M][dim] rotated queries
+  void *kc, *vc;                   // this layer's cache [rows][kv][max_seq][head]
+  int kv_bf16;                     // cache element type: 1 bf16, 0 F32
+  int max_seq, half, dim, kvw;
+  int hshift;                      // log2(half): half is 32 or 64
+  int row0;                        // cache row of token row 0
+  const float *rope_cs, *rope_sn;  // [max_seq][half]
+  int pos[kMaxBatch];              // position of each token row
+};
+
+// logical row L of the stacked q|k|v rows -> the weight row it reads: inside the q and k heads,
+// logical rows 2i and 2i+1 of a head are rows i and i + half
+__device__ __forceinline__ int rope_row(int L, int qk_rows, int hshift) {
+  if (L >= qk_rows) return L;
+  const int w = L & ((2 << hshift) - 1);
+  return (L - w) + (w >> 1) + ((w & 1) << hshift);
+}
+
+// pair index i (cos/sin column) of logical row L of the q and k heads
+__device__ __forceinline__ int rope_pair_index(int L, int hshift) { return (L & ((2 << hshift) - 1)) >> 1; }
+
+// the epilogue for one logical row L of token row t: val = its projection, pv = its pair partner's,
+// (c, s) = cos/sin of the token's position at the row's pair index (unused for value rows)
+__device__ __forceinline__ void rope_append(const RopeAppend &ra, float *y, int t, int L, float val, float pv, float c,
+                                            float s) {
+  const int dshift = ra.hshift + 1, D = 1 << dshift, qk = ra.dim + ra.kvw;
+  const int p = ra.pos[t];
+  int P = L;
+  float out = val;
+  if (L < qk) {
+    const int w = L & (D - 1), i = w >> 1, upper = w & 1;
+    P = (L - w) + i + (upper << ra.hshift);
+    // rot_lo: lo*c - hi*s (own = lo); rot_hi: hi*c + lo*s (own = hi)
+    out = rope_pair(val, upper ? pv : -pv, c, s);
+  }
+  y[P] = val;
+  if (P < ra.dim) {
+    ra.qrot[(size_t)t * ra.dim + P] = out;
+    return;
+  }
+  const bool is_k = P < qk;
+  const int r = is_k ? P - ra.dim : P - qk;  // row within the k (or v) heads
+  const int j = r >> dshift, d = r & (D - 1);
+  const size_t off = (((size_t)(ra.row0 + t) * (ra.kvw >> dshift) + j) * ra.max_seq + p) * D + d;
+  void *base = is_k ? ra.kc : ra.vc;
+  if (ra.kv_bf16)
+    reinterpret_cast<bf16_t *>(base)[off] = f32_to_bf16(out);
+  else
+    reinterpret_cast<float *>(base)[off] = out;
+}
 
 struct GemvArgs {
   const float *x;      // input [K] (for the norm epilogues: the raw residual stream)
@@ -215,6 +293,7 @@ struct GemvArgs {
   float *part_v;       // [grid] per-block winners
   int *part_i;
   int32_t *next;       // nullable: argmax written by a one-block reduce
+  RopeAppend ra;       // EPI_ROPE
 };
 
 // several token rows at once (matrix cores): operands split into bf16 hi/lo by k_split
@@ -241,15 +320,14 @@ struct GemmArgs {
   float *part_v;       // EPI_ARGMAX: [M][part_ld] per-block winners
   int *part_i;
   int part_ld;
+  RopeAppend ra;       // EPI_ROPE
 };
 
 struct AttnArgs {
-  const float *qkv;    // [B][qkv_stride]: q [dim], k [kvw], v [kvw] before RoPE
-  int qkv_stride;
-  void *kc, *vc;       // this layer's cache: [rows][kv][max_seq][head]
+  const float *q;      // [B][dim] rotated query heads
+  void *kc, *vc;       // this layer's cache: [rows][kv][max_seq][head], positions 0..t stored
   int kv, max_seq, half;
   int row0;            // cache row of batch entry 0
-  const float *rope_cs, *rope_sn;  // [max_seq][half]
   float *out;          // [B][dim]
   int out_stride;
   float *part_o;       // [B][kv][nch][g][head]
@@ -298,7 +376,7 @@ hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, in
 int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is instantiated
 hipError_t launch_attention(int kvdtype, int head, int g, AttnArgs a, int B, int nch_launch, hipStream_t s);
 int attention_supported(int head, int g);
-int attention_chunk(int kvdtype, int head);  // positions per attention block (fixed per cache type and head)
+int attention_chunk(int kvdtype, int head, int g);  // positions per attention block (per cache type, head, g)
 int gemm_skinny_supported(int wdtype, int K, int M);
 int gemm_skinny_blocks(int N);
 // a split is always followed by its product: the split takes a timing scope's start event, the

@@ -11,7 +11,8 @@
 // of X, B = 16 weight rows transposed: lane l loads 16 contiguous bytes of weight row n0 + l%16.
 // A block owns 16 weight rows (two sets for SwiGLU: gate and up); its 4 wavefronts take interleaved
 // 32-element K steps (a block step reads 256 contiguous bytes of each row) and their sums are added in a
-// fixed order through LDS.  Epilogues as the GEMV: store, residual, SwiGLU, LM head (+ block winners).
+// fixed order through LDS.  Epilogues as the GEMV: store, residual, SwiGLU, RoPE + cache append, LM head
+// (+ block winners).
 #include "common.h"
 
 namespace lm {
@@ -27,7 +28,10 @@ __global__ __launch_bounds__(kThreads) void k_split(SplitArgs a) {
   bf16_t *hi = a.xhi + (size_t)b * a.ldx;
   bf16_t *lo = a.xlo + (size_t)b * a.ldx;
   if (b >= a.M) {
-    for (int k = tid; k < a.K; k += kThreads) hi[k] = lo[k] = 0;
+    for (int k = 2 * tid; k < a.K; k += 2 * kThreads) {
+      *reinterpret_cast<uint32_t *>(hi + k) = 0u;
+      *reinterpret_cast<uint32_t *>(lo + k) = 0u;
+    }
     return;
   }
   const float *x = a.x + (size_t)b * a.ldin;
@@ -43,12 +47,14 @@ __global__ __launch_bounds__(kThreads) void k_split(SplitArgs a) {
     r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
   }
   const GT *g = reinterpret_cast<const GT *>(a.gain);
-  for (int k = tid; k < a.K; k += kThreads) {
-    const float v = NORM ? load_scalar<GT>(g, k) * (x[k] * r) : x[k];
-    const uint16_t h = f32_to_bf16(v);
-    const float rest = v - bf16_to_f32(h);
-    hi[k] = h;
-    lo[k] = f32_to_bf16(rest);
+  // pairs of numbers (K is even): one packed conversion per pair
+  for (int k = 2 * tid; k < a.K; k += 2 * kThreads) {
+    const float v0 = NORM ? load_scalar<GT>(g, k) * (x[k] * r) : x[k];
+    const float v1 = NORM ? load_scalar<GT>(g, k + 1) * (x[k + 1] * r) : x[k + 1];
+    uint32_t h, l;
+    split_bf16x2(v0, v1, h, l);
+    *reinterpret_cast<uint32_t *>(hi + k) = h;
+    *reinterpret_cast<uint32_t *>(lo + k) = l;
   }
 }
 
@@ -67,9 +73,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(GemmArgs a) {
     wrow[0] = reinterpret_cast<const bf16_t *>(a.w[0]) + (size_t)row * a.K;
     wrow[PAIRS - 1] = reinterpret_cast<const bf16_t *>(a.w[1]) + (size_t)row * a.K;
   } else {
-    const bf16_t *base = reinterpret_cast<const bf16_t *>(row >= a.rs[2] ? a.w[2] : (row >= a.rs[1] ? a.w[1] : a.w[0]));
-    const int r0 = row >= a.rs[2] ? a.rs[2] : (row >= a.rs[1] ? a.rs[1] : 0);
-    wrow[0] = base + (size_t)(row - r0) * a.K;
+    const int wr = EPI == EPI_ROPE ? rope_row(row, a.ra.dim + a.ra.kvw, a.ra.hshift) : row;
+    const bf16_t *base = reinterpret_cast<const bf16_t *>(wr >= a.rs[2] ? a.w[2] : (wr >= a.rs[1] ? a.w[1] : a.w[0]));
+    const int r0 = wr >= a.rs[2] ? a.rs[2] : (wr >= a.rs[1] ? a.rs[1] : 0);
+    wrow[0] = base + (size_t)(wr - r0) * a.K;
   }
   f32x4 acc[PAIRS][MT];
 #pragma unroll
@@ -128,6 +135,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(GemmArgs a) {
         *y = a.res[(size_t)t * a.ldres + n] + v[0];
       } else if (EPI == EPI_SWIGLU) {
         *y = (v[0] / (1.0f + expf(-v[0]))) * v[PAIRS - 1];
+      } else if (EPI == EPI_ROPE) {
+        const int j2 = j ^ 1;  // the pair partner (logical rows 2i, 2i+1), in this block's 16 rows
+        const float pv = (red[0][0][t][j2] + red[1][0][t][j2]) + (red[2][0][t][j2] + red[3][0][t][j2]);
+        const size_t ci = (size_t)a.ra.pos[t] * a.ra.half + rope_pair_index(n, a.ra.hshift);
+        const bool qk = n < a.ra.dim + a.ra.kvw;
+        rope_append(a.ra, a.y + (size_t)t * a.ldy, t, n, v[0], pv, qk ? a.ra.rope_cs[ci] : 0.f,
+                    qk ? a.ra.rope_sn[ci] : 0.f);
       } else if (a.y) {
         *y = v[0];
       }
@@ -180,6 +194,7 @@ static hipError_t launch_mt(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool 
     case EPI_RESID: launch(k_gemm_skinny<MT, EPI_RESID>, g, dim3(kThreads), s, false, last, a); break;
     case EPI_SWIGLU: launch(k_gemm_skinny<MT, EPI_SWIGLU>, g, dim3(kThreads), s, false, last, a); break;
     case EPI_ARGMAX: launch(k_gemm_skinny<MT, EPI_ARGMAX>, g, dim3(kThreads), s, false, last, a); break;
+    case EPI_ROPE: launch(k_gemm_skinny<MT, EPI_ROPE>, g, dim3(kThreads), s, false, last, a); break;
   }
   return hipGetLastError();
 }

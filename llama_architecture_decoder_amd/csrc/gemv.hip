@@ -3,7 +3,8 @@
 // y = W x with W [N][K] row-major (row = output, main.bend type LW), F32 or bf16 weights, F32
 // arithmetic.  The projections of main.bend "A layer" (block): q/k/v from the attention norm, o with
 // the first residual, gate/up from the MLP norm with SwiGLU (silu(g) * u, silu(z) = z / (1 + e^-z)),
-// down with the second residual; and "The model" head_of: logits = W_lm * rmsnorm(x, lnf) with the
+// down with the second residual; the q/k/v projection can also finish with RoPE and the cache append
+// (EPI_ROPE); and "The model" head_of: logits = W_lm * rmsnorm(x, lnf) with the
 // argmax of main.bend `argmax` (first index of the largest value).
 //
 // Layout of the work: one 256-thread block owns R consecutive rows at a time (a row group) and the
@@ -71,12 +72,18 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   constexpr int PAIRS = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int R = RowsPerGroup<KCH, PAIRS>::value;
   constexpr int NV = R * PAIRS;  // partial sums per thread per group
+  static_assert(EPI != EPI_ROPE || NORM, "the RoPE epilogue's cos/sin reach LDS through the norm prologue's barrier");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunk = a.K / E;
   const bool ragged = (nchunk % kThreads) != 0;  // uniform: some threads' last chunk is past K
 
   __shared__ float red[4][NV];
   __shared__ float ss_w[4];
+  __shared__ float rope_s[EPI == EPI_ROPE ? 2 * 64 : 1];  // cos | sin of the position (half <= 64)
+  if (EPI == EPI_ROPE && tid < 2 * a.ra.half) {
+    const size_t ci = (size_t)a.ra.pos[0] * a.ra.half + (tid % a.ra.half);
+    rope_s[tid] = tid < a.ra.half ? a.ra.rope_cs[ci] : a.ra.rope_sn[ci];
+  }
 
   // ---- the input slice of this thread: chunks j*256 + tid
   float xr[KCH][E];
@@ -135,8 +142,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         const int row = row0 + r;
         // unconditional loads: a row past N reads row N-1 (its result is never stored) and a chunk past
         // the row end reads the row's last chunk (zeroed below)
-        const WT *wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)min(row, a.N - 1) * (size_t)a.K
-                                           : row_ptr<WT>(a, min(row, a.N - 1));
+        const int crow = min(row, a.N - 1);
+        const WT *wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)crow * (size_t)a.K
+                       : (EPI == EPI_ROPE) ? row_ptr<WT>(a, rope_row(crow, a.ra.dim + a.ra.kvw, a.ra.hshift))
+                                           : row_ptr<WT>(a, crow);
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
           const int ci = min(j * kThreads + tid, nchunk - 1);
@@ -182,6 +191,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         } else if (EPI == EPI_SWIGLU) {
           const float gt = val[0], up = val[PAIRS - 1];
           a.y[row] = (gt / (1.0f + expf(-gt))) * up;
+        } else if (EPI == EPI_ROPE) {
+          // the pair partner is logical row row ^ 1, in this group (R is even)
+          const int v2 = tid ^ 1;
+          const float pv = (red[0][v2] + red[1][v2]) + (red[2][v2] + red[3][v2]);
+          const int ci = rope_pair_index(row, a.ra.hshift);
+          rope_append(a.ra, a.y, 0, row, val[0], pv, rope_s[ci], rope_s[a.ra.half + ci]);
         } else {  // EPI_ARGMAX
           if (a.y) a.y[row] = val[0];
         }
@@ -311,6 +326,10 @@ static hipError_t launch_typed(GemvEpi epi, bool norm, GemvArgs a, int grid_cap,
   if (grid < 1) grid = 1;
   const dim3 g(grid);
   if (epi == EPI_STORE && norm) return dispatch_kch<WT, EPI_STORE, true>(kch, g, a, s, true);
+  if (epi == EPI_ROPE && norm) {
+    if (R % 2) return hipErrorInvalidValue;
+    return dispatch_kch<WT, EPI_ROPE, true>(kch, g, a, s, true);
+  }
   if (epi == EPI_STORE && !norm) return dispatch_kch<WT, EPI_STORE, false>(kch, g, a, s, true);
   if (epi == EPI_RESID && !norm) return dispatch_kch<WT, EPI_RESID, false>(kch, g, a, s, true);
   if (epi == EPI_SWIGLU && norm) return dispatch_kch<WT, EPI_SWIGLU, true>(kch, g, a, s, true);

@@ -257,12 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
       const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       uint32_t h4[4], l4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
-        const uint16_t r0 = f32_to_bf16(f[2 * e] - bf16_to_f32(h0)), r1 = f32_to_bf16(f[2 * e + 1] - bf16_to_f32(h1));
-        h4[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        l4[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
-      }
+      for (int e = 0; e < 4; ++e) split_bf16x2(f[2 * e], f[2 * e + 1], h4[e], l4[e]);
       qh[ks] = u32x4{h4[0], h4[1], h4[2], h4[3]};
       ql[ks] = u32x4{l4[0], l4[1], l4[2], l4[3]};
     }
@@ -352,13 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
         const int mt = kk >> 1, r0 = (kk & 1) * 8;
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float f0 = s[mt][r0 + 2 * e], f1 = s[mt][r0 + 2 * e + 1];
-          const uint16_t h0 = f32_to_bf16(f0), h1 = f32_to_bf16(f1);
-          const uint16_t q0 = f32_to_bf16(f0 - bf16_to_f32(h0)), q1 = f32_to_bf16(f1 - bf16_to_f32(h1));
-          ph[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          pl[e] = (uint32_t)q0 | ((uint32_t)q1 << 16);
-        }
+        for (int e = 0; e < 4; ++e) split_bf16x2(s[mt][r0 + 2 * e], s[mt][r0 + 2 * e + 1], ph[e], pl[e]);
         const u32x4 pfh = u32x4{ph[0], ph[1], ph[2], ph[3]}, pfl = u32x4{pl[0], pl[1], pl[2], pl[3]};
         // keys of slot e of half hsel within the 16-group: 8(e/4) + 4 hsel + e%4
         const int kb = kk * 16 + 4 * hsel;
