@@ -314,7 +314,7 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
 
 // Several token rows with bf16 weights: each projection is one matrix-core product over all rows (the
 // weights stream once per step instead of once per row); operands are split into bf16 hi/lo first.
-int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int nch_launch, int B, float *logits, int32_t *next,
+int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, float *logits, int32_t *next,
                   bool want_head) {
   const Dims &d = x.d;
   const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f, V = (int)d.vocab;
@@ -377,7 +377,7 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int nch_launch, int 
     }
     {
       ProfScope ps(LLAMA_K_ATTN, x.s);
-      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
+      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, tmax, x.s)))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_O, x.s);
@@ -533,7 +533,6 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   // attention: one block per (chunk of positions, kv head, row)
   int tmax = 0;
   for (int b = 0; b < B; ++b) tmax = pos[b] > tmax ? pos[b] : tmax;
-  const int nch_launch = tmax / attention_chunk(x.c->kv_dtype, (int)d.head, (int)d.g) + 1;
 
   AttnArgs aa = {};
   aa.q = x.at<float>(x.L.qrot);
@@ -564,7 +563,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   for (int b = 0; b < B; ++b) ra.pos[b] = pos[b];
 
   if (B > 1 && gemm_skinny_supported(wdt, H, B) && gemm_skinny_supported(wdt, F, B) && !trace)
-    return run_step_rows(x, aa, ra, nch_launch, B, logits, next, want_head);
+    return run_step_rows(x, aa, ra, tmax, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
   for (int l = 0; l < (int)d.layers; ++l) {
@@ -595,7 +594,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
     }
     {
       ProfScope ps(LLAMA_K_ATTN, x.s);
-      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, nch_launch, x.s)))) return rc;
+      if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, tmax, x.s)))) return rc;
     }
     float *tr = trace ? trace + (size_t)l * tstride : nullptr;
     if (tr) {

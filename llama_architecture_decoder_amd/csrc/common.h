@@ -374,9 +374,11 @@ inline void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, bool first, b
 // host-side launchers (one per kernel family); return hipSuccess or the launch error
 hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, int grid_cap, hipStream_t s);
 int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is instantiated
-hipError_t launch_attention(int kvdtype, int head, int g, AttnArgs a, int B, int nch_launch, hipStream_t s);
+// rows' positions in a.pos[0..B-1], tmax = their maximum
+hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int tmax, hipStream_t s);
 int attention_supported(int head, int g);
-int attention_chunk(int kvdtype, int head, int g);  // positions per attention block (per cache type, head, g)
+int attention_chunk(int kvdtype, int head, int g);
+ // the smallest chunk of positions an attention block takes
 int gemm_skinny_supported(int wdtype, int K, int M);
 int gemm_skinny_blocks(int N);
 // a split is always followed by its product: the split takes a timing scope's start event, the
