@@ -26,6 +26,7 @@ constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 // Defaults measured on MI355X at the 8B shape; LLAMA_GEMV_GRID sets all, LLAMA_GEMV_GRID_<NAME> one.
 struct Tun {
   int qkv = 1024, o = 512, gate_up = 2048, down = 768, lm = 512;
+  int rows_blocks = 512;  // batched rows: K slices are chosen for about this many blocks per product
   static void env(const char *name, int &v) {
     if (const char *e = getenv(name))
       if (atoi(e) > 0) v = atoi(e);
@@ -39,6 +40,7 @@ struct Tun {
     env("LLAMA_GEMV_GRID_GATE_UP", gate_up);
     env("LLAMA_GEMV_GRID_DOWN", down);
     env("LLAMA_GEMV_GRID_LM", lm);
+    env("LLAMA_ROWS_BLOCKS", rows_blocks);
   }
 };
 const Tun &tun() {
@@ -115,7 +117,8 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, total;
+  size_t status, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
+      total;
   int nch;
   int lm_ld;  // per-row stride of the LM head's block winners
   int mpad;   // token rows of the split operands (max_batch rounded up to 16)
@@ -123,9 +126,25 @@ struct WsLayout {
 
 // the matrix-core prefill: bf16 weights and cache, head 64 or 128, K of every product a multiple of 32
 bool prefill_tiled_ok(const llama_cfg *c) {
+  const int64_t dim = 2 * (int64_t)c->half * c->kv * c->g;
   return c->weight_dtype == LLAMA_BF16 && c->kv_dtype == LLAMA_BF16 && (c->half == 32 || c->half == 64) &&
-         gemm_skinny_supported(LLAMA_BF16, (int)(2 * c->half * c->kv * c->g), 1) &&
-         gemm_skinny_supported(LLAMA_BF16, c->f, 1);
+         dim % 32 == 0 && c->f % 32 == 0;
+}
+
+// the matrix-core path for several decode rows: bf16 weights, K of every product a multiple of 128
+bool rows_ok(const llama_cfg *c, int B) {
+  const int dim = (int)(2 * (int64_t)c->half * c->kv * c->g);
+  return B > 1 && gemm_rows_supported(c->weight_dtype, dim, B) && gemm_rows_supported(c->weight_dtype, c->f, B);
+}
+
+// K slices of each batched-rows product (q|k|v, o, gate/up, down)
+struct RowsSlices {
+  int qkv, o, gu, down;
+};
+RowsSlices rows_slices(const Dims &d) {
+  const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f, T = tun().rows_blocks;
+  return {gemm_rows_slices(H + 2 * KW, H, false, T), gemm_rows_slices(H, H, false, T),
+          gemm_rows_slices(F, H, true, T), gemm_rows_slices(H, F, false, T)};
 }
 
 WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill) {
@@ -152,15 +171,33 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.m = take(sizeof(float) * rows * d.f);
   L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
   L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
+  const bool rows_path = rows_ok(c, max_batch);
   L.lm_ld = kLmGridMax;
-  if (max_batch > 1 && gemm_skinny_blocks((int)d.vocab) > L.lm_ld) L.lm_ld = gemm_skinny_blocks((int)d.vocab);
+  if (rows_path && gemm_rows_blocks((int)d.vocab, false) > L.lm_ld) L.lm_ld = gemm_rows_blocks((int)d.vocab, false);
   L.lm_v = take(sizeof(float) * (size_t)max_batch * L.lm_ld);
   L.lm_i = take(sizeof(int) * (size_t)max_batch * L.lm_ld);
-  L.mpad = max_batch > 1 ? (max_batch + 15) / 16 * 16 : 0;
+  L.mpad = rows_path ? (max_batch + 15) / 16 * 16 : 0;
   if (prows > 0 && gemm_tiled_rows(prows) > L.mpad) L.mpad = gemm_tiled_rows(prows);
   const int64_t kmax = d.dim > d.f ? d.dim : d.f;
   L.xhi = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
   L.xlo = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
+  // batched rows: a second operand pair (the MLP's inner activations) and the K-slice partial sums
+  const int64_t mrows = rows_path ? (max_batch + 15) / 16 * 16 : 0;
+  L.xhi2 = take(sizeof(uint16_t) * (size_t)mrows * d.f);
+  L.xlo2 = take(sizeof(uint16_t) * (size_t)mrows * d.f);
+  size_t part = 0;
+  if (rows_path) {
+    const RowsSlices S = rows_slices(d);
+    auto need = [&](int slices, int64_t nout) {
+      const size_t n = (size_t)slices * (size_t)max_batch * (size_t)nout;
+      part = n > part ? n : part;
+    };
+    need(S.qkv, d.dim + 2 * d.kvw);
+    need(S.o, d.dim);
+    need(S.gu, 2 * d.f);
+    need(S.down, d.dim);
+  }
+  L.part = take(sizeof(float) * part);
   L.total = o;
   return L;
 }
@@ -313,7 +350,9 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
 }
 
 // Several token rows with bf16 weights: each projection is one matrix-core product over all rows (the
-// weights stream once per step instead of once per row); operands are split into bf16 hi/lo first.
+// weights stream once per step instead of once per row), on bf16 hi/lo operands.  The operands of the
+// next product are formed where the previous one is finished: the residual + RMSNorm + split after o and
+// down (k_rows_reduce_norm), the SwiGLU output straight from the gate/up product.
 int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, float *logits, int32_t *next,
                   bool want_head) {
   const Dims &d = x.d;
@@ -322,29 +361,32 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
   float *xs = x.at<float>(x.L.x);
   float *qkv = x.at<float>(x.L.qkv);
   float *att = x.at<float>(x.L.attn);
-  float *mm = x.at<float>(x.L.m);
-  bf16_t *xhi = x.at<bf16_t>(x.L.xhi), *xlo = x.at<bf16_t>(x.L.xlo);
+  bf16_t *ahi = x.at<bf16_t>(x.L.xhi), *alo = x.at<bf16_t>(x.L.xlo);    // operands with K = dim
+  bf16_t *bhi = x.at<bf16_t>(x.L.xhi2), *blo = x.at<bf16_t>(x.L.xlo2);  // operands with K = f
+  float *part = x.at<float>(x.L.part);
   const int wdt = x.c->weight_dtype;
   const int qkv_stride = H + 2 * KW;
-  auto split = [&](const float *in, int ldin, const void *gain, int K) {
+  const RowsSlices S = rows_slices(d);
+  auto split = [&](const float *in, const void *gain) {
     SplitArgs sa = {};
     sa.x = in;
-    sa.ldin = ldin;
+    sa.ldin = H;
     sa.gain = gain;
     sa.eps = x.c->eps;
-    sa.K = K;
+    sa.K = H;
     sa.M = B;
-    sa.xhi = xhi;
-    sa.xlo = xlo;
-    sa.ldx = K;
+    sa.xhi = ahi;
+    sa.xlo = alo;
+    sa.ldx = H;
     return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
   };
-  auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
-                  int ldy, const float *res, bool last) {
+  auto gemm = [&](GemvEpi epi, bool wide_in, const void *w0, const void *w1, const void *w2, int r1, int r2, int N,
+                  int slices, float *y, int ldy, bool first, bool last) {
     GemmArgs ga = {};
-    ga.xhi = xhi;
-    ga.xlo = xlo;
-    ga.ldx = K;
+    ga.xhi = wide_in ? bhi : ahi;
+    ga.xlo = wide_in ? blo : alo;
+    ga.K = wide_in ? F : H;
+    ga.ldx = ga.K;
     ga.w[0] = w0;
     ga.w[1] = w1;
     ga.w[2] = w2;
@@ -353,27 +395,47 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
     ga.rs[2] = r2;
     ga.rs[3] = N;
     ga.N = N;
-    ga.K = K;
     ga.M = B;
     ga.y = y;
     ga.ldy = ldy;
-    ga.res = res;
-    ga.ldres = ldy;
+    ga.part = part;
+    ga.ohi = bhi;
+    ga.olo = blo;
+    ga.ldo = F;
     ga.part_v = x.at<float>(x.L.lm_v);
     ga.part_i = x.at<int>(x.L.lm_i);
     ga.part_ld = x.L.lm_ld;
     if (epi == EPI_ROPE) ga.ra = ra;
-    return hip_rc(launch_gemm_skinny(epi, ga, x.s, last));
+    return hip_rc(launch_gemm_rows(epi, ga, slices, x.s, first, last));
+  };
+  auto reduce_norm = [&](int slices, const void *gain) {
+    RowsNormArgs na = {};
+    na.part = part;
+    na.S = slices;
+    na.M = B;
+    na.N = H;
+    na.x = xs;
+    na.ldx = H;
+    na.gain = gain;
+    na.eps = x.c->eps;
+    na.xhi = ahi;
+    na.xlo = alo;
+    na.ldo = H;
+    return hip_rc(launch_rows_reduce_norm(wdt, na, x.s, true));
   };
   int rc;
+  {
+    ProfScope ps(LLAMA_K_QKV, x.s);
+    if ((rc = split(xs, x.w->layers[0].ln1))) return rc;  // layer 0's operands; later layers' come from down
+  }
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
     aa.kc = ra.kc = layer_cache(x, x.kv->k, l);
     aa.vc = ra.vc = layer_cache(x, x.kv->v, l);
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
-      if ((rc = split(xs, H, lw.ln1, H))) return rc;
-      if ((rc = gemm(EPI_ROPE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, true))) return rc;
+      if ((rc = gemm(EPI_ROPE, false, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, S.qkv, qkv, qkv_stride, true, true)))
+        return rc;
     }
     {
       ProfScope ps(LLAMA_K_ATTN, x.s);
@@ -381,28 +443,30 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
     }
     {
       ProfScope ps(LLAMA_K_O, x.s);
-      if ((rc = split(att, H, nullptr, H))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, true))) return rc;
+      if ((rc = split(att, nullptr))) return rc;
+      if ((rc = gemm(EPI_RESID, false, lw.wo, lw.wo, lw.wo, H, H, H, S.o, nullptr, H, false, false))) return rc;
+      if ((rc = reduce_norm(S.o, lw.ln2))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
-      if ((rc = split(xs, H, lw.ln2, H))) return rc;
-      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr, true))) return rc;
+      if ((rc = gemm(EPI_SWIGLU, false, lw.w_gate, lw.w_up, lw.w_up, F, F, F, S.gu, nullptr, F, true, true))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_DOWN, x.s);
-      if ((rc = split(mm, F, nullptr, F))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true))) return rc;
+      const void *next_gain = l + 1 < (int)d.layers ? x.w->layers[l + 1].ln1 : x.w->final_norm;
+      if ((rc = gemm(EPI_RESID, true, lw.w_down, lw.w_down, lw.w_down, H, H, H, S.down, nullptr, H, true, false)))
+        return rc;
+      if ((rc = reduce_norm(S.down, next_gain))) return rc;
     }
   }
   if (!want_head || (!logits && !next)) return LLAMA_OK;
+  // the operands hold rmsnorm(x, final norm) (the last down's reduce)
   ProfScope ps(LLAMA_K_LM_HEAD, x.s);
-  if ((rc = split(xs, H, x.w->final_norm, H))) return rc;
   const void *wl = x.c->tied_lm_head ? x.w->emb : x.w->lm_head;
-  if ((rc = gemm(EPI_ARGMAX, wl, wl, wl, V, V, V, H, logits, V, nullptr, next == nullptr))) return rc;
+  if ((rc = gemm(EPI_ARGMAX, false, wl, wl, wl, V, V, V, 1, logits, V, true, next == nullptr))) return rc;
   if (next)
-    return hip_rc(launch_argmax_final(x.at<float>(x.L.lm_v), x.at<int>(x.L.lm_i), gemm_skinny_blocks(V), x.L.lm_ld, B,
-                                      next, x.s));
+    return hip_rc(launch_argmax_final(x.at<float>(x.L.lm_v), x.at<int>(x.L.lm_i), gemm_rows_blocks(V, false),
+                                      x.L.lm_ld, B, next, x.s));
   return LLAMA_OK;
 }
 
@@ -562,7 +626,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   ra.rope_sn = x.at<float>(x.L.rope_sn);
   for (int b = 0; b < B; ++b) ra.pos[b] = pos[b];
 
-  if (B > 1 && gemm_skinny_supported(wdt, H, B) && gemm_skinny_supported(wdt, F, B) && !trace)
+  if (rows_ok(x.c, B) && !trace)
     return run_step_rows(x, aa, ra, tmax, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;

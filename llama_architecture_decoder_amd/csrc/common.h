@@ -321,6 +321,23 @@ struct GemmArgs {
   int *part_i;
   int part_ld;
   RopeAppend ra;       // EPI_ROPE
+  // k_gemm_rows
+  float *part;         // [S][M][N] partial sums of the K slices (SwiGLU: [S][M][2N], gate then up)
+  int tiles_per_slice; // set by the launcher
+  bf16_t *ohi, *olo;   // EPI_SWIGLU: the output as the next product's operands [mpad][ldo]
+  int ldo;
+};
+
+// x[t] += sum_s part[s][t][:], then the next product's operands from rmsnorm(x[t], gain)
+struct RowsNormArgs {
+  const float *part;   // [S][M][N]
+  int S, M, N;
+  float *x;            // [M][ldx] residual stream (updated in place)
+  int ldx;
+  const void *gain;    // RMSNorm gains [N] (weight type)
+  float eps;
+  bf16_t *xhi, *xlo;   // [mpad][ldo]
+  int ldo;
 };
 
 struct AttnArgs {
@@ -379,12 +396,15 @@ hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int
 int attention_supported(int head, int g);
 int attention_chunk(int kvdtype, int head, int g);
  // the smallest chunk of positions an attention block takes
-int gemm_skinny_supported(int wdtype, int K, int M);
-int gemm_skinny_blocks(int N);
+int gemm_rows_supported(int wdtype, int K, int M);  // k_gemm_rows: bf16 weights, K % 128 == 0, 1 <= M <= 64
+int gemm_rows_blocks(int N, bool swiglu);
+int gemm_rows_slices(int N, int K, bool swiglu, int target);
 // a split is always followed by its product: the split takes a timing scope's start event, the
 // product (and, for the LM head, the argmax reduce) its stop event
 hipError_t launch_split(int gdtype, bool norm, const SplitArgs &a, int mpad, hipStream_t s);
-hipError_t launch_gemm_skinny(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
+// S K slices; `first`/`last` mark the timing scope's first and last launch
+hipError_t launch_gemm_rows(GemvEpi epi, GemmArgs a, int S, hipStream_t s, bool first, bool last);
+hipError_t launch_rows_reduce_norm(int gdtype, const RowsNormArgs &a, hipStream_t s, bool last);
 // many token rows (prefill): 128 x 128 tiles; the operands need gemm_tiled_rows(M) rows (zero-padded)
 int gemm_tiled_rows(int M);
 hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);

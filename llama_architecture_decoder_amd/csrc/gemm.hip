@@ -7,12 +7,22 @@
 // fragment, so products are exact and the result matches an F32 product to about 2^-17 relative.
 //
 // v_mfma_f32_16x16x32_bf16: A (16 x 32) lane l holds A[l%16][8(l/16) .. +8], B (32 x 16) lane l holds
-// B[8(l/16) .. +8][l%16], C (16 x 16) lane l holds C[4(l/16) + r][l%16], r < 4.  Here A = a 16-token tile
-// of X, B = 16 weight rows transposed: lane l loads 16 contiguous bytes of weight row n0 + l%16.
-// A block owns 16 weight rows (two sets for SwiGLU: gate and up); its 4 wavefronts take interleaved
-// 32-element K steps (a block step reads 256 contiguous bytes of each row) and their sums are added in a
-// fixed order through LDS.  Epilogues as the GEMV: store, residual, SwiGLU, RoPE + cache append, LM head
-// (+ block winners).
+// B[8(l/16) .. +8][l%16], C (16 x 16) lane l holds C[4(l/16) + r][l%16], r < 4.  A = a 16-token tile of
+// X (from LDS), B = 16 weight rows transposed: lane l loads 16 contiguous bytes of weight row l%16.
+//
+// k_gemm_rows: block (bx, s) owns 128 consecutive outputs (wave w: outputs 32w .. +32 as two 16-row
+// tiles; SwiGLU: 64 outputs, wave w's tiles are the gate and the up rows of outputs 16w .. +16) over the
+// s-th slice of K.  X tiles of 128 columns are staged in LDS once for the 4 waves (double buffered); each
+// wave keeps the next tile's weight loads in flight while it multiplies the current one.  With one slice
+// the epilogue runs in the kernel; with several, each slice writes its partial sums and a reduce kernel
+// adds them in slice order (deterministic) and runs the epilogue.  The number of slices is chosen so
+// the launch has ~512 blocks: at these sizes every CU must see all of X, so X re-reads, not weights,
+// decide how many output rows a block should own.
+//
+// Epilogues: STORE, RESID (y = res + XW^T), SWIGLU (silu(gate) * up, written straight as the next
+// product's bf16 hi/lo operands), ROPE (RoPE + cache append, as the GEMV), ARGMAX (LM head: logits and
+// per-block winners).  The residual + RMSNorm + split of the next product's input are fused into the
+// reduce kernel k_rows_reduce_norm (one block per token row).
 #include "common.h"
 
 namespace lm {
@@ -58,119 +68,340 @@ __global__ __launch_bounds__(kThreads) void k_split(SplitArgs a) {
   }
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
 
-template <int MT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm_skinny(GemmArgs a) {
-  constexpr int PAIRS = (EPI == EPI_SWIGLU) ? 2 : 1;
-  constexpr int U = 4;  // K steps per wavefront per iteration (loads in flight)
+constexpr int kRT = 128;           // K columns per tile
+constexpr int kRowsOut = 128;      // outputs per block (SwiGLU: 64)
+constexpr int kLdt = kRT + 8;      // LDS row of an X tile (bf16): 272 bytes, 16-byte reads of 16 rows hit distinct banks
+
+// weight row (in the stacked q|k|v or plain matrix) that output n of the epilogue reads
+template <int EPI>
+__device__ __forceinline__ const bf16_t *weight_row(const GemmArgs &a, int n, int which) {
+  if (EPI == EPI_SWIGLU) return reinterpret_cast<const bf16_t *>(a.w[which]) + (size_t)n * a.K;
+  const int wr = EPI == EPI_ROPE ? rope_row(n, a.ra.dim + a.ra.kvw, a.ra.hshift) : n;
+  const int seg = wr >= a.rs[2] ? 2 : (wr >= a.rs[1] ? 1 : 0);
+  return reinterpret_cast<const bf16_t *>(a.w[seg]) + (size_t)(wr - a.rs[seg]) * a.K;
+}
+
+template <int MT, int EPI, bool PART>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int ROWS = SW ? kRowsOut / 2 : kRowsOut;
+  constexpr int XCH = MT * 16 * kRT / 8 / kThreads;  // 16-byte chunks of one X array per thread per tile (= MT)
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][2][MT * 16 * kLdt];  // [buffer][hi, lo]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int nl = lane & 15, q = lane >> 4;
-  const int row = min(n0 + nl, a.N - 1);
-  const bf16_t *wrow[PAIRS];
-  if (EPI == EPI_SWIGLU) {
-    wrow[0] = reinterpret_cast<const bf16_t *>(a.w[0]) + (size_t)row * a.K;
-    wrow[PAIRS - 1] = reinterpret_cast<const bf16_t *>(a.w[1]) + (size_t)row * a.K;
-  } else {
-    const int wr = EPI == EPI_ROPE ? rope_row(row, a.ra.dim + a.ra.kvw, a.ra.hshift) : row;
-    const bf16_t *base = reinterpret_cast<const bf16_t *>(wr >= a.rs[2] ? a.w[2] : (wr >= a.rs[1] ? a.w[1] : a.w[0]));
-    const int r0 = wr >= a.rs[2] ? a.rs[2] : (wr >= a.rs[1] ? a.rs[1] : 0);
-    wrow[0] = base + (size_t)(wr - r0) * a.K;
-  }
-  f32x4 acc[PAIRS][MT];
-#pragma unroll
-  for (int p = 0; p < PAIRS; ++p)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[p][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int l16 = lane & 15, q8 = (lane >> 4) * 8;
+  const int nb = blockIdx.x * ROWS;
+  const int ntile_all = a.K / kRT;
+  const int t0 = blockIdx.y * a.tiles_per_slice;
+  const int nt = min(a.tiles_per_slice, ntile_all - t0);  // >= 1 (slices are never empty)
 
-  const int ksteps = a.K / 32;
-  for (int ks0 = wave; ks0 < ksteps; ks0 += 4 * U) {
-    u32x4 wv[PAIRS][U], xh[U][MT], xl[U][MT];
+  // this lane's two weight rows (tile j), at its 16-byte piece of the first K step of the slice
+  const bf16_t *wp[2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = min(ks0 + 4 * u, ksteps - 1);  // a step past the end repeats the last one, unused
-      const size_t ko = (size_t)ks * 32 + q * 8;
+  for (int j = 0; j < 2; ++j) {
+    const int n = min(SW ? nb + 16 * wave + l16 : nb + 32 * wave + 16 * j + l16, a.N - 1);
+    wp[j] = weight_row<EPI>(a, n, j) + (size_t)t0 * kRT + q8;
+  }
+  // X staging: chunk c = tid + 256 i is row c / 16, columns 8 (c % 16) .. +8 of the tile
+  const bf16_t *xg[2][XCH];
+  int xo[XCH];
 #pragma unroll
-      for (int p = 0; p < PAIRS; ++p) wv[p][u] = load_stream16(wrow[p] + ko);
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tid + kThreads * i, r = c >> 4, cc = (c & 15) * 8;
+    xo[i] = r * kLdt + cc;
+    xg[0][i] = a.xhi + (size_t)r * a.ldx + (size_t)t0 * kRT + cc;
+    xg[1][i] = a.xlo + (size_t)r * a.ldx + (size_t)t0 * kRT + cc;
+  }
+
+  u32x4 xr[2][XCH];
+  u32x4 w0[4][2], w1[4][2];
+  auto load_x = [&](int t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) xr[h][i] = load16(xg[h][i] + (size_t)t * kRT);
+  };
+  auto stash_x = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4 *>(&xs[buf][h][xo[i]]) = xr[h][i];
+  };
+  auto load_w = [&](u32x4 (&w)[4][2], int t) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[ks][j] = load_stream16(wp[j] + (size_t)t * kRT + ks * 32);
+  };
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const u32x4 (&w)[4][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        xh[u][m] = load16(a.xhi + (size_t)(m * 16 + nl) * a.ldx + ko);
-        xl[u][m] = load16(a.xlo + (size_t)(m * 16 + nl) * a.ldx + ko);
+        const int off = (m * 16 + l16) * kLdt + ks * 32 + q8;
+        const u32x4 ah = *reinterpret_cast<const u32x4 *>(&xs[buf][0][off]);
+        const u32x4 al = *reinterpret_cast<const u32x4 *>(&xs[buf][1][off]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[m][j] = mfma16(ah, w[ks][j], acc[m][j]);
+          acc[m][j] = mfma16(al, w[ks][j], acc[m][j]);
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ks0 + 4 * u < ksteps) {
-#pragma unroll
-        for (int p = 0; p < PAIRS; ++p)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh[u][m]), as_bf16x8(wv[p][u]), acc[p][m], 0, 0, 0);
-            acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl[u][m]), as_bf16x8(wv[p][u]), acc[p][m], 0, 0, 0);
-          }
-      }
+  };
+
+  // tiles in pairs (t even: buffer 0 and w0, t odd: buffer 1 and w1); the next tile's X and weight loads
+  // are in flight while a tile is multiplied, and LDS barriers leave them in flight
+  load_x(0);
+  load_w(w0, 0);
+  stash_x(0);
+  lds_barrier();
+  for (int t = 0; t < nt; t += 2) {
+    if (t + 1 < nt) {
+      load_x(t + 1);
+      load_w(w1, t + 1);
+    }
+    compute(0, w0);
+    if (t + 1 >= nt) break;
+    stash_x(1);
+    lds_barrier();
+    if (t + 2 < nt) {
+      load_x(t + 2);
+      load_w(w0, t + 2);
+    }
+    compute(1, w1);
+    if (t + 2 < nt) {
+      stash_x(0);
+      lds_barrier();
     }
   }
 
-  // the 4 wavefronts' sums, added in a fixed order; lane l holds C[4q + r][nl] of each tile
-  __shared__ float red[4][PAIRS][MT * 16][16];
-#pragma unroll
-  for (int p = 0; p < PAIRS; ++p)
+  // lane holds C[token 4(lane/16) + r][output l16] of tile (m, j)
+  if (PART) {
+    // partial sums of this slice: part[s][t][n], n over the N (SwiGLU: 2N, gate then up) outputs
+    const int nout = SW ? 2 * a.N : a.N;
+    float *pp = a.part + (size_t)blockIdx.y * a.M * nout;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][p][m * 16 + 4 * q + r][nl] = acc[p][m][r];
-  lds_barrier();
-  for (int idx = tid; idx < MT * 16 * 16; idx += kThreads) {
-    const int t = idx / 16, j = idx % 16, n = n0 + j;
-    float v[PAIRS];
+      for (int r = 0; r < 4; ++r) {
+        const int t = m * 16 + (lane >> 4) * 4 + r;
+        if (t >= a.M) continue;
 #pragma unroll
-    for (int p = 0; p < PAIRS; ++p) v[p] = (red[0][p][t][j] + red[1][p][t][j]) + (red[2][p][t][j] + red[3][p][t][j]);
-    if (t < a.M && n < a.N) {
-      float *y = a.y + (size_t)t * a.ldy + n;
-      if (EPI == EPI_STORE) {
-        *y = v[0];
-      } else if (EPI == EPI_RESID) {
-        *y = a.res[(size_t)t * a.ldres + n] + v[0];
-      } else if (EPI == EPI_SWIGLU) {
-        *y = (v[0] / (1.0f + expf(-v[0]))) * v[PAIRS - 1];
-      } else if (EPI == EPI_ROPE) {
-        const int j2 = j ^ 1;  // the pair partner (logical rows 2i, 2i+1), in this block's 16 rows
-        const float pv = (red[0][0][t][j2] + red[1][0][t][j2]) + (red[2][0][t][j2] + red[3][0][t][j2]);
-        const size_t ci = (size_t)a.ra.pos[t] * a.ra.half + rope_pair_index(n, a.ra.hshift);
-        const bool qk = n < a.ra.dim + a.ra.kvw;
-        rope_append(a.ra, a.y + (size_t)t * a.ldy, t, n, v[0], pv, qk ? a.ra.rope_cs[ci] : 0.f,
-                    qk ? a.ra.rope_sn[ci] : 0.f);
-      } else if (a.y) {
-        *y = v[0];
-      }
-    }
-    if (EPI == EPI_ARGMAX) red[0][0][t][j] = (t < a.M && n < a.N) ? v[0] : -INFINITY;
-  }
-  if (EPI == EPI_ARGMAX) {
-    lds_barrier();
-    // winner of this block's 16 rows for every token: first index of the largest value
-    for (int t = tid; t < MT * 16; t += kThreads) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int j = 0; j < 16; ++j) {
-        const float v = red[0][0][t][j];
-        if (v > bv) {
-          bv = v;
-          bi = n0 + j;
+        for (int j = 0; j < 2; ++j) {
+          const int n = SW ? nb + 16 * wave + l16 : nb + 32 * wave + 16 * j + l16;
+          if (n < a.N) pp[(size_t)t * nout + (SW ? j * a.N : 0) + n] = acc[m][j][r];
         }
       }
-      if (t < a.M) {
-        a.part_v[(size_t)t * a.part_ld + blockIdx.x] = bv;
-        a.part_i[(size_t)t * a.part_ld + blockIdx.x] = bi;
+    return;
+  }
+  if (EPI == EPI_ARGMAX) {
+    // per token: this block's largest logit and its first index
+    __shared__ float bv_s[4][MT * 16];
+    __shared__ int bi_s[4][MT * 16];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = m * 16 + (lane >> 4) * 4 + r;
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = nb + 32 * wave + 16 * j + l16;
+          const float v = acc[m][j][r];
+          if (t < a.M && n < a.N) {
+            if (a.y) a.y[(size_t)t * a.ldy + n] = v;
+            if (v > bv) {
+              bv = v;
+              bi = n;
+            }
+          }
+        }
+        // over the 16 lanes of the row (outputs l16); ties keep the lower index
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (l16 == 0) {
+          bv_s[wave][t] = bv;
+          bi_s[wave][t] = bi;
+        }
+      }
+    lds_barrier();
+    for (int t = tid; t < a.M; t += kThreads) {
+      float bv = bv_s[0][t];
+      int bi = bi_s[0][t];
+#pragma unroll
+      for (int w = 1; w < 4; ++w)
+        if (bv_s[w][t] > bv || (bv_s[w][t] == bv && bi_s[w][t] < bi)) {
+          bv = bv_s[w][t];
+          bi = bi_s[w][t];
+        }
+      a.part_v[(size_t)t * a.part_ld + blockIdx.x] = bv;
+      a.part_i[(size_t)t * a.part_ld + blockIdx.x] = bi;
+    }
+    return;
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = m * 16 + (lane >> 4) * 4 + r;
+      if (SW) {
+        // m = silu(gate) * up, straight to the next product's operands: lanes l, l+1 hold outputs n, n+1
+        const int n = nb + 16 * wave + l16;
+        const float gt = acc[m][0][r], up = acc[m][1][r];
+        const float v = (gt / (1.0f + expf(-gt))) * up;
+        const float v1 = __shfl_xor(v, 1);
+        if (t < a.M && n < a.N && (n & 1) == 0) {
+          uint32_t h, l;
+          split_bf16x2(v, v1, h, l);
+          *reinterpret_cast<uint32_t *>(a.ohi + (size_t)t * a.ldo + n) = h;
+          *reinterpret_cast<uint32_t *>(a.olo + (size_t)t * a.ldo + n) = l;
+        }
+        continue;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = nb + 32 * wave + 16 * j + l16;
+        const float v = acc[m][j][r];
+        if (EPI == EPI_ROPE) {
+          const float pv = __shfl_xor(v, 1);  // the pair partner: logical rows 2i, 2i + 1
+          if (t < a.M && n < a.N) {
+            const bool qk = n < a.ra.dim + a.ra.kvw;
+            const size_t ci = (size_t)a.ra.pos[t] * a.ra.half + rope_pair_index(n, a.ra.hshift);
+            rope_append(a.ra, a.y + (size_t)t * a.ldy, t, n, v, pv, qk ? a.ra.rope_cs[ci] : 0.f,
+                        qk ? a.ra.rope_sn[ci] : 0.f);
+          }
+        } else if (t < a.M && n < a.N) {
+          float *y = a.y + (size_t)t * a.ldy + n;
+          *y = EPI == EPI_RESID ? a.res[(size_t)t * a.ldres + n] + v : v;
+        }
       }
     }
+}
+
+// Sum of the slices' partial sums in slice order, then the epilogue; thread = a pair of outputs (n, n+1)
+// of token row blockIdx.y.  ROPE needs both numbers of a pair; SWIGLU writes the next operands.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void k_rows_reduce(GemmArgs a, int S) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  const int t = blockIdx.y;
+  const int n = 2 * (blockIdx.x * kThreads + threadIdx.x);
+  if (n >= a.N) return;
+  const int nout = SW ? 2 * a.N : a.N;
+  const float *pp = a.part + (size_t)t * nout + n;
+  const size_t sstride = (size_t)a.M * nout;
+  float v0 = 0.f, v1 = 0.f, u0 = 0.f, u1 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float2 p = *reinterpret_cast<const float2 *>(pp + s * sstride);
+    v0 += p.x;
+    v1 += p.y;
+    if (SW) {
+      const float2 q = *reinterpret_cast<const float2 *>(pp + s * sstride + a.N);
+      u0 += q.x;
+      u1 += q.y;
+    }
+  }
+  if (SW) {
+    const float m0 = (v0 / (1.0f + expf(-v0))) * u0, m1 = (v1 / (1.0f + expf(-v1))) * u1;
+    uint32_t h, l;
+    split_bf16x2(m0, m1, h, l);
+    *reinterpret_cast<uint32_t *>(a.ohi + (size_t)t * a.ldo + n) = h;
+    *reinterpret_cast<uint32_t *>(a.olo + (size_t)t * a.ldo + n) = l;
+  } else if (EPI == EPI_ROPE) {
+    float *y = a.y + (size_t)t * a.ldy;
+    float c = 0.f, s = 0.f;
+    if (n < a.ra.dim + a.ra.kvw) {
+      const size_t ci = (size_t)a.ra.pos[t] * a.ra.half + rope_pair_index(n, a.ra.hshift);
+      c = a.ra.rope_cs[ci];
+      s = a.ra.rope_sn[ci];
+    }
+    rope_append(a.ra, y, t, n, v0, v1, c, s);
+    rope_append(a.ra, y, t, n + 1, v1, v0, c, s);
+  } else {
+    float *y = a.y + (size_t)t * a.ldy + n;
+    if (EPI == EPI_RESID) {
+      const float *r = a.res + (size_t)t * a.ldres + n;
+      v0 += r[0];
+      v1 += r[1];
+    }
+    y[0] = v0;
+    y[1] = v1;
   }
 }
 
-int gemm_skinny_supported(int wdtype, int K, int M) {
-  return wdtype == LLAMA_BF16 && K % 32 == 0 && M >= 1 && M <= kMaxBatch;
+// x[t] = x[t] + sum of the slices' partials (slice order), stored; then the next product's operands
+// g * (x * (1 / sqrt(sum x^2 / N + eps))) as bf16 hi + lo (main.bend rmsnorm).  Block = token row t.
+template <typename GT>
+__global__ __launch_bounds__(kThreads) void k_rows_reduce_norm(RowsNormArgs a) {
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float *pp = a.part + (size_t)t * a.N;
+  const size_t sstride = (size_t)a.M * a.N;
+  float *x = a.x + (size_t)t * a.ldx;
+  float ss = 0.f;
+  for (int n = 2 * tid; n < a.N; n += 2 * kThreads) {
+    float2 v = *reinterpret_cast<const float2 *>(x + n);  // the residual stream
+    float s0 = 0.f, s1 = 0.f;
+    for (int s = 0; s < a.S; ++s) {
+      const float2 p = *reinterpret_cast<const float2 *>(pp + s * sstride + n);
+      s0 += p.x;
+      s1 += p.y;
+    }
+    v.x += s0;
+    v.y += s1;
+    *reinterpret_cast<float2 *>(x + n) = v;
+    ss += v.x * v.x + v.y * v.y;
+  }
+  __shared__ float ss_w[4];
+  ss = wave_sum(ss);
+  if (lane == 0) ss_w[wave] = ss;
+  lds_barrier();
+  const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
+  const float r = 1.0f / sqrtf(tot / (float)a.N + a.eps);
+  const GT *g = reinterpret_cast<const GT *>(a.gain);
+  for (int n = 2 * tid; n < a.N; n += 2 * kThreads) {
+    const float2 v = *reinterpret_cast<const float2 *>(x + n);
+    uint32_t h, l;
+    split_bf16x2(load_scalar<GT>(g, n) * (v.x * r), load_scalar<GT>(g, n + 1) * (v.y * r), h, l);
+    *reinterpret_cast<uint32_t *>(a.xhi + (size_t)t * a.ldo + n) = h;
+    *reinterpret_cast<uint32_t *>(a.xlo + (size_t)t * a.ldo + n) = l;
+  }
+}
+
+int gemm_rows_supported(int wdtype, int K, int M) {
+  return wdtype == LLAMA_BF16 && K % kRT == 0 && M >= 1 && M <= kMaxBatch;
+}
+
+int gemm_rows_blocks(int N, bool swiglu) {
+  const int rows = swiglu ? kRowsOut / 2 : kRowsOut;
+  return (N + rows - 1) / rows;
+}
+
+// K slices for ~target blocks in all (never an empty slice)
+int gemm_rows_slices(int N, int K, bool swiglu, int target) {
+  const int nb = gemm_rows_blocks(N, swiglu);
+  const int ntile = K / kRT;
+  int s = (target + nb - 1) / nb;
+  if (s < 1) s = 1;
+  if (s > ntile) s = ntile;
+  const int per = (ntile + s - 1) / s;
+  return (ntile + per - 1) / per;
 }
 
 hipError_t launch_split(int gdtype, bool norm, const SplitArgs &a, int mpad, hipStream_t s) {
@@ -186,30 +417,63 @@ hipError_t launch_split(int gdtype, bool norm, const SplitArgs &a, int mpad, hip
   return hipGetLastError();
 }
 
-template <int MT>
-static hipError_t launch_mt(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last) {
-  const dim3 g((a.N + 15) / 16);
+template <int MT, bool PART>
+static void launch_rows_mt(GemvEpi epi, const GemmArgs &a, dim3 g, hipStream_t s, bool first, bool last) {
   switch (epi) {
-    case EPI_STORE: launch(k_gemm_skinny<MT, EPI_STORE>, g, dim3(kThreads), s, false, last, a); break;
-    case EPI_RESID: launch(k_gemm_skinny<MT, EPI_RESID>, g, dim3(kThreads), s, false, last, a); break;
-    case EPI_SWIGLU: launch(k_gemm_skinny<MT, EPI_SWIGLU>, g, dim3(kThreads), s, false, last, a); break;
-    case EPI_ARGMAX: launch(k_gemm_skinny<MT, EPI_ARGMAX>, g, dim3(kThreads), s, false, last, a); break;
-    case EPI_ROPE: launch(k_gemm_skinny<MT, EPI_ROPE>, g, dim3(kThreads), s, false, last, a); break;
+    case EPI_STORE: launch(k_gemm_rows<MT, EPI_STORE, PART>, g, dim3(kThreads), s, first, last, a); break;
+    case EPI_RESID: launch(k_gemm_rows<MT, EPI_RESID, PART>, g, dim3(kThreads), s, first, last, a); break;
+    case EPI_SWIGLU: launch(k_gemm_rows<MT, EPI_SWIGLU, PART>, g, dim3(kThreads), s, first, last, a); break;
+    case EPI_ROPE: launch(k_gemm_rows<MT, EPI_ROPE, PART>, g, dim3(kThreads), s, first, last, a); break;
+    case EPI_ARGMAX:
+      if constexpr (!PART) launch(k_gemm_rows<MT, EPI_ARGMAX, false>, g, dim3(kThreads), s, first, last, a);
+      break;
+  }
+}
+
+template <int MT>
+static hipError_t launch_rows(GemvEpi epi, const GemmArgs &a, int S, bool part, hipStream_t s, bool first, bool last) {
+  const dim3 g(gemm_rows_blocks(a.N, epi == EPI_SWIGLU), S);
+  if (part)
+    launch_rows_mt<MT, true>(epi, a, g, s, first, last);
+  else
+    launch_rows_mt<MT, false>(epi, a, g, s, first, last);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rows(GemvEpi epi, GemmArgs a, int S, hipStream_t s, bool first, bool last) {
+  if (a.K % kRT != 0 || a.M < 1 || a.M > kMaxBatch || S < 1) return hipErrorInvalidValue;
+  if (S > 1 && epi == EPI_ARGMAX) return hipErrorInvalidValue;
+  const int ntile = a.K / kRT;
+  a.tiles_per_slice = (ntile + S - 1) / S;
+  if ((S - 1) * a.tiles_per_slice >= ntile) return hipErrorInvalidValue;  // an empty slice
+  // RESID always leaves partial sums (slice 0 alone when S = 1): k_rows_reduce_norm adds them to the
+  // residual stream and forms the next product's operands
+  const bool part = S > 1 || epi == EPI_RESID;
+  const bool reduce = S > 1 && epi != EPI_RESID;
+  hipError_t e = hipErrorInvalidValue;
+  switch ((a.M + 15) / 16) {
+    case 1: e = launch_rows<1>(epi, a, S, part, s, first, last && !reduce); break;
+    case 2: e = launch_rows<2>(epi, a, S, part, s, first, last && !reduce); break;
+    case 3: e = launch_rows<3>(epi, a, S, part, s, first, last && !reduce); break;
+    case 4: e = launch_rows<4>(epi, a, S, part, s, first, last && !reduce); break;
+  }
+  if (e != hipSuccess || !reduce) return e;
+  const dim3 g((a.N / 2 + kThreads - 1) / kThreads, a.M);
+  switch (epi) {
+    case EPI_STORE: launch(k_rows_reduce<EPI_STORE>, g, dim3(kThreads), s, false, last, a, S); break;
+    case EPI_SWIGLU: launch(k_rows_reduce<EPI_SWIGLU>, g, dim3(kThreads), s, false, last, a, S); break;
+    case EPI_ROPE: launch(k_rows_reduce<EPI_ROPE>, g, dim3(kThreads), s, false, last, a, S); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_skinny(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last) {
-  const int mt = (a.M + 15) / 16;
-  switch (mt) {
-    case 1: return launch_mt<1>(epi, a, s, last);
-    case 2: return launch_mt<2>(epi, a, s, last);
-    case 3: return launch_mt<3>(epi, a, s, last);
-    case 4: return launch_mt<4>(epi, a, s, last);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_rows_reduce_norm(int gdtype, const RowsNormArgs &a, hipStream_t s, bool last) {
+  if (gdtype == LLAMA_BF16)
+    launch(k_rows_reduce_norm<bf16_t>, dim3(a.M), dim3(kThreads), s, false, last, a);
+  else
+    launch(k_rows_reduce_norm<float>, dim3(a.M), dim3(kThreads), s, false, last, a);
+  return hipGetLastError();
 }
-
-int gemm_skinny_blocks(int N) { return (N + 15) / 16; }
 
 }  // namespace lm

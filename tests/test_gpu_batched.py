@@ -1,8 +1,9 @@
 """GPU parity of batched decode rows against the CPU oracle.
 
-Several cache rows each take one token at their own position in one step; with bf16 weights the
-projections run as one matrix-core product over all rows (operands split into bf16 hi + lo), so this
-covers tile counts 1..4 of 16 token rows and ragged last tiles.  Every row is compared with an oracle
+Several cache rows each take one token at their own position in one step; with bf16 weights (widths a
+multiple of 128) the projections run as matrix-core products over all rows (operands split into bf16
+hi + lo), so this covers tile counts 1..4 of 16 token rows and ragged last tiles; narrower models take
+the per-row path.  Every row is compared with an oracle
 decode of that row alone: logits within max|d| 2e-2, argmax equal outside near-ties, the appended K/V
 slot within bf16 rounding.  Two teacher-forced steps, so the second reads what the first appended.
 """
@@ -27,10 +28,12 @@ def _cfg(name, layers):
 
 CASES = [
     # model, layers, rows, max_seq
-    ("smollm2_135m_bf16", 3, 64, 512),   # the largest batch: four full 16-row tiles
-    ("smollm2_135m_bf16", 3, 17, 512),   # two tiles, the second holding one row
-    ("llama31_8b", 2, 2, 256),           # one ragged tile at the 8B width
-    ("llama31_8b", 2, 33, 4096),         # three tiles at the 8B width, lengths across several chunks
+    ("smollm2_135m_bf16", 3, 64, 512),   # widths not a multiple of 128: the per-row path, largest batch
+    ("smollm2_135m_bf16", 3, 17, 512),
+    ("llama31_8b", 2, 2, 256),           # matrix-core rows: one ragged 16-row tile
+    ("llama31_8b", 2, 20, 512),          # two tiles, the second ragged
+    ("llama31_8b", 2, 33, 4096),         # three tiles, lengths across several attention chunks
+    ("llama31_8b", 2, 64, 512),          # the largest batch: four full tiles
 ]
 
 
