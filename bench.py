@@ -293,6 +293,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 4096-position prefill (for profiling its kernels)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="time only the batch-32 long-context decode (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
@@ -313,10 +315,14 @@ def main():
     p0 = cfg.kv_fill
     steps = max(1, min(args.steps, cfg.max_seq - p0))
     want_cpu = not args.no_cpu_baseline
-    if args.prefill_only:
+    if args.prefill_only or args.batched_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
         c5 = configs.LLAMA31_8B_LONG
-        print(json.dumps({"prefill": time_prefill(c5, lm, synth, dec.w, 2, 1)}), flush=True)
+        if args.prefill_only:
+            print(json.dumps({"prefill": time_prefill(c5, lm, synth, dec.w, 2, 1)}), flush=True)
+        else:
+            print(json.dumps({"batched": time_batched(c5, lm, synth, dec.w, min(args.steps, c5.decode_steps),
+                                                      args.warmup)}), flush=True)
         return
     dec, w, kc, vc = build_model(cfg, lm, synth, cfg.max_seq, p0, keep_host=want_cpu)
     first = int(synth.tokens(cfg, "bench/first", 1)[0])

@@ -13,11 +13,13 @@
 // k_gemm_rows: block (bx, s) owns 128 consecutive outputs (wave w: outputs 32w .. +32 as two 16-row
 // tiles; SwiGLU: 64 outputs, wave w's tiles are the gate and the up rows of outputs 16w .. +16) over the
 // s-th slice of K.  X tiles of 128 columns are staged in LDS once for the 4 waves (double buffered); each
-// wave keeps the next tile's weight loads in flight while it multiplies the current one.  With one slice
+// wave keeps the weight loads of the next two tiles in flight while it multiplies the current one.  The
+// weights are loaded in 256-byte runs of a row (the MFMA layout would give 64-byte pieces of 16 rows per
+// load, which streams from HBM markedly slower) and rearranged through the wave's own LDS tile.  With one slice
 // the epilogue runs in the kernel; with several, each slice writes its partial sums and a reduce kernel
 // adds them in slice order (deterministic) and runs the epilogue.  The number of slices is chosen so
-// the launch has ~512 blocks: at these sizes every CU must see all of X, so X re-reads, not weights,
-// decide how many output rows a block should own.
+// the launch has at most 512 blocks (two resident per CU): at these sizes every CU must see all of X, so
+// X re-reads, not weights, decide how many output rows a block should own.
 //
 // Epilogues: STORE, RESID (y = res + XW^T), SWIGLU (silu(gate) * up, written straight as the next
 // product's bf16 hi/lo operands), ROPE (RoPE + cache append, as the GEMV), ARGMAX (LM head: logits and
@@ -87,11 +89,12 @@ __device__ __forceinline__ const bf16_t *weight_row(const GemmArgs &a, int n, in
 }
 
 template <int MT, int EPI, bool PART>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, MT <= 2 ? 2 : 1) void k_gemm_rows(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
   constexpr int ROWS = SW ? kRowsOut / 2 : kRowsOut;
   constexpr int XCH = MT * 16 * kRT / 8 / kThreads;  // 16-byte chunks of one X array per thread per tile (= MT)
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][2][MT * 16 * kLdt];  // [buffer][hi, lo]
+  __shared__ __attribute__((aligned(16))) bf16_t ws[4][32 * kLdt];          // each wave's weight tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q8 = (lane >> 4) * 8;
   const int nb = blockIdx.x * ROWS;
@@ -99,12 +102,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
   const int t0 = blockIdx.y * a.tiles_per_slice;
   const int nt = min(a.tiles_per_slice, ntile_all - t0);  // >= 1 (slices are never empty)
 
-  // this lane's two weight rows (tile j), at its 16-byte piece of the first K step of the slice
-  const bf16_t *wp[2];
+  // The wave's 32 weight rows (SwiGLU: rows 0..15 gate, 16..31 up) are read in runs of 256 bytes: load
+  // i brings rows 4i .. 4i+3, lane l the 16 bytes at 8 (l%16) of row 4i + l/16.  They reach the MFMA
+  // layout (lane l: row l%16 of a 16-row tile) through the wave's own LDS tile.
+  const bf16_t *wrow[8];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = min(SW ? nb + 16 * wave + l16 : nb + 32 * wave + 16 * j + l16, a.N - 1);
-    wp[j] = weight_row<EPI>(a, n, j) + (size_t)t0 * kRT + q8;
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int n = min(SW ? nb + 16 * wave + (r & 15) : nb + 32 * wave + r, a.N - 1);
+    wrow[i] = weight_row<EPI>(a, n, SW ? r >> 4 : 0) + (size_t)t0 * kRT + l16 * 8;
   }
   // X staging: chunk c = tid + 256 i is row c / 16, columns 8 (c % 16) .. +8 of the tile
   const bf16_t *xg[2][XCH];
@@ -116,9 +122,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
     xg[0][i] = a.xhi + (size_t)r * a.ldx + (size_t)t0 * kRT + cc;
     xg[1][i] = a.xlo + (size_t)r * a.ldx + (size_t)t0 * kRT + cc;
   }
+  bf16_t *wl = ws[wave];
 
   u32x4 xr[2][XCH];
-  u32x4 w0[4][2], w1[4][2];
+  u32x4 w0[8], w1[8], w2[8];
   auto load_x = [&](int t) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -131,20 +138,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4 *>(&xs[buf][h][xo[i]]) = xr[h][i];
   };
-  auto load_w = [&](u32x4 (&w)[4][2], int t) {
+  auto load_w = [&](u32x4 (&w)[8], int t) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) w[ks][j] = load_stream16(wp[j] + (size_t)t * kRT + ks * 32);
+    for (int i = 0; i < 8; ++i) w[i] = load_stream16(wrow[i] + (size_t)t * kRT);
   };
   f32x4 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, const u32x4 (&w)[4][2]) {
+  auto compute = [&](int buf, const u32x4 (&w)[8]) {
+    // the weight tile into the wave's LDS rows (LDS operations of a wave complete in order, so the
+    // reads below see these writes and the writes of the next tile follow these reads)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(&wl[(4 * i + (lane >> 4)) * kLdt + l16 * 8]) = w[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      u32x4 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const u32x4 *>(&wl[(16 * j + l16) * kLdt + ks * 32 + q8]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int off = (m * 16 + l16) * kLdt + ks * 32 + q8;
@@ -152,37 +167,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
         const u32x4 al = *reinterpret_cast<const u32x4 *>(&xs[buf][1][off]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          acc[m][j] = mfma16(ah, w[ks][j], acc[m][j]);
-          acc[m][j] = mfma16(al, w[ks][j], acc[m][j]);
+          acc[m][j] = mfma16(ah, b[j], acc[m][j]);
+          acc[m][j] = mfma16(al, b[j], acc[m][j]);
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   };
-
-  // tiles in pairs (t even: buffer 0 and w0, t odd: buffer 1 and w1); the next tile's X and weight loads
-  // are in flight while a tile is multiplied, and LDS barriers leave them in flight
-  load_x(0);
-  load_w(w0, 0);
-  stash_x(0);
-  lds_barrier();
-  for (int t = 0; t < nt; t += 2) {
+  // one tile: the X tile after it (LDS, distance 1) and the weights two tiles ahead (registers, a ring of
+  // three) are requested first, X before weights so that waiting for X leaves the weights in flight; LDS
+  // barriers do not wait for global loads
+  auto step = [&](int t, const u32x4 (&wcur)[8], u32x4 (&wahead)[8]) {
+    if (t + 1 < nt) load_x(t + 1);
+    if (t + 2 < nt) load_w(wahead, t + 2);
+    compute(t & 1, wcur);
     if (t + 1 < nt) {
-      load_x(t + 1);
-      load_w(w1, t + 1);
-    }
-    compute(0, w0);
-    if (t + 1 >= nt) break;
-    stash_x(1);
-    lds_barrier();
-    if (t + 2 < nt) {
-      load_x(t + 2);
-      load_w(w0, t + 2);
-    }
-    compute(1, w1);
-    if (t + 2 < nt) {
-      stash_x(0);
+      stash_x((t + 1) & 1);
       lds_barrier();
     }
+  };
+  load_x(0);
+  load_w(w0, 0);
+  if (nt > 1) load_w(w1, 1);
+  stash_x(0);
+  lds_barrier();
+  for (int t = 0; t < nt; t += 3) {
+    step(t, w0, w2);
+    if (t + 1 >= nt) break;
+    step(t + 1, w1, w0);
+    if (t + 2 >= nt) break;
+    step(t + 2, w2, w1);
   }
 
   // lane holds C[token 4(lane/16) + r][output l16] of tile (m, j)
@@ -347,40 +363,53 @@ __global__ __launch_bounds__(kThreads) void k_rows_reduce(GemmArgs a, int S) {
 }
 
 // x[t] = x[t] + sum of the slices' partials (slice order), stored; then the next product's operands
-// g * (x * (1 / sqrt(sum x^2 / N + eps))) as bf16 hi + lo (main.bend rmsnorm).  Block = token row t.
+// g * (x * (1 / sqrt(sum x^2 / N + eps))) as bf16 hi + lo (main.bend rmsnorm).  Block = token row t, 1024
+// threads with 4 consecutive numbers each, every slice's partial loaded before any is added.
+constexpr int kNormThreads = 1024;
 template <typename GT>
-__global__ __launch_bounds__(kThreads) void k_rows_reduce_norm(RowsNormArgs a) {
+__global__ __launch_bounds__(kNormThreads) void k_rows_reduce_norm(RowsNormArgs a) {
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *pp = a.part + (size_t)t * a.N;
   const size_t sstride = (size_t)a.M * a.N;
   float *x = a.x + (size_t)t * a.ldx;
   float ss = 0.f;
-  for (int n = 2 * tid; n < a.N; n += 2 * kThreads) {
-    float2 v = *reinterpret_cast<const float2 *>(x + n);  // the residual stream
-    float s0 = 0.f, s1 = 0.f;
-    for (int s = 0; s < a.S; ++s) {
-      const float2 p = *reinterpret_cast<const float2 *>(pp + s * sstride + n);
-      s0 += p.x;
-      s1 += p.y;
+  for (int n = 4 * tid; n < a.N; n += 4 * kNormThreads) {
+    const float4 r = *reinterpret_cast<const float4 *>(x + n);  // the residual stream
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+      float4 p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        p[k] = *reinterpret_cast<const float4 *>(pp + (size_t)min(s0 + k, a.S - 1) * sstride + n);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.S) {
+          acc.x += p[k].x;
+          acc.y += p[k].y;
+          acc.z += p[k].z;
+          acc.w += p[k].w;
+        }
     }
-    v.x += s0;
-    v.y += s1;
-    *reinterpret_cast<float2 *>(x + n) = v;
-    ss += v.x * v.x + v.y * v.y;
+    const float4 v = make_float4(r.x + acc.x, r.y + acc.y, r.z + acc.z, r.w + acc.w);
+    *reinterpret_cast<float4 *>(x + n) = v;
+    ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
   }
-  __shared__ float ss_w[4];
+  __shared__ float ss_w[kNormThreads / 64];
   ss = wave_sum(ss);
   if (lane == 0) ss_w[wave] = ss;
   lds_barrier();
-  const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += ss_w[w];
   const float r = 1.0f / sqrtf(tot / (float)a.N + a.eps);
   const GT *g = reinterpret_cast<const GT *>(a.gain);
-  for (int n = 2 * tid; n < a.N; n += 2 * kThreads) {
-    const float2 v = *reinterpret_cast<const float2 *>(x + n);
-    uint32_t h, l;
-    split_bf16x2(load_scalar<GT>(g, n) * (v.x * r), load_scalar<GT>(g, n + 1) * (v.y * r), h, l);
-    *reinterpret_cast<uint32_t *>(a.xhi + (size_t)t * a.ldo + n) = h;
-    *reinterpret_cast<uint32_t *>(a.xlo + (size_t)t * a.ldo + n) = l;
+  for (int n = 4 * tid; n < a.N; n += 4 * kNormThreads) {
+    const float4 v = *reinterpret_cast<const float4 *>(x + n);  // this thread's own store above
+    uint32_t h0, l0, h1, l1;
+    split_bf16x2(load_scalar<GT>(g, n) * (v.x * r), load_scalar<GT>(g, n + 1) * (v.y * r), h0, l0);
+    split_bf16x2(load_scalar<GT>(g, n + 2) * (v.z * r), load_scalar<GT>(g, n + 3) * (v.w * r), h1, l1);
+    *reinterpret_cast<uint2 *>(a.xhi + (size_t)t * a.ldo + n) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2 *>(a.xlo + (size_t)t * a.ldo + n) = make_uint2(l0, l1);
   }
 }
 
@@ -393,11 +422,12 @@ int gemm_rows_blocks(int N, bool swiglu) {
   return (N + rows - 1) / rows;
 }
 
-// K slices for ~target blocks in all (never an empty slice)
+// K slices for at most `target` blocks in all (one round of resident blocks: a second, partial round
+// would cost as much as the first), never an empty slice
 int gemm_rows_slices(int N, int K, bool swiglu, int target) {
   const int nb = gemm_rows_blocks(N, swiglu);
   const int ntile = K / kRT;
-  int s = (target + nb - 1) / nb;
+  int s = target / nb;
   if (s < 1) s = 1;
   if (s > ntile) s = ntile;
   const int per = (ntile + s - 1) / s;
@@ -469,10 +499,11 @@ hipError_t launch_gemm_rows(GemvEpi epi, GemmArgs a, int S, hipStream_t s, bool 
 }
 
 hipError_t launch_rows_reduce_norm(int gdtype, const RowsNormArgs &a, hipStream_t s, bool last) {
+  if (a.N % 4 != 0) return hipErrorInvalidValue;
   if (gdtype == LLAMA_BF16)
-    launch(k_rows_reduce_norm<bf16_t>, dim3(a.M), dim3(kThreads), s, false, last, a);
+    launch(k_rows_reduce_norm<bf16_t>, dim3(a.M), dim3(kNormThreads), s, false, last, a);
   else
-    launch(k_rows_reduce_norm<float>, dim3(a.M), dim3(kThreads), s, false, last, a);
+    launch(k_rows_reduce_norm<float>, dim3(a.M), dim3(kNormThreads), s, false, last, a);
   return hipGetLastError();
 }
 
