@@ -230,8 +230,8 @@ struct FlashShape {
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
   using F = FlashShape<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t s_k[kKT * F::KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t s_vt[D * F::VROW];
+  __shared__ __attribute__((aligned(16))) bf16_t s_k[2][kKT * F::KROW];   // double buffered
+  __shared__ __attribute__((aligned(16))) bf16_t s_vt[2][D * F::VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqt = gridDim.x;
   const int qt = nqt - 1 - (int)blockIdx.x;  // the longest tiles first
@@ -272,31 +272,55 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
   const float sc = a.scale * 1.4426950408889634f;
 
   const int ntiles = last_pos / kKT + 1;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int k0 = tile * kKT;
-    // stage K (row-major) and V (transposed) of positions k0 .. k0+63 (past last_pos: clamped, masked)
-    constexpr int KCH = kKT * D / 8;  // 16-byte chunks of the K tile
-    for (int c = tid; c < KCH; c += kThreads) {
-      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-      const int p = min(k0 + r, last_pos);
-      *reinterpret_cast<u32x4 *>(&s_k[r * F::KROW + cc]) = load16(Kh + (size_t)p * D + cc);
-    }
-    // V: thread takes 4 consecutive keys x 8 consecutive d and writes 8 rows of 4 keys of V^T
-    constexpr int VCH = (kKT / 4) * (D / 8);
-    for (int c = tid; c < VCH; c += kThreads) {
-      const int dc = c % (D / 8), kq = c / (D / 8);
-      u32x4 v[4];
+  // K (row-major) and V (transposed) of positions k0 .. k0+63 (past last_pos: clamped, masked): the next
+  // tile's loads are in flight in registers while the current tile is multiplied, then written to the
+  // other LDS buffer; one barrier per tile
+  constexpr int KCH = kKT * D / 8;            // 16-byte chunks of the K tile
+  constexpr int KPT = (KCH + kThreads - 1) / kThreads;
+  constexpr int VCH = (kKT / 4) * (D / 8);    // (4 keys x 8 numbers) pieces of the V tile
+  u32x4 kreg[KPT], vreg[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load16(Vh + (size_t)min(k0 + 4 * kq + u, last_pos) * D + dc * 8);
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kThreads;
+      if (KCH % kThreads == 0 || c < KCH) {
+        const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
+        kreg[i] = load16(Kh + (size_t)min(k0 + r, last_pos) * D + cc);
+      }
+    }
+    if (tid < VCH) {
+      const int dc = tid % (D / 8), kq = tid / (D / 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vreg[u] = load16(Vh + (size_t)min(k0 + 4 * kq + u, last_pos) * D + dc * 8);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kThreads;
+      if (KCH % kThreads == 0 || c < KCH) {
+        const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&s_k[buf][r * F::KROW + cc]) = kreg[i];
+      }
+    }
+    // V: this thread's 4 consecutive keys x 8 consecutive numbers go to 8 rows of 4 keys of V^T
+    if (tid < VCH) {
+      const int dc = tid % (D / 8), kq = tid / (D / 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1, sh = (e & 1) * 16;
-        const uint32_t b0 = (v[0][w] >> sh) & 0xffffu, b1 = (v[1][w] >> sh) & 0xffffu;
-        const uint32_t b2 = (v[2][w] >> sh) & 0xffffu, b3 = (v[3][w] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2 *>(&s_vt[(dc * 8 + e) * F::VROW + 4 * kq]) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+        const uint32_t b0 = (vreg[0][w] >> sh) & 0xffffu, b1 = (vreg[1][w] >> sh) & 0xffffu;
+        const uint32_t b2 = (vreg[2][w] >> sh) & 0xffffu, b3 = (vreg[3][w] >> sh) & 0xffffu;
+        *reinterpret_cast<u32x2 *>(&s_vt[buf][(dc * 8 + e) * F::VROW + 4 * kq]) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
       }
     }
-    __syncthreads();
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int k0 = tile * kKT, buf = tile & 1;
+    if (tile + 1 < ntiles) fetch(k0 + kKT);
 
     if (active) {
       // scores S^T for keys k0 + 32 mt + (8(r/4) + 4 hsel + r%4), query q_i
@@ -307,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < F::KS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4 *>(&s_k[(mt * 32 + l32) * F::KROW + ks * 16 + hsel * 8]);
+          const u32x4 kf = *reinterpret_cast<const u32x4 *>(&s_k[buf][(mt * 32 + l32) * F::KROW + ks * 16 + hsel * 8]);
           s[mt] = mfma32(kf, qh[ks], s[mt]);
           s[mt] = mfma32(kf, ql[ks], s[mt]);
         }
@@ -353,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
         const int kb = kk * 16 + 4 * hsel;
 #pragma unroll
         for (int t = 0; t < F::DT; ++t) {
-          const bf16_t *vr = &s_vt[(t * 32 + l32) * F::VROW + kb];
+          const bf16_t *vr = &s_vt[buf][(t * 32 + l32) * F::VROW + kb];
           const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(vr);
           const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(vr + 8);
           const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
@@ -362,6 +386,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(PrefillArgs a) {
         }
       }
     }
+    // the other buffer was last read in the previous tile, before the previous barrier
+    if (tile + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
   }
 
