@@ -26,14 +26,18 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ------------------------------------------------------------------------ tiled product ----
-// Block: 128 token rows x 128 weight rows (SwiGLU: 64 gate rows + the same 64 up rows), K in steps of
-// 32 through double-buffered LDS.  Wave (wm, wn) owns 64 x 64 of the block as 2 x 2 tiles of 32 x 32.
-constexpr int kTM = 128, kTN = 128, kTK = 32;
+// Block: 128 token rows x 256 weight rows (SwiGLU: 128 gate rows + the same 128 up rows), K in steps of
+// 32 through double-buffered LDS.  Wave (wm, wn) owns 64 x 128 of the block as 2 x 4 tiles of 32 x 32, so
+// each k step reads 2 (x hi, lo) A fragments and 4 B fragments from LDS for 16 MFMAs: the LDS traffic per
+// MFMA (reads + the staging writes) stays well under what the LDS delivers while the matrix cores run.
+constexpr int kTM = 128, kTN = 256, kTK = 32;
 constexpr int kRowA = kTK + 8;  // LDS row of a tile: 40 bf16 = 80 bytes (16-byte reads of 16 rows hit distinct banks)
 
 template <int EPI>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_tiled(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int AC = 2 * kTM * (kTK / 8) / kThreads;  // 16-byte chunks of A (hi and lo) per thread per stage
+  constexpr int BC = kTN * (kTK / 8) / kThreads;      // of B
   __shared__ __attribute__((aligned(16))) bf16_t s_a[2][2][kTM * kRowA];  // [buffer][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t s_b[2][kTN * kRowA];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -41,51 +45,51 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
   const int m0 = blockIdx.y * kTM;
   const int n0 = blockIdx.x * (SW ? kTN / 2 : kTN);
 
-  // staging: 16-byte chunk c = tid + 256 i of a 128 x 32 tile is row c / 4, columns 8 (c % 4) .. +8
-  const bf16_t *ga_hi[2], *ga_lo[2], *gb[2];
-  int lds_off[2];
+  // staging: 16-byte chunk c of a tile (rows of 32 columns) is row c / 4, columns 8 (c % 4) .. +8; A chunks
+  // c < 512 are hi, the rest lo
+  const bf16_t *ga[AC], *gb[BC];
+  int ao[AC], bo[BC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + kThreads * i, h = c / (kTM * 4), cr = c % (kTM * 4), r = cr >> 2, cc = (cr & 3) * 8;
+    ao[i] = h * kTM * kRowA + r * kRowA + cc;
+    ga[i] = (h ? a.xlo : a.xhi) + (size_t)(m0 + r) * a.ldx + cc;
+  }
+#pragma unroll
+  for (int i = 0; i < BC; ++i) {
     const int c = tid + kThreads * i, r = c >> 2, cc = (c & 3) * 8;
-    lds_off[i] = r * kRowA + cc;
-    ga_hi[i] = a.xhi + (size_t)(m0 + r) * a.ldx + cc;
-    ga_lo[i] = a.xlo + (size_t)(m0 + r) * a.ldx + cc;
+    bo[i] = r * kRowA + cc;
     const bf16_t *base;
-    int n;
     if (SW) {
-      n = min(n0 + (r & 63), a.N - 1);
-      base = reinterpret_cast<const bf16_t *>(r < 64 ? a.w[0] : a.w[1]) + (size_t)n * a.K;
+      const int n = min(n0 + (r & 127), a.N - 1);
+      base = reinterpret_cast<const bf16_t *>(r < 128 ? a.w[0] : a.w[1]) + (size_t)n * a.K;
     } else {
-      n = min(n0 + r, a.N - 1);
+      const int n = min(n0 + r, a.N - 1);
       const int seg = n >= a.rs[2] ? 2 : (n >= a.rs[1] ? 1 : 0);
       base = reinterpret_cast<const bf16_t *>(a.w[seg]) + (size_t)(n - a.rs[seg]) * a.K;
     }
     gb[i] = base + cc;
   }
 
-  u32x4 rh[2], rl[2], rb[2];
+  u32x4 ra[AC], rb[BC];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rh[i] = load16(ga_hi[i] + k0);
-      rl[i] = load16(ga_lo[i] + k0);
-      rb[i] = load16(gb[i] + k0);
-    }
+    for (int i = 0; i < AC; ++i) ra[i] = load16(ga[i] + k0);
+#pragma unroll
+    for (int i = 0; i < BC; ++i) rb[i] = load16(gb[i] + k0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4 *>(&s_a[buf][0][lds_off[i]]) = rh[i];
-      *reinterpret_cast<u32x4 *>(&s_a[buf][1][lds_off[i]]) = rl[i];
-      *reinterpret_cast<u32x4 *>(&s_b[buf][lds_off[i]]) = rb[i];
-    }
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<u32x4 *>(&s_a[buf][0][ao[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BC; ++i) *reinterpret_cast<u32x4 *>(&s_b[buf][bo[i]]) = rb[i];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
     for (int kk = 0; kk < kTK / 16; ++kk) {
       const int ko = kk * 16 + hsel;
-      u32x4 ah[2], al[2], b[2];
+      u32x4 ah[2], al[2], b[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm * 64 + i * 32 + l32;
@@ -108,14 +112,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
         al[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][1][row * kRowA + ko]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int brow = SW ? (wn * 32 + j * 64 + l32) : (wn * 64 + j * 32 + l32);
+      for (int j = 0; j < 4; ++j) {
+        // SwiGLU: tiles 0, 1 are gate rows, 2, 3 the up rows of the same outputs
+        const int brow = SW ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32) : (wn * 128 + j * 32 + l32);
         b[j] = *reinterpret_cast<const u32x4 *>(&s_b[buf][brow * kRowA + ko]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
           acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
           acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
         }
@@ -132,15 +137,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
       const int t = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (t >= a.M) continue;
       if (SW) {
-        const int n = n0 + wn * 32 + l32;
-        if (n < a.N) {
-          const float gt = acc[i][0][r], up = acc[i][1][r];
-          a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int n = n0 + wn * 64 + jj * 32 + l32;
+          if (n < a.N) {
+            const float gt = acc[i][jj][r], up = acc[i][2 + jj][r];
+            a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+          }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 128 + j * 32 + l32;
           if (n >= a.N) continue;
           float *y = a.y + (size_t)t * a.ldy + n;
           if (EPI == EPI_RESID)
