@@ -87,7 +87,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 
   // ---- the input slice of this thread: chunks j*256 + tid
   float xr[KCH][E];
-  float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < KCH; ++j) {
     const int ci = j * kThreads + tid;
@@ -104,45 +103,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) xr[j][e] = 0.f;
     }
-    if (NORM) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) ss += xr[j][e] * xr[j][e];
-    }
   }
+  // the norm gains of the slice (also independent of everything else)
+  u32x4 gr[NORM ? KCH : 1];
   if (NORM) {
-    // RMSNorm prologue: g * (x * (1 / sqrt(sum(x^2) / K + eps)))
-    ss = wave_sum(ss);
-    if (lane == 0) ss_w[wave] = ss;
-    lds_barrier();
-    const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
-    const float r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
     const WT *g = reinterpret_cast<const WT *>(a.gain);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = j * kThreads + tid;
-      if (ci < nchunk) {
-        float gv[E];
-        Vec16<WT>::unpack(load16(g + (size_t)ci * E), gv);
-#pragma unroll
-        for (int e = 0; e < E; ++e) xr[j][e] = gv[e] * (xr[j][e] * r);
-      }
-    }
+    for (int j = 0; j < KCH; ++j) gr[j] = load16(g + (size_t)min(j * kThreads + tid, nchunk - 1) * E);
   }
 
-  float best_v = -INFINITY;
-  int best_i = 0x7fffffff;
-
-  for (int grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+  // the weights of a row group: unconditional loads (a row past N reads row N-1, whose result is never
+  // stored; a chunk past the row end reads the row's last chunk and is zeroed)
+  auto load_group = [&](int grp, u32x4 (&wv)[NV][KCH]) {
     const int row0 = grp * R;
-    u32x4 wv[NV][KCH];
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
-        // unconditional loads: a row past N reads row N-1 (its result is never stored) and a chunk past
-        // the row end reads the row's last chunk (zeroed below)
-        const int crow = min(row, a.N - 1);
+        const int crow = min(row0 + r, a.N - 1);
         const WT *wp = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT *>(a.w[p]) + (size_t)crow * (size_t)a.K
                        : (EPI == EPI_ROPE) ? row_ptr<WT>(a, rope_row(crow, a.ra.dim + a.ra.kvw, a.ra.hshift))
                                            : row_ptr<WT>(a, crow);
@@ -151,12 +129,48 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
           const int ci = min(j * kThreads + tid, nchunk - 1);
           wv[p * R + r][j] = load_stream16(wp + (size_t)ci * E);
         }
-        if (ragged) {  // a chunk past the row end contributes exact zeros, whatever was stored there
-#pragma unroll
-          for (int j = 0; j < KCH; ++j)
-            if (j * kThreads + tid >= nchunk) wv[p * R + r][j] = u32x4{0u, 0u, 0u, 0u};
-        }
       }
+    }
+  };
+  // the first group's weights go out before the norm prologue (loads complete in order: the prologue
+  // waits for x and the gains only, and the weights stream meanwhile)
+  u32x4 wv[NV][KCH];
+  int grp = blockIdx.x;
+  if (grp < a.ngroups) load_group(grp, wv);
+
+  if (NORM) {
+    // RMSNorm prologue: g * (x * (1 / sqrt(sum(x^2) / K + eps)))
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += xr[j][e] * xr[j][e];
+    ss = wave_sum(ss);
+    if (lane == 0) ss_w[wave] = ss;
+    lds_barrier();
+    const float tot = (ss_w[0] + ss_w[1]) + (ss_w[2] + ss_w[3]);
+    const float r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      float gv[E];
+      Vec16<WT>::unpack(gr[j], gv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) xr[j][e] = gv[e] * (xr[j][e] * r);  // chunks past K: x = 0
+    }
+  }
+
+  float best_v = -INFINITY;
+  int best_i = 0x7fffffff;
+
+  for (; grp < a.ngroups; grp += gridDim.x) {
+    const int row0 = grp * R;
+    if (grp != (int)blockIdx.x) load_group(grp, wv);
+    if (ragged) {  // a chunk past the row end contributes exact zeros, whatever was stored there
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int j = 0; j < KCH; ++j)
+          if (j * kThreads + tid >= nchunk) wv[v][j] = u32x4{0u, 0u, 0u, 0u};
     }
     float acc[NV];
 #pragma unroll
