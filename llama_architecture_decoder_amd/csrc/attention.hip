@@ -182,8 +182,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 // k_attn_mfma (bf16 cache): each wavefront takes chunk/4 consecutive positions, in groups of 16.
 //   Scores: S[q][p] = Q K^T with v_mfma_f32_16x16x32_bf16, A = the group's query heads (rows q < g of
 //   16; the F32 queries as bf16 hi + lo, so the products are those of the F32 values to ~2^-17) and
-//   B = K^T, whose lane layout (lane l: position l%16, 8 consecutive numbers at 8(l/16) of a 32-wide
-//   slice) is a plain 16-byte load of a key row.  Lane l then holds S[4(l/16) + r][l%16].
+//   B = K^T (lane l: position l%16, 8 consecutive numbers at 8(l/16) of a 32-wide slice).  In large
+//   launches keys are loaded as whole rows and reach that layout through a small per-wave LDS tile, 16
+//   keys at a time; in small ones they are loaded in that layout directly.
+//   Lane l then holds S[4(l/16) + r][l%16].
 //   Softmax pieces per head over the wave's positions (max by DPP within 16-lane rows), the weights go
 //   through LDS to the layout of the V loads (lane l: position l/LPR of PPI rows, numbers 8(l%LPR) .. +8),
 //   and the weighted V sum runs on the vector units.  The wave's lane groups and the 4 waves are combined
@@ -216,10 +218,11 @@ struct MfmaAttnShape {
   static constexpr int NV = NPW / PPI;    // V loads per lane
   static constexpr int GP = G <= 4 ? 4 : 8;  // weights per position in LDS (padded)
   static constexpr int NG = kThreads / LPR;  // lane groups per block
-  static constexpr size_t LDS = sizeof(float) * (4 * NPW * GP + 8 * G + (size_t)NG * G * D);
+  static constexpr int KROW = D + 8;      // LDS row of a wave's 16-key staging tile (bf16)
+  static constexpr size_t LDS = sizeof(float) * (4 * NPW * GP + 8 * G + (size_t)NG * G * D) + 2 * 4 * 16 * KROW;
 };
 
-template <int D, int G, int NPW_>
+template <int D, int G, int NPW_, bool KROWS>
 __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   using S = MfmaAttnShape<D, G, NPW_>;
   constexpr int CHUNK = S::CHUNK, NPW = S::NPW, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
@@ -236,13 +239,16 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float p_s[4][NPW][GP];
   __shared__ float m_s[4][G], l_s[4][G];
   __shared__ __attribute__((aligned(16))) float o_g[NG][G][D];
+  __shared__ __attribute__((aligned(16))) bf16_t k_s[4][16 * S::KROW];  // each wave's 16 keys in turn
 
   const size_t head_off = ((size_t)(a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
   const bf16_t *Kh = reinterpret_cast<const bf16_t *>(a.kc) + head_off;
   const bf16_t *Vh = reinterpret_cast<const bf16_t *>(a.vc) + head_off;
 
   // (1) loads, oldest first: the queries (lane l: head l%16 of the group, numbers 32 ks + 8(l/16) .. +8),
-  // the keys in the B layout, the values in row slices.  Positions after t read row t (never used).
+  // then keys and values in row slices (lane l: 16 bytes at 8 (l%LPR) of row l/LPR of PPI rows, so a load
+  // reads whole rows; the MFMA layout would read 64-byte pieces of 16 rows, which streams slower).
+  // Positions after t read row t (never used).
   const int qrow = lane & 15, qh8 = (lane >> 4) * 8;
   const float *qp = a.q + (size_t)b * (a.kv * G * D) + ((size_t)j * G + min(qrow, G - 1)) * D;
   float4 qv[KS][2];
@@ -251,14 +257,22 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
     qv[ks][0] = *reinterpret_cast<const float4 *>(qp + 32 * ks + qh8);
     qv[ks][1] = *reinterpret_cast<const float4 *>(qp + 32 * ks + qh8 + 4);
   }
-  u32x4 kf[NGI][KS], vr[NV];
-#pragma unroll
-  for (int gi = 0; gi < NGI; ++gi) {
-    const int p = min(pw0 + 16 * gi + qrow, t);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[gi][ks] = load_stream16(Kh + (size_t)p * D + 32 * ks + qh8);
-  }
+  u32x4 kr[KROWS ? NV : 1], kb[KROWS ? 1 : NGI][KS], vr[NV];
   const int vl = lane % LPR, vg = lane / LPR;
+  if (KROWS) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int p = min(pw0 + PPI * i + vg, t);
+      kr[i] = load_stream16(Kh + (size_t)p * D + 8 * vl);
+    }
+  } else {
+#pragma unroll
+    for (int gi = 0; gi < NGI; ++gi) {
+      const int p = min(pw0 + 16 * gi + qrow, t);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[gi][ks] = load_stream16(Kh + (size_t)p * D + 32 * ks + qh8);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int p = min(pw0 + PPI * i + vg, t);
@@ -282,13 +296,34 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   // pw0 + 16 gi + lane%16
   const float scale2 = a.scale * 1.4426950408889634f;
   float sc[NGI][4];
+  bf16_t *kw = k_s[wave];
+  constexpr int IPG = 16 / PPI;  // key loads per 16-key group
 #pragma unroll
   for (int gi = 0; gi < NGI; ++gi) {
+    u32x4 kf[KS];
+    if (KROWS) {
+      // the group's 16 key rows through the wave's LDS tile into the B layout (lane l: key l%16, numbers
+      // 32 ks + 8(l/16) .. +8); LDS operations of a wave complete in order
+#pragma unroll
+      for (int u = 0; u < IPG; ++u)
+        *reinterpret_cast<u32x4 *>(&kw[(PPI * u + vg) * S::KROW + 8 * vl]) = kr[gi * IPG + u];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4 *>(&kw[qrow * S::KROW + 32 * ks + qh8]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = kb[gi][ks];
+    }
     af32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      acc = mfma16(qhi[ks], kf[gi][ks], acc);
-      acc = mfma16(qlo[ks], kf[gi][ks], acc);
+      acc = mfma16(qhi[ks], kf[ks], acc);
+      acc = mfma16(qlo[ks], kf[ks], acc);
     }
     const int p = pw0 + 16 * gi + qrow;
 #pragma unroll
@@ -514,7 +549,12 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
   a.direct = (nch_launch == 1);
   const bool merge = !a.direct;
   if constexpr (use_mfma<KT, D, G>()) {
-    launch(k_attn_mfma<D, G, kMfmaNpw>, grid, dim3(kThreads), s, true, !merge, a);
+    // keys as whole rows (through LDS) pay off when the launch streams many blocks per CU; a launch of
+    // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout
+    if ((long)B * a.kv * nch_launch >= 4096)
+      launch(k_attn_mfma<D, G, kMfmaNpw, true>, grid, dim3(kThreads), s, true, !merge, a);
+    else
+      launch(k_attn_mfma<D, G, kMfmaNpw, false>, grid, dim3(kThreads), s, true, !merge, a);
   } else {
     launch(k_attn<KT, D, G>, grid, dim3(kThreads), s, true, !merge, a);
   }
