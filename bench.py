@@ -284,6 +284,39 @@ def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
                       f"(same weights and pre-filled cache as the GPU run), {el:.1f}s wall"}
 
 
+def time_secondary(args, lm, synth, configs):
+    """The 1.7B shape (F32): its 512-position prompt, then 512 timed greedy steps, then a profiled pass."""
+    import torch
+    c3 = configs.SMOLLM2_1_7B
+    dec3, _, _, _ = build_model(c3, lm, synth, c3.max_seq, 0, keep_host=False)
+    prompt = torch.from_numpy(synth.tokens(c3, "bench/prompt", c3.prompt_len)).cuda()
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    dec3.prefill(prompt, pos0=0, next_tok=nxt)
+    torch.cuda.synchronize()
+    s3 = c3.decode_steps
+    ev3, _, _ = time_decode(dec3, c3, c3.prompt_len, s3, args.warmup, int(nxt.item()))
+    ms3 = ev3 / s3
+    pev3, _, prof3 = time_decode(dec3, c3, c3.prompt_len, s3, 0, int(nxt.item()), profile=True)
+    b3 = sum(token_bytes(c3, c3.prompt_len + i) for i in range(s3)) / s3
+    mean3 = c3.prompt_len + (s3 - 1) // 2
+    k3 = {}
+    for name, (n, kms) in prof3.items():
+        if n:
+            per = kms / n
+            kb = kernel_bytes(c3, name, mean3) if name != "embed" else None
+            k3[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(kms / pev3, 4),
+                        "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
+    res3 = {"workload": f"smollm2_1_7b-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
+                                       f"then {s3} steps at positions {c3.prompt_len}..{c3.prompt_len + s3 - 1}",
+                           "value": round(1e3 / ms3, 2), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
+                           "dtype": "f32", "hbm_fraction": round(b3 / (ms3 * 1e-3) / HBM_PEAK, 4),
+                           "bytes_per_token": int(b3), "kernels": k3}
+    log(f"1.7B: {1e3 / ms3:.1f} tok/s")
+    del dec3
+    torch.cuda.empty_cache()
+    return res3
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +328,8 @@ def main():
                     help="time only the 4096-position prefill (for profiling its kernels)")
     ap.add_argument("--batched-only", action="store_true",
                     help="time only the batch-32 long-context decode (for profiling its kernels)")
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="time only the 1.7B-shaped decode (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
@@ -315,6 +350,9 @@ def main():
     p0 = cfg.kv_fill
     steps = max(1, min(args.steps, cfg.max_seq - p0))
     want_cpu = not args.no_cpu_baseline
+    if args.secondary_only:
+        print(json.dumps({"secondary": time_secondary(args, lm, synth, configs)}), flush=True)
+        return
     if args.prefill_only or args.batched_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
         c5 = configs.LLAMA31_8B_LONG
@@ -394,23 +432,7 @@ def main():
     w = kc = vc = None
 
     if not args.no_secondary:
-        c3 = configs.SMOLLM2_1_7B
-        dec3, _, _, _ = build_model(c3, lm, synth, c3.max_seq, 0, keep_host=False)
-        prompt = torch.from_numpy(synth.tokens(c3, "bench/prompt", c3.prompt_len)).cuda()
-        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
-        dec3.prefill(prompt, pos0=0, next_tok=nxt)
-        torch.cuda.synchronize()
-        s3 = c3.decode_steps
-        ev3, _, _ = time_decode(dec3, c3, c3.prompt_len, s3, args.warmup, int(nxt.item()))
-        ms3 = ev3 / s3
-        b3 = sum(token_bytes(c3, c3.prompt_len + i) for i in range(s3)) / s3
-        result["secondary"] = {"workload": f"smollm2_1_7b-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
-                                           f"then {s3} steps at positions {c3.prompt_len}..{c3.prompt_len + s3 - 1}",
-                               "value": round(1e3 / ms3, 2), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
-                               "dtype": "f32", "hbm_fraction": round(b3 / (ms3 * 1e-3) / HBM_PEAK, 4),
-                               "bytes_per_token": int(b3)}
-        log(f"1.7B: {1e3 / ms3:.1f} tok/s")
-        del dec3
+        result["secondary"] = time_secondary(args, lm, synth, configs)
     print(json.dumps(result), flush=True)
 
 
