@@ -117,7 +117,7 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
+  size_t status, done, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
       total;
   int nch;
   int lm_ld;  // per-row stride of the LM head's block winners
@@ -162,6 +162,7 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
     return at;
   };
   L.status = take(64);
+  L.done = take(sizeof(unsigned) * (size_t)max_batch * d.kv);  // zeroed with the status word at init
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * rows * d.dim);
@@ -608,6 +609,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   aa.out_stride = H;
   aa.part_o = x.at<float>(x.L.part_o);
   aa.part_ml = x.at<float>(x.L.part_ml);
+  aa.done = x.at<unsigned>(x.L.done);
   aa.nch = x.L.nch;
   aa.scale = 1.0f / sqrtf((float)d.head);
   for (int b = 0; b < B; ++b) aa.pos[b] = pos[b];

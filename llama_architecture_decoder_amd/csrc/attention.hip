@@ -11,8 +11,9 @@
 // head j and all g query heads of the group, so each K/V byte is read from HBM once for g heads.
 // Two kernels: k_attn_mfma (bf16 caches) forms the scores on the matrix cores and the weighted V sum
 // on the vector units; k_attn (any cache type) does both on the vector units.  Each chunk writes an
-// unnormalised partial (o, m, l); a second small kernel merges the chunks of each (row, kv head) in
-// chunk order, so results do not depend on block timing.  When one chunk covers every row's positions
+// unnormalised partial (o, m, l); the chunks of each (row, kv head) are merged in chunk order, so
+// results do not depend on block timing: by a second small kernel, or for small merges by the last
+// block of the (row, kv head) to finish (device-scope stores, loads and a completion counter).  When one chunk covers every row's positions
 // the attention kernel normalises directly and no merge runs.
 //
 // k_attn: 256 threads = 256/LPR position groups of LPR lanes, LPR lanes covering one 16-byte slice each
@@ -34,7 +35,106 @@ struct AttnShape {
   static constexpr int CHUNK = NR * PPR;      // positions per block
 };
 
-template <typename KT, int D, int G>
+// The end of a chunk when the merge runs in the last block of its (row b, kv head j): the partials went
+// out with device-scope stores; once they have completed, one thread counts the chunk done with a
+// device-scope atomic, and the block that brings the count to nact merges every chunk in chunk order:
+// M = max_c m_c, w_c = 2^(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L (maxima are base 2),
+// reading the partials with device-scope loads, then clears the count for the next launch.
+template <int G, int D>
+__device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, size_t slot) {
+  constexpr int OPT = (G * D + kThreads - 1) / kThreads;  // outputs per thread
+  constexpr int CB = 16;                                    // chunks per batch of loads
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int last_s;
+  __shared__ float w_s[kAttnMaxChunks * G];
+  __shared__ float red_m[4][G], red_l[4][G];
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&a.done[b * a.kv + j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = prev == (unsigned)(nact - 1);
+  }
+  __syncthreads();
+  if (!last_s) return;
+  const float *pml = a.part_ml + slot * (size_t)(G * 2);
+  const float *po = a.part_o + slot * (size_t)(G * D);
+  // (m, l) of chunks tid, tid + 256 for every head
+  float mv[2][G], lv[2][G];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int cc = min(tid + k * kThreads, nact - 1);
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      mv[k][q] = load_dev(pml + (size_t)cc * G * 2 + 2 * q);
+      lv[k][q] = load_dev(pml + (size_t)cc * G * 2 + 2 * q + 1);
+    }
+  }
+  // the first batch of o partials goes out with them
+  float ov[OPT][CB];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i)
+#pragma unroll
+    for (int k = 0; k < CB; ++k)
+      ov[i][k] = load_dev(po + (size_t)min(k, nact - 1) * G * D + min(tid + i * kThreads, G * D - 1));
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (tid + k * kThreads < nact) m = fmaxf(m, mv[k][q]);
+    m = wave_max(m);
+    if (lane == 0) red_m[wave][q] = m;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const float M = fmaxf(fmaxf(red_m[0][q], red_m[1][q]), fmaxf(red_m[2][q], red_m[3][q]));
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int cc = tid + k * kThreads;
+      if (cc < nact) {
+        const float w = __builtin_amdgcn_exp2f(mv[k][q] - M);
+        w_s[cc * G + q] = w;
+        l = fmaf(w, lv[k][q], l);
+      }
+    }
+    l = wave_sum(l);
+    if (lane == 0) red_l[wave][q] = l;
+  }
+  lds_barrier();
+  float acc[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < nact; c0 += CB) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int i = 0; i < OPT; ++i)
+#pragma unroll
+        for (int k = 0; k < CB; ++k)
+          ov[i][k] = load_dev(po + (size_t)min(c0 + k, nact - 1) * G * D + min(tid + i * kThreads, G * D - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) {
+      const int q = min(tid + i * kThreads, G * D - 1) / D;
+#pragma unroll
+      for (int k = 0; k < CB; ++k)
+        if (c0 + k < nact) acc[i] = fmaf(w_s[(c0 + k) * G + q], ov[i][k], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < G * D) {
+      const int q = idx / D;
+      const float L = (red_l[0][q] + red_l[1][q]) + (red_l[2][q] + red_l[3][q]);
+      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc[i] / L;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&a.done[b * a.kv + j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename KT, int D, int G, bool SELF>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   using S = AttnShape<KT, D>;
   constexpr int E = S::E, LPR = S::LPR, PPR = S::PPR, NR = S::NR, CHUNK = S::CHUNK;
@@ -168,6 +268,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     }
     if (a.direct) {
       a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+    } else if (SELF) {
+      store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
+      if (d == 0) {
+        store_dev(&a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * i], M);
+        store_dev(&a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * i + 1], L);
+      }
     } else {
       a.part_o[(slot + c) * (size_t)(G * D) + idx] = acc;
       if (d == 0) {
@@ -176,6 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       }
     }
   }
+  if (SELF && !a.direct) finish_chunk_merge<G, D>(a, b, j, nact, slot);
 }
 
 // ------------------------------------------------------------------ matrix-core scores ----
@@ -222,7 +329,7 @@ struct MfmaAttnShape {
   static constexpr size_t LDS = sizeof(float) * (4 * NPW * GP + 8 * G + (size_t)NG * G * D) + 2 * 4 * 16 * KROW;
 };
 
-template <int D, int G, int NPW_, bool KROWS>
+template <int D, int G, int NPW_, bool KROWS, bool SELF>
 __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   using S = MfmaAttnShape<D, G, NPW_>;
   constexpr int CHUNK = S::CHUNK, NPW = S::NPW, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
@@ -416,6 +523,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
     }
     if (a.direct) {
       a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+    } else if (SELF) {
+      store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
+      if (d == 0) {
+        store_dev(&a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * q], M);
+        store_dev(&a.part_ml[(slot + c) * (size_t)(G * 2) + 2 * q + 1], L);
+      }
     } else {
       a.part_o[(slot + c) * (size_t)(G * D) + idx] = acc;
       if (d == 0) {
@@ -424,6 +537,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
       }
     }
   }
+  if (SELF && !a.direct) finish_chunk_merge<G, D>(a, b, j, nact, slot);
 }
 
 // Merge of the chunk partials of one (row, kv head), in chunk order (a separate launch: the kernel
@@ -548,17 +662,28 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
   const dim3 grid(nch_launch, a.kv, B);
   a.direct = (nch_launch == 1);
   const bool merge = !a.direct;
+  // Small merges (few chunks x few outputs per (row, kv head)) run in the attention kernel's last block
+  // per (row, kv head): measured faster than a separate launch for the 1.7B shape (8 chunks x 64 outputs:
+  // 7.4 vs 10.0 us per layer), slower for the 8B shape at 8K positions (32 x 512: 16.3 vs 14.6 us) and
+  // for 32 long rows.  LLAMA_ATTN_SEPARATE_MERGE forces the separate launch.
+  static const bool separate = getenv("LLAMA_ATTN_SEPARATE_MERGE") != nullptr;
+  const bool self = merge && !separate && (long)nch_launch * G * D <= 4096;
   if constexpr (use_mfma<KT, D, G>()) {
     // keys as whole rows (through LDS) pay off when the launch streams many blocks per CU; a launch of
     // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout
-    if ((long)B * a.kv * nch_launch >= 4096)
-      launch(k_attn_mfma<D, G, kMfmaNpw, true>, grid, dim3(kThreads), s, true, !merge, a);
-    else
-      launch(k_attn_mfma<D, G, kMfmaNpw, false>, grid, dim3(kThreads), s, true, !merge, a);
+    const bool krows = (long)B * a.kv * nch_launch >= 4096;
+    if (krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, true, true>, grid, dim3(kThreads), s, true, true, a);
+    if (krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, true, false>, grid, dim3(kThreads), s, true, !merge, a);
+    if (!krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, false, true>, grid, dim3(kThreads), s, true, true, a);
+    if (!krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, false, false>, grid, dim3(kThreads), s, true, !merge, a);
   } else {
-    launch(k_attn<KT, D, G>, grid, dim3(kThreads), s, true, !merge, a);
+    if (self)
+      launch(k_attn<KT, D, G, true>, grid, dim3(kThreads), s, true, true, a);
+    else
+      launch(k_attn<KT, D, G, false>, grid, dim3(kThreads), s, true, !merge, a);
   }
-  if (merge) launch(k_attn_merge<G, D>, dim3(G * D / 64, a.kv, B), dim3(kThreads), s, false, true, a, chunk);
+  if (merge && !self)
+    launch(k_attn_merge<G, D>, dim3(G * D / 64, a.kv, B), dim3(kThreads), s, false, true, a, chunk);
   return hipGetLastError();
 }
 

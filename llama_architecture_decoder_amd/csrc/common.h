@@ -350,6 +350,7 @@ struct AttnArgs {
   float *part_o;       // [B][kv][nch][g][head]
   float *part_ml;      // [B][kv][nch][g][2]
   int nch;             // chunk slots per (row, kv head) in the partial arrays
+  unsigned *done;      // [B][kv] chunks finished per (row, kv head); zero between launches
   int direct;          // set by the launcher: one chunk per row, outputs written normalised
   float scale;         // 1/sqrt(head)
   int pos[kMaxBatch];
@@ -395,6 +396,14 @@ int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is in
 hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int tmax, hipStream_t s);
 int attention_supported(int head, int g);
 int attention_chunk(int kvdtype, int head, int g);
+// device-scope stores and loads (the scope bits on the instruction keep them coherent across the XCDs'
+// L2 caches: a store is written through, a load does not hit a stale line)
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
  // the smallest chunk of positions an attention block takes
 int gemm_rows_supported(int wdtype, int K, int M);  // k_gemm_rows: bf16 weights, K % 128 == 0, 1 <= M <= 64
 int gemm_rows_blocks(int N, bool swiglu);
