@@ -284,10 +284,11 @@ def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
                       f"(same weights and pre-filled cache as the GPU run), {el:.1f}s wall"}
 
 
-def time_secondary(args, lm, synth, configs):
-    """The 1.7B shape (F32): its 512-position prompt, then 512 timed greedy steps, then a profiled pass."""
+def time_secondary(args, lm, synth, configs, c3=None):
+    """A batch-1 F32 workload (default the 1.7B shape): its prompt, then its timed greedy steps, then a
+    profiled pass."""
     import torch
-    c3 = configs.SMOLLM2_1_7B
+    c3 = c3 or configs.SMOLLM2_1_7B
     dec3, _, _, _ = build_model(c3, lm, synth, c3.max_seq, 0, keep_host=False)
     prompt = torch.from_numpy(synth.tokens(c3, "bench/prompt", c3.prompt_len)).cuda()
     nxt = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -306,12 +307,12 @@ def time_secondary(args, lm, synth, configs):
             kb = kernel_bytes(c3, name, mean3) if name != "embed" else None
             k3[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(kms / pev3, 4),
                         "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
-    res3 = {"workload": f"smollm2_1_7b-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
+    res3 = {"workload": f"{c3.name}-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
                                        f"then {s3} steps at positions {c3.prompt_len}..{c3.prompt_len + s3 - 1}",
                            "value": round(1e3 / ms3, 2), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
                            "dtype": "f32", "hbm_fraction": round(b3 / (ms3 * 1e-3) / HBM_PEAK, 4),
                            "bytes_per_token": int(b3), "kernels": k3}
-    log(f"1.7B: {1e3 / ms3:.1f} tok/s")
+    log(f"{c3.name}: {1e3 / ms3:.1f} tok/s")
     del dec3
     torch.cuda.empty_cache()
     return res3
@@ -433,6 +434,9 @@ def main():
 
     if not args.no_secondary:
         result["secondary"] = time_secondary(args, lm, synth, configs)
+        # the two small shapes of the pages' table, for completeness (launch-bound at these sizes)
+        result["small_shapes"] = [time_secondary(args, lm, synth, configs, c)
+                                  for c in (configs.SMOLLM2_135M, configs.SMOLLM2_360M)]
     print(json.dumps(result), flush=True)
 
 
