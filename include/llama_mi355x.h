@@ -105,7 +105,8 @@ typedef struct llama_kv {
 
 /* A workspace bound by llama_workspace_init: device scratch (activations, split-attention partials,
  * counters, the rope cos/sin table, the status flag) for batches up to max_batch, positions up to
- * max_seq and prompts up to max_prefill tokens.  Fill it only through llama_workspace_init. */
+ * max_seq and prompt chunks of up to max_prefill positions (the matrix-core prefill; 0 = none, at most
+ * 65535).  Fill it only through llama_workspace_init. */
 typedef struct llama_ws {
   void *base;
   size_t bytes;
@@ -125,7 +126,8 @@ int kv_cache_alloc(const llama_cfg *c, int32_t rows, int32_t max_seq, void *k_me
 /* Bytes of workspace for the given capacities; < 0 on error. */
 int64_t llama_workspace_bytes(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill);
 
-/* Bind `mem` (>= llama_workspace_bytes) as a workspace: clears its status flag and uploads
+/* Bind `mem` (>= llama_workspace_bytes) as a workspace: clears its status flag and the attention
+ * kernels' per-(row, kv head) completion counters (each call leaves them zero again), and uploads
  * the rope cos/sin table for positions 0..max_seq-1 (angle t*inv_freq[i] rounded to F32, then cos, sin;
  * main.bend rot_at).  Synchronous: returns after the stream has finished the upload. */
 int llama_workspace_init(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32_t max_prefill, void *mem,
@@ -160,8 +162,11 @@ int llama_decode_step_traced(const llama_cfg *c, const llama_weights *w, const l
  * A prompt of S tokens (device int32 [S]) into cache row `row` at positions pos0..pos0+S-1
  * (main.bend forward_pre for each prompt position; nest prefill<S>(tokens, pos)), then the final norm,
  * LM head and argmax after the last token only: logits_last [vocab] and next [1] (each optional).
- * Decoding continues at pos0 + S.  Errors: E_SHAPE (S <= 0, row outside the cache, S > ws->max_prefill
- * when the batched path is used), E_POS (pos0 < 0, pos0 + S > max_seq), plus those of decode.
+ * Decoding continues at pos0 + S.  With bf16 weights and cache and a workspace whose max_prefill >= 2,
+ * the prompt goes through each layer in chunks of up to max_prefill positions (matrix-core products over
+ * the chunk, causal attention over the cache); otherwise one position after another through the decode
+ * kernels.  Errors: E_SHAPE (S <= 0, row outside the cache), E_POS (pos0 < 0, pos0 + S > max_seq), plus
+ * those of decode.
  */
 int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, int32_t row, const int32_t *tokens,
                   int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream);
