@@ -68,6 +68,14 @@ def lib():
     L.oracle_prefill_row.restype = i32
     L.oracle_bf16.argtypes = [f32]
     L.oracle_bf16.restype = ctypes.c_uint16
+    L.oracle_hash32.argtypes = [ctypes.c_uint32]
+    L.oracle_hash32.restype = ctypes.c_uint32
+    L.oracle_uniform.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    L.oracle_uniform.restype = f32
+    L.oracle_topk.argtypes = [i32, vp, i32, vp, vp]
+    L.oracle_topk.restype = i32
+    L.oracle_sample.argtypes = [i32, vp, f32, i32, f32, f32, vp, vp, vp]
+    L.oracle_sample.restype = i32
     _lib = L
     return L
 
@@ -156,6 +164,37 @@ def head_attention(q, K, V, t: int, scale: float, kvdt: int = F32) -> np.ndarray
 
 def bf16(x: float) -> int:
     return int(lib().oracle_bf16(np.float32(x)))
+
+
+# ------------------------------------------------------------------------ sampling ----
+
+def hash32(x: int) -> int:
+    return int(lib().oracle_hash32(int(x) & 0xFFFFFFFF))
+
+
+def uniform(seed: int, n: int) -> np.float32:
+    return np.float32(lib().oracle_uniform(int(seed) & 0xFFFFFFFF, int(n) & 0xFFFFFFFF))
+
+
+def topk(xs, k: int):
+    """(ids, values) of the min(k, n) largest, largest first, equal values in id order."""
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    kk = max(0, min(int(k), xs.size))
+    ids = np.empty(max(kk, 1), dtype=np.int32)
+    vals = np.empty(max(kk, 1), dtype=np.float32)
+    m = lib().oracle_topk(xs.size, _p(xs), int(k), _p(ids), _p(vals))
+    return ids[:m], vals[:m]
+
+
+def sample(xs, temp: float, k: int, p: float, u: float):
+    """One draw: (id, logit, kept count, kept weight z)."""
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    v = ctypes.c_float()
+    nk = ctypes.c_int32()
+    z = ctypes.c_float()
+    i = lib().oracle_sample(xs.size, _p(xs), np.float32(temp), int(k), np.float32(p), np.float32(u),
+                            ctypes.byref(v), ctypes.byref(nk), ctypes.byref(z))
+    return int(i), np.float32(v.value), int(nk.value), np.float32(z.value)
 
 
 # ----------------------------------------------------------------------- the model ----

@@ -7,7 +7,7 @@
  * Sources (page titles as printed):
  *   [bend]   bend-ml-llama@0.2.1.0 main.bend (jend.leeeet.dev): "The configuration", "The numeric
  *            pieces", "The key/value cache in flat arrays", "Grouped-query attention over the
- *            arrays", "A layer", "The model".  Every F32 operation there follows transformers'
+ *            arrays", "A layer", "The model", "Sampling".  Every F32 operation there follows transformers'
  *            modeling_llama.py, and this file takes the same operations in the same order.
  *   [nest]   Llama 3.1 8B Instruct model card (nest.franknoh.dev): README "Validation" and
  *            `rope.linnet` (`tables`) for the llama3 frequency rescale; `attention.linnet`
@@ -366,3 +366,107 @@ int oracle_prefill_row(const ocfg *c, const omodel *m, void *kc, void *vc, int r
 
 /* F32 -> bf16 bits as the oracle rounds cache writes (exposed for tests) */
 uint16_t oracle_bf16(float f) { return o_bf16(f); }
+
+/* ------------------------------------------------------ sampling ([bend] "Sampling") ---- */
+/*
+ * Temperature, top-k and top-p with one uniform draw, every step an F32 operation in the order the
+ * page gives.  Readings taken where the page leaves a step open: F32.exp is the correctly rounded
+ * F32 exponential (here exp in double precision, rounded once to float); logits are finite, so the
+ * IEEE comparisons the page uses never meet a NaN.
+ */
+
+/* lowbias32 (Chris Wellons, public domain): two xor-shift / odd-multiply rounds and a last xor-shift,
+ * a bijection on 32-bit words ([bend] hash32). */
+uint32_t oracle_hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 2146121005u;
+  x ^= x >> 15;
+  x *= 2221713035u;
+  x ^= x >> 16;
+  return x;
+}
+
+/* draw n of a seed: the top 24 bits of hash32(hash32(seed) + n) scaled by 2^-24, exact in F32 and in
+ * [0, 1) ([bend] uniform) */
+float oracle_uniform(uint32_t seed, uint32_t n) {
+  uint32_t h = oracle_hash32(oracle_hash32(seed) + n);
+  return (float)(h >> 8) * 5.9604644775390625e-8f;
+}
+
+/* The k largest of xs[0..n), largest first, in one pass over xs ([bend] topk): a value enters while
+ * fewer than k are held, or when it is strictly above the smallest held; it is placed after every held
+ * value that is not smaller than it, so equal values keep id order (lower id first), and the list is
+ * cut back to k.  Writes min(k, n) candidates and returns that count. */
+int oracle_topk(int n, const float *xs, int k, int32_t *ids, float *vals) {
+  int m = 0;
+  if (k <= 0) return 0;
+  for (int i = 0; i < n; ++i) {
+    const float h = xs[i];
+    if (!(m < k || h > vals[m - 1])) continue;
+    int at = 0;
+    while (at < m && !(vals[at] < h)) ++at; /* walk past the held values that are not smaller */
+    int last = (m < k) ? m : k - 1;         /* the slot that receives the tail (the k-th drops off) */
+    for (int j = last; j > at; --j) {
+      vals[j] = vals[j - 1];
+      ids[j] = ids[j - 1];
+    }
+    vals[at] = h;
+    ids[at] = i;
+    if (m < k) ++m;
+  }
+  return m;
+}
+
+/* exp(v/temp - top/temp): the weight of a candidate, 1 for the largest ([bend] weight) */
+static float samp_weight(float v, float temp, float top) {
+  const float a = v / temp;
+  const float b = top / temp;
+  const float d = a - b;
+  return (float)exp((double)d);
+}
+
+/*
+ * One draw ([bend] sample): top-k candidates; Z = their weights summed from 0 in candidate order;
+ * lim = p * Z; the first candidate is always kept and each next one is kept while the running weight
+ * before it is below lim ([bend] kept.go); z = the kept weight; target = u * z; the draw stops at the
+ * first kept candidate whose running weight including itself is above target, or at the last kept one
+ * ([bend] stops, pick.go).  Returns the drawn id (or -1 for n <= 0 or k <= 0) and, when the pointers
+ * are not NULL, its logit, the kept count and the kept weight z.
+ */
+int oracle_sample(int n, const float *xs, float temp, int k, float p, float u, float *v_out, int32_t *n_kept,
+                  float *z_out) {
+  if (n <= 0 || k <= 0) return -1;
+  const int kk = k < n ? k : n;
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * kk);
+  float *vals = (float *)malloc(sizeof(float) * kk);
+  const int m = oracle_topk(n, xs, k, ids, vals);
+  const float top = vals[0];
+  float Z = 0.0f;
+  for (int j = 0; j < m; ++j) Z = Z + samp_weight(vals[j], temp, top);
+  const float lim = p * Z;
+  int kept = 0;
+  float acc = 0.0f;
+  for (int j = 0; j < m; ++j) {
+    if (j > 0 && !(acc < lim)) break; /* the running weight before candidate j */
+    acc = acc + samp_weight(vals[j], temp, top);
+    ++kept;
+  }
+  const float z = acc;
+  const float target = u * z;
+  int pick = kept - 1;
+  float run = 0.0f;
+  for (int j = 0; j < kept - 1; ++j) {
+    run = run + samp_weight(vals[j], temp, top);
+    if (target < run) {
+      pick = j;
+      break;
+    }
+  }
+  const int id = ids[pick];
+  if (v_out) *v_out = vals[pick];
+  if (n_kept) *n_kept = kept;
+  if (z_out) *z_out = z;
+  free(ids);
+  free(vals);
+  return id;
+}
