@@ -179,6 +179,33 @@ int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidd
                    int32_t *argmax, const llama_ws *ws, void *stream);
 
 /*
+ * Sampling with temperature, top-k and top-p (main.bend "Sampling": topk, weight, total, kept, pick,
+ * sample; draws from its `uniform`).  For each row b < B of logits (device F32, row b at
+ * logits + b*ld, V values): the min(k, V) largest logits, largest first, equal logits in id order;
+ * weights w_j = exp(v_j/temp - v_0/temp) in F32 (the exponential correctly rounded); running sums
+ * S_j = S_{j-1} + w_j from 0 in that order, Z the last; top-p keeps candidate 0 and each next one while
+ * the running sum before it is below p*Z; z = the running sum of the last kept one; with the uniform
+ * u_b, the drawn candidate is the first kept one whose S_j is above u_b*z, else the last kept one.
+ *   u_b      u[b] when `u` (device F32 [B], values in [0, 1)) is not NULL, else draw `draw` of the seed
+ *            seeds[b] (device uint32 [B]): the top 24 bits of lowbias32(lowbias32(seed) + draw) times
+ *            2^-24, so a (seed, draw) pair gives the same u whatever ran before.
+ *   ids      device int32 [B]: the drawn token ids (required); vals: device F32 [B], their logits
+ *            (optional); topk_ids: device int32 [B][k], the candidates in order, -1 past V (optional).
+ *   scratch  device memory of at least llama_sample_scratch_bytes(B, V, k) bytes, 8-byte aligned,
+ *            owned by the caller; it holds per-chunk candidates between the two kernels, so calls
+ *            sharing one scratch buffer must be ordered on one stream.
+ * Logits must be finite.  Runs on `stream`; every value is written on the device, nothing is
+ * synchronised.  Errors (nothing launched): E_SHAPE (B < 0, V < 1, ld < V), E_CONFIG (k < 1, temp not
+ * finite and > 0, p not finite), E_NULL (logits, ids or scratch NULL, or both seeds and u NULL),
+ * E_WORKSPACE (scratch too small or misaligned), E_UNSUPPORTED (k > 256, or V above 4096 * (16384 /
+ * K2) with K2 = k rounded up to a power of two: 262144 at k = 256).  B = 0 returns LLAMA_OK.
+ */
+int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k);
+int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
+                 const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals, int32_t *topk_ids,
+                 void *scratch, size_t scratch_bytes, void *stream);
+
+/*
  * Kernel timing for measurement.  While enabled, every kernel launch of the calls above is bracketed
  * by two HIP events recorded on the call's stream, grouped by kernel class; llama_profile_read waits
  * for the recorded events and returns the number of launches of one class and their summed elapsed
@@ -187,7 +214,7 @@ int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidd
  */
 enum {
   LLAMA_K_EMBED = 0, LLAMA_K_QKV = 1, LLAMA_K_ATTN = 2, LLAMA_K_O = 3, LLAMA_K_GATE_UP = 4, LLAMA_K_DOWN = 5,
-  LLAMA_K_LM_HEAD = 6
+  LLAMA_K_LM_HEAD = 6, LLAMA_K_SAMPLE = 7
 };
 int llama_profile_enable(int on);
 int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms);

@@ -91,6 +91,10 @@ def lib():
     L.llama_prefill.argtypes = [pc, pw, pk, i32, vp, i32, i32, vp, vp, ps, vp]
     L.lm_head_argmax.argtypes = [pc, pw, vp, i32, vp, vp, ps, vp]
     L.llama_status.argtypes = [ps, vp]
+    L.llama_sample_scratch_bytes.argtypes = [i32, i32, i32]
+    L.llama_sample_scratch_bytes.restype = i64
+    L.llama_sample.argtypes = [vp, i64, i32, i32, ctypes.c_float, i32, ctypes.c_float, vp, ctypes.c_uint32, vp, vp,
+                               vp, vp, vp, sz, vp]
     L.llama_profile_enable.argtypes = [ctypes.c_int]
     L.llama_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
     _lib = L
@@ -274,9 +278,37 @@ class Decoder:
         return int(lib().llama_status(ctypes.byref(self.ws.rec), _stream_handle(stream)))
 
 
-K_EMBED, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LM_HEAD = range(7)
+K_EMBED, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LM_HEAD, K_SAMPLE = range(8)
 KERNEL_CLASSES = {"embed": K_EMBED, "qkv": K_QKV, "attention": K_ATTN, "o_proj": K_O, "gate_up": K_GATE_UP,
-                  "down": K_DOWN, "lm_head": K_LM_HEAD}
+                  "down": K_DOWN, "lm_head": K_LM_HEAD, "sample": K_SAMPLE}
+
+
+def sample_scratch_bytes(B: int, V: int, k: int) -> int:
+    n = int(lib().llama_sample_scratch_bytes(B, V, k))
+    if n < 0:
+        raise LlamaError(n, "llama_sample_scratch_bytes")
+    return n
+
+
+def sample(logits, temp: float, k: int, p: float, seeds=None, draw: int = 0, u=None, ids=None, vals=None,
+           topk_ids=None, scratch=None, stream=None):
+    """Draw one token per row of `logits` (device F32 [B][V], rows may be strided) with temperature,
+    top-k and top-p.  u: device F32 [B] uniforms, or None to draw `draw` of each row's seed (device
+    uint32 [B], as int32 tensors).  Returns the ids tensor (device int32 [B]); vals and topk_ids are
+    filled when given.  scratch: a device uint8 tensor of sample_scratch_bytes(B, V, k) bytes, or None
+    to allocate one."""
+    torch = _torch()
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    if ids is None:
+        ids = torch.empty(B, dtype=torch.int32, device=logits.device)
+    if scratch is None:
+        scratch = torch.empty(max(8, sample_scratch_bytes(B, V, k)), dtype=torch.uint8, device=logits.device)
+    rc = lib().llama_sample(logits.data_ptr(), int(logits.stride(0)), B, V, float(temp), int(k), float(p),
+                            _ptr(seeds), int(draw) & 0xFFFFFFFF, _ptr(u), ids.data_ptr(), _ptr(vals), _ptr(topk_ids),
+                            scratch.data_ptr(), int(scratch.numel()), _stream_handle(stream))
+    _check(rc, "llama_sample")
+    return ids
 
 
 def profile_enable(on: bool = True) -> None:

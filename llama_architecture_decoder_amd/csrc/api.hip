@@ -7,6 +7,8 @@
 // Every check that the host can make happens before the first launch, so an error leaves the caches
 // and outputs untouched (main.bend's room proof before KV.push; needle's validation before use).
 #include <math.h>
+
+#include <cmath>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -959,6 +961,56 @@ int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms) {
   *launches = n;
   *total_ms = ms;
   return LLAMA_OK;
+}
+
+namespace {
+int sample_k2(int k) {
+  int k2 = 1;
+  while (k2 < k) k2 <<= 1;
+  return k2;
+}
+}  // namespace
+
+int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k) {
+  if (B < 0 || V < 1) return LLAMA_E_SHAPE;
+  if (k < 1) return LLAMA_E_CONFIG;
+  if (k > kSampleMaxK) return LLAMA_E_UNSUPPORTED;
+  const int K2 = sample_k2(k);
+  if (sample_sort_size(V, K2) > kSampleSortMax) return LLAMA_E_UNSUPPORTED;
+  return (int64_t)B * sample_chunks(V) * K2 * (int64_t)sizeof(uint64_t);
+}
+
+int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
+                 const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals, int32_t *topk_ids,
+                 void *scratch, size_t scratch_bytes, void *stream) {
+  const int64_t need = llama_sample_scratch_bytes(B, V, k);
+  if (need < 0) return (int)need;
+  if (ld < V) return LLAMA_E_SHAPE;
+  if (!(temp > 0.f) || !std::isfinite(temp) || !std::isfinite(p)) return LLAMA_E_CONFIG;
+  if (B == 0) return LLAMA_OK;
+  if (!logits || !ids || (!seeds && !u)) return LLAMA_E_NULL;
+  if (!scratch) return LLAMA_E_NULL;
+  if ((size_t)need > scratch_bytes || ((uintptr_t)scratch & 7u)) return LLAMA_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  SampleArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.V = V;
+  a.k = k;
+  a.K2 = sample_k2(k);
+  a.nchunk = sample_chunks(V);
+  a.n2 = sample_sort_size(V, a.K2);
+  a.temp = temp;
+  a.p = p;
+  a.seeds = seeds;
+  a.draw = draw;
+  a.u = u;
+  a.ids = ids;
+  a.vals = vals;
+  a.topk_ids = topk_ids;
+  a.cand = reinterpret_cast<uint64_t *>(scratch);
+  ProfScope ps(LLAMA_K_SAMPLE, s);
+  return hip_rc(launch_sample(a, B, s));
 }
 
 int llama_status(const llama_ws *ws, void *stream) {

@@ -424,6 +424,27 @@ hipError_t launch_argmax_final(const float *part_v, const int *part_i, int n, in
                                hipStream_t s);
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
                         int *status, hipStream_t s);
+
+// sampling (temperature, top-k, top-p): per-row candidate keys of the first pass in `cand`
+// [B][nchunk][K2]; the second pass sorts n2 = sample_sort_size(V, K2) keys per row in LDS
+constexpr int kSampleMaxK = 256;
+constexpr int kSampleSortMax = 16384;
+struct SampleArgs {
+  const float *logits;
+  int64_t ld;
+  int V, k, K2, nchunk, n2;
+  float temp, p;
+  const uint32_t *seeds;
+  uint32_t draw;
+  const float *u;
+  int32_t *ids;
+  float *vals;
+  int32_t *topk_ids;
+  uint64_t *cand;
+};
+int sample_chunks(int V);
+int sample_sort_size(int V, int K2);
+hipError_t launch_sample(const SampleArgs &a, int B, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 }  // namespace lm

@@ -19,7 +19,8 @@ def test_header_declares_the_boundary():
     names = set(lm.header_functions())
     for need in ("llama_decode_step", "llama_prefill", "kv_cache_alloc", "lm_head_argmax", "llama_kv_cache_bytes",
                  "llama_workspace_bytes", "llama_workspace_init", "llama_status", "llama_strerror",
-                 "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version"):
+                 "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version", "llama_sample",
+                 "llama_sample_scratch_bytes"):
         assert need in names, need
 
 
@@ -137,3 +138,43 @@ def test_decode_and_prefill_reject_before_any_device_work(L):
     # a misaligned weight pointer is refused
     lw[3].wq = fake + 2
     assert dec(1, [0]) == lm.E_SHAPE
+
+
+def test_sample_scratch_bytes_and_argument_checks(L):
+    """Sampling's size query and its argument errors, all decided on the host (the fake device pointers
+    are never dereferenced)."""
+    V = 128256
+    # 32 chunks of 4096 logits, k = 50 rounds up to 64 candidates per chunk, 8-byte keys
+    assert L.llama_sample_scratch_bytes(3, V, 50) == 3 * 32 * 64 * 8
+    assert L.llama_sample_scratch_bytes(1, 1, 1) == 8
+    assert L.llama_sample_scratch_bytes(0, V, 1) == 0
+    assert L.llama_sample_scratch_bytes(-1, V, 1) == lm.E_SHAPE
+    assert L.llama_sample_scratch_bytes(1, 0, 1) == lm.E_SHAPE
+    assert L.llama_sample_scratch_bytes(1, V, 0) == lm.E_CONFIG
+    assert L.llama_sample_scratch_bytes(1, V, 257) == lm.E_UNSUPPORTED
+    assert L.llama_sample_scratch_bytes(1, 262144, 256) == 64 * 256 * 8
+    assert L.llama_sample_scratch_bytes(1, 262145, 256) == lm.E_UNSUPPORTED
+    assert L.llama_sample_scratch_bytes(1, 524288, 128) == 128 * 128 * 8
+    fake = 1 << 40
+    big = 1 << 30
+
+    def smp(B=1, V=V, ld=V, temp=0.8, k=50, p=0.9, seeds=fake, u=None, ids=fake, scratch=fake, nbytes=big,
+            logits=fake):
+        return L.llama_sample(logits, ld, B, V, temp, k, p, seeds, 0, u, ids, None, None, scratch, nbytes, None)
+
+    assert smp(ld=V - 1) == lm.E_SHAPE
+    assert smp(B=-1) == lm.E_SHAPE
+    assert smp(temp=0.0) == lm.E_CONFIG
+    assert smp(temp=-1.0) == lm.E_CONFIG
+    assert smp(temp=float("inf")) == lm.E_CONFIG
+    assert smp(temp=float("nan")) == lm.E_CONFIG
+    assert smp(p=float("nan")) == lm.E_CONFIG
+    assert smp(k=0) == lm.E_CONFIG
+    assert smp(k=300) == lm.E_UNSUPPORTED
+    assert smp(logits=None) == lm.E_NULL
+    assert smp(ids=None) == lm.E_NULL
+    assert smp(seeds=None) == lm.E_NULL
+    assert smp(scratch=None) == lm.E_NULL
+    assert smp(nbytes=32 * 64 * 8 - 1) == lm.E_WORKSPACE
+    assert smp(scratch=fake + 4) == lm.E_WORKSPACE
+    assert smp(B=0, logits=None, ids=None, scratch=None) == lm.OK
