@@ -318,6 +318,38 @@ def time_secondary(args, lm, synth, configs, c3=None):
     return res3
 
 
+def time_sample(lm, vocab, reps=200):
+    """Sampling (temperature 0.6, top-k 50, top-p 0.9) over synthetic F32 logits resident in HBM, for 1
+    and 64 rows of the vocabulary; HIP events around `reps` back-to-back calls on one stream."""
+    import torch
+    out = {"workload": f"sampling over [B][{vocab}] F32 logits: temperature 0.6, top-k 50, top-p 0.9, "
+                       f"seeded draws", "rows": {}}
+    for B in (1, 64):
+        g = torch.Generator(device="cuda").manual_seed(1234 + B)
+        logits = torch.randn((B, vocab), generator=g, device="cuda") * 3.0
+        seeds = torch.arange(B, dtype=torch.int32, device="cuda")
+        ids = torch.empty(B, dtype=torch.int32, device="cuda")
+        scratch = torch.empty(lm.sample_scratch_bytes(B, vocab, 50), dtype=torch.uint8, device="cuda")
+        for i in range(5):
+            lm.sample(logits, 0.6, 50, 0.9, seeds=seeds, draw=i, ids=ids, scratch=scratch)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            lm.sample(logits, 0.6, 50, 0.9, seeds=seeds, draw=i, ids=ids, scratch=scratch)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = B * vocab * 4
+        out["rows"][str(B)] = {"us_per_call": round(us, 2), "logit_bytes": nbytes,
+                               "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                               "hbm_fraction": round(nbytes / (us * 1e-6) / HBM_PEAK, 4)}
+        log(f"sampling B={B}: {us:.2f} us per call")
+        del logits, scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +363,8 @@ def main():
                     help="time only the batch-32 long-context decode (for profiling its kernels)")
     ap.add_argument("--secondary-only", action="store_true",
                     help="time only the 1.7B-shaped decode (for profiling its kernels)")
+    ap.add_argument("--sample-only", action="store_true",
+                    help="time only sampling over the 8B vocabulary (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
@@ -353,6 +387,9 @@ def main():
     want_cpu = not args.no_cpu_baseline
     if args.secondary_only:
         print(json.dumps({"secondary": time_secondary(args, lm, synth, configs)}), flush=True)
+        return
+    if args.sample_only:
+        print(json.dumps({"sampling": time_sample(lm, cfg.vocab)}), flush=True)
         return
     if args.prefill_only or args.batched_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
@@ -413,6 +450,7 @@ def main():
         result["prefill"] = time_prefill(c5, lm, synth, dec.w, 3, 1)
         log(f"prefill {c5.prompt_len}: {result['prefill']['ms_per_prefill']:.1f} ms, "
             f"{result['prefill']['tflops']:.0f} TFLOP/s")
+        result["sampling"] = time_sample(lm, cfg.vocab)
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:

@@ -197,8 +197,8 @@ int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidd
  * Logits must be finite.  Runs on `stream`; every value is written on the device, nothing is
  * synchronised.  Errors (nothing launched): E_SHAPE (B < 0, V < 1, ld < V), E_CONFIG (k < 1, temp not
  * finite and > 0, p not finite), E_NULL (logits, ids or scratch NULL, or both seeds and u NULL),
- * E_WORKSPACE (scratch too small or misaligned), E_UNSUPPORTED (k > 256, or V above 4096 * (16384 /
- * K2) with K2 = k rounded up to a power of two: 262144 at k = 256).  B = 0 returns LLAMA_OK.
+ * E_WORKSPACE (scratch too small or misaligned), E_UNSUPPORTED (k > 256, or V above 8192 * (8192 / K2)
+ * with K2 = k rounded up to a power of two: 262144 at k = 256).  B = 0 returns LLAMA_OK.
  */
 int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k);
 int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,

@@ -976,7 +976,7 @@ int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k) {
   if (k < 1) return LLAMA_E_CONFIG;
   if (k > kSampleMaxK) return LLAMA_E_UNSUPPORTED;
   const int K2 = sample_k2(k);
-  if (sample_sort_size(V, K2) > kSampleSortMax) return LLAMA_E_UNSUPPORTED;
+  if (sample_candidates(V, K2) > kSampleCandMax) return LLAMA_E_UNSUPPORTED;
   return (int64_t)B * sample_chunks(V) * K2 * (int64_t)sizeof(uint64_t);
 }
 
@@ -999,7 +999,6 @@ int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float te
   a.k = k;
   a.K2 = sample_k2(k);
   a.nchunk = sample_chunks(V);
-  a.n2 = sample_sort_size(V, a.K2);
   a.temp = temp;
   a.p = p;
   a.seeds = seeds;

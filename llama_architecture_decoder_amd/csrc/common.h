@@ -426,13 +426,13 @@ hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int 
                         int *status, hipStream_t s);
 
 // sampling (temperature, top-k, top-p): per-row candidate keys of the first pass in `cand`
-// [B][nchunk][K2]; the second pass sorts n2 = sample_sort_size(V, K2) keys per row in LDS
+// [B][nchunk][K2]; the second pass selects from the nchunk*K2 <= kSampleCandMax keys of a row
 constexpr int kSampleMaxK = 256;
-constexpr int kSampleSortMax = 16384;
+constexpr int kSampleCandMax = 8192;
 struct SampleArgs {
   const float *logits;
   int64_t ld;
-  int V, k, K2, nchunk, n2;
+  int V, k, K2, nchunk;
   float temp, p;
   const uint32_t *seeds;
   uint32_t draw;
@@ -443,7 +443,7 @@ struct SampleArgs {
   uint64_t *cand;
 };
 int sample_chunks(int V);
-int sample_sort_size(int V, int K2);
+int sample_candidates(int V, int K2);
 hipError_t launch_sample(const SampleArgs &a, int B, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 

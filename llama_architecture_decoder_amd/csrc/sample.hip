@@ -6,28 +6,27 @@
 // equal), the low word is 0xFFFFFFFF − id, so a larger key is a larger logit or, for equal logits,
 // the lower id.  Keys are unique; 0 marks an empty slot (no real key is 0).
 //
-//   k_topk_chunk   block (c, b): the 4096 logits of chunk c of row b into LDS as keys, a bitonic
-//                  sort, the K2 largest out (K2 = k rounded up to a power of two).
-//   k_sample_rows  block b: the nchunk sorted lists of row b into LDS with every odd list reversed,
-//                  which is the state of a bitonic sort after its runs of K2, so the sort continues
-//                  from runs of 2*K2; then one wavefront does the draw.
+//   k_topk_chunk   block (c, b): the 8192 logits of chunk c of row b, 32 keys per thread in
+//                  registers; their K2 largest (K2 = k rounded up to a power of two), sorted, out.
+//   k_sample_rows  block b: the nchunk lists of row b, the K2 largest of them, then one wavefront
+//                  does the draw.
 //
-// The draw keeps the page's F32 order: each candidate's weight exp(v/temp − top/temp) (the
-// exponential computed in double and rounded once, i.e. the correctly rounded F32 value), one
-// running sum from 0 in candidate order (lanes hand their weights to the sum through readlane, and
-// each lane keeps the partial sums of its candidates), Z = the last running sum, lim = p*Z, kept =
-// the candidates up to the first one after which the running sum is not below lim, z = the running
-// sum of the last kept one, target = u*z, and the draw is the first kept candidate whose running
-// sum is above target, or the last kept one.  Every partial sum the page forms (total, kept.go,
-// pick.go) is one of these running sums, so the comparisons see the same F32 values.
+// Selection of the K2 largest of a block's keys (block_select) sorts only what can be among them.
+// Each wavefront sorts its 64 per-thread maxima in registers and takes the m-th largest, m =
+// ceil(K2/4); T, the smallest of the four, has at least K2 keys at or above it (m distinct maxima in
+// each wavefront), so every key of the answer is >= T.  The keys >= T are appended to LDS (positions
+// from ballots, one LDS atomic per wavefront) and sorted: in registers by one wavefront when there
+// are at most 256, else by a bitonic network over LDS.  If more than the LDS buffer holds pass T (only
+// for adversarial orders), the buffer's K2-th largest becomes the new T and the keys are scanned again.
 #include "common.h"
 
 namespace lm {
 
 namespace {
 
-constexpr int kChunk = 4096;   // logits per block of the first pass
-constexpr int kSortT = 1024;   // threads per block of both passes
+constexpr int kT = 256;        // threads per block of both passes
+constexpr int kChunk = 8192;   // logits per block of the first pass (32 per thread)
+constexpr int kCap = 2048;     // keys the selection buffer holds
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
   uint32_t b = __float_as_uint(v);
@@ -58,39 +57,170 @@ __device__ __forceinline__ float uniform_draw(uint32_t seed, uint32_t n) {
   return (float)(lowbias32(lowbias32(seed) + n) >> 8) * 0x1p-24f;
 }
 
-// bitonic sort of s[0..n) (n a power of two) into descending order, starting from runs of size0/2
-// that are already sorted, alternately descending and ascending
-__device__ __forceinline__ void bitonic_desc(uint64_t *s, int n, int size0) {
-  for (int size = size0; size <= n; size <<= 1)
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// lanes below this one whose bit is set in m
+__device__ __forceinline__ int below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// bitonic sort, descending, of the 64*R keys of one wavefront (element r*64 + lane in a[r])
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[R]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * R; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 64) {
+        const int rs = stride >> 6;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & rs) continue;
+          const bool desc = ((r * 64 + lane) & size) == 0;
+          const uint64_t x = a[r], y = a[r | rs];
+          if ((x < y) == desc) {
+            a[r] = y;
+            a[r | rs] = x;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint64_t o = shfl_xor64(a[r], stride);
+          const bool desc = ((r * 64 + lane) & size) == 0;
+          const bool low = (lane & stride) == 0;
+          const bool keep_max = low == desc;
+          a[r] = keep_max ? (a[r] > o ? a[r] : o) : (a[r] < o ? a[r] : o);
+        }
+      }
+    }
+  }
+}
+
+// bitonic sort, descending, of s[0..n) (n a power of two) by the whole block
+__device__ __forceinline__ void lds_sort_desc(uint64_t *s, int n) {
+  for (int size = 2; size <= n; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       __syncthreads();
-      for (int i = threadIdx.x; i < (n >> 1); i += kSortT) {
+      for (int i = threadIdx.x; i < (n >> 1); i += kT) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
-        const uint64_t a = s[lo], b = s[hi];
+        const uint64_t x = s[lo], y = s[hi];
         const bool desc = (lo & size) == 0;
-        if ((a < b) == desc) {
-          s[lo] = b;
-          s[hi] = a;
+        if ((x < y) == desc) {
+          s[lo] = y;
+          s[hi] = x;
         }
       }
     }
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSortT) void k_topk_chunk(const float *logits, int64_t ld, int V, int K2,
-                                                      uint64_t *cand) {
-  __shared__ uint64_t s[kChunk];
+template <int R>
+__device__ __forceinline__ void wave0_sort(uint64_t *buf) {
+  uint64_t a[R];
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < R; ++r) a[r] = buf[r * 64 + lane];
+  wave_sort_desc<R>(a);
+#pragma unroll
+  for (int r = 0; r < R; ++r) buf[r * 64 + lane] = a[r];
+}
+
+struct SelectLds {
+  uint64_t buf[kCap];
+  uint64_t wt[kT / 64];
+  int count;
+};
+
+// The K2 largest of the block's keys (thread t holds key[j]; 0 = empty), sorted descending, into
+// L.buf[0..K2) (0 past the real keys).  Every thread of the block calls it.
+template <int NPT>
+__device__ void block_select(const uint64_t (&key)[NPT], int K2, SelectLds &L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t mx[1] = {0ull};
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) mx[0] = key[j] > mx[0] ? key[j] : mx[0];
+  wave_sort_desc<1>(mx);
+  const int m = (K2 + 3) / 4;
+  const uint64_t tw = readlane64(mx[0], m - 1);
+  if (lane == 0) L.wt[wave] = tw;
+  if (tid == 0) L.count = 0;
+  __syncthreads();
+  uint64_t T = L.wt[0];
+#pragma unroll
+  for (int w = 1; w < kT / 64; ++w) T = L.wt[w] < T ? L.wt[w] : T;
+  if (T == 0ull) T = 1ull;
+  int cnt;
+  for (;;) {
+    int total = 0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) total += __popcll(__ballot(key[j] >= T));
+    int base = 0;
+    if (lane == 0 && total) base = atomicAdd(&L.count, total);
+    base = __shfl(base, 0);
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const bool pass = key[j] >= T;
+      const uint64_t bm = __ballot(pass);
+      const int pos = base + below(bm);
+      if (pass && pos < kCap) L.buf[pos] = key[j];
+      base += __popcll(bm);
+    }
+    __syncthreads();
+    cnt = L.count;
+    if (cnt <= kCap) break;
+    // too many passed: the K2-th largest of those held is a higher bound with K2 keys at or above it
+    lds_sort_desc(L.buf, kCap);
+    T = L.buf[K2 - 1];
+    __syncthreads();
+    if (tid == 0) L.count = 0;
+    __syncthreads();
+  }
+  int n = 64;
+  while (n < cnt || n < K2) n <<= 1;
+  for (int i = cnt + tid; i < n; i += kT) L.buf[i] = 0ull;
+  __syncthreads();
+  if (n <= 256) {
+    if (wave == 0) {
+      if (n == 64)
+        wave0_sort<1>(L.buf);
+      else if (n == 128)
+        wave0_sort<2>(L.buf);
+      else
+        wave0_sort<4>(L.buf);
+    }
+    __syncthreads();
+  } else {
+    lds_sort_desc(L.buf, n);
+  }
+}
+
+__global__ __launch_bounds__(kT) void k_topk_chunk(const float *logits, int64_t ld, int V, int K2, uint64_t *cand) {
+  __shared__ SelectLds L;
   const int c = blockIdx.x, b = blockIdx.y, nchunk = gridDim.x;
   const float *row = logits + (int64_t)b * ld;
   const int base = c * kChunk;
-  for (int j = threadIdx.x; j < kChunk; j += kSortT) {
-    const int id = base + j;
-    s[j] = id < V ? cand_key(row[id], id) : 0ull;
+  uint64_t key[kChunk / kT];
+#pragma unroll
+  for (int j = 0; j < kChunk / kT; ++j) {
+    const int id = base + j * kT + (int)threadIdx.x;
+    key[j] = id < V ? cand_key(row[id], id) : 0ull;
   }
-  bitonic_desc(s, kChunk, 2);
+  block_select<kChunk / kT>(key, K2, L);
   uint64_t *out = cand + ((int64_t)b * nchunk + c) * K2;
-  for (int j = threadIdx.x; j < K2; j += kSortT) out[j] = s[j];
+  for (int j = threadIdx.x; j < K2; j += kT) out[j] = L.buf[j];
 }
 
 __device__ __forceinline__ float lane_of(const float (&r)[4], int j) {
@@ -115,23 +245,25 @@ __device__ __forceinline__ int first_set(const bool (&f)[4], int none) {
   return none;
 }
 
-template <int NMAX>
-__global__ __launch_bounds__(kSortT) void k_sample_rows(SampleArgs a) {
-  __shared__ uint64_t s[NMAX];
+template <int NPT>
+__global__ __launch_bounds__(kT) void k_sample_rows(SampleArgs a) {
+  __shared__ SelectLds L;
   const int b = blockIdx.x;
-  const int K2 = a.K2, n2 = a.n2;
-  const uint64_t *src = a.cand + (int64_t)b * a.nchunk * K2;
-  for (int j = threadIdx.x; j < n2; j += kSortT) {
-    const int c = j / K2, r = j - c * K2;
-    s[j] = c < a.nchunk ? src[(int64_t)c * K2 + ((c & 1) ? K2 - 1 - r : r)] : 0ull;
+  const int K2 = a.K2, total = a.nchunk * K2;
+  const uint64_t *src = a.cand + (int64_t)b * total;
+  uint64_t key[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i = j * kT + (int)threadIdx.x;
+    key[j] = i < total ? src[i] : 0ull;
   }
-  bitonic_desc(s, n2, 2 * K2);
+  block_select<NPT>(key, K2, L);
   if (threadIdx.x >= 64) return;
 
   const int lane = threadIdx.x;
   const int keff = a.k < a.V ? a.k : a.V;
   const float temp = a.temp;
-  const float top = from_order((uint32_t)(s[0] >> 32));
+  const float top = from_order((uint32_t)(L.buf[0] >> 32));
   float w[4], S[4];
   int id[4];
 #pragma unroll
@@ -141,7 +273,7 @@ __global__ __launch_bounds__(kSortT) void k_sample_rows(SampleArgs a) {
     S[q] = 0.f;
     id[q] = -1;
     if (j < keff) {
-      const uint64_t key = s[j];
+      const uint64_t key = L.buf[j];
       const float v = from_order((uint32_t)(key >> 32));
       id[q] = (int)(0xFFFFFFFFu - (uint32_t)key);
       const float qv = v / temp;
@@ -196,20 +328,14 @@ __global__ __launch_bounds__(kSortT) void k_sample_rows(SampleArgs a) {
 
 int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
-int sample_sort_size(int V, int K2) {
-  int n = 1;
-  while (n < sample_chunks(V) * K2) n <<= 1;
-  return n < K2 ? K2 : n;
-}
+int sample_candidates(int V, int K2) { return sample_chunks(V) * K2; }
 
 hipError_t launch_sample(const SampleArgs &a, int B, hipStream_t s) {
-  launch(k_topk_chunk, dim3(a.nchunk, B), dim3(kSortT), s, true, false, a.logits, a.ld, a.V, a.K2, a.cand);
-  if (a.n2 <= 1024)
-    launch(k_sample_rows<1024>, dim3(B), dim3(kSortT), s, false, true, a);
-  else if (a.n2 <= 4096)
-    launch(k_sample_rows<4096>, dim3(B), dim3(kSortT), s, false, true, a);
+  launch(k_topk_chunk, dim3(a.nchunk, B), dim3(kT), s, true, false, a.logits, a.ld, a.V, a.K2, a.cand);
+  if (a.nchunk * a.K2 <= 4 * kT)
+    launch(k_sample_rows<4>, dim3(B), dim3(kT), s, false, true, a);
   else
-    launch(k_sample_rows<kSampleSortMax>, dim3(B), dim3(kSortT), s, false, true, a);
+    launch(k_sample_rows<kSampleCandMax / kT>, dim3(B), dim3(kT), s, false, true, a);
   return hipGetLastError();
 }
 

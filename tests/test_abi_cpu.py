@@ -144,17 +144,17 @@ def test_sample_scratch_bytes_and_argument_checks(L):
     """Sampling's size query and its argument errors, all decided on the host (the fake device pointers
     are never dereferenced)."""
     V = 128256
-    # 32 chunks of 4096 logits, k = 50 rounds up to 64 candidates per chunk, 8-byte keys
-    assert L.llama_sample_scratch_bytes(3, V, 50) == 3 * 32 * 64 * 8
+    # 16 chunks of 8192 logits, k = 50 rounds up to 64 candidates per chunk, 8-byte keys
+    assert L.llama_sample_scratch_bytes(3, V, 50) == 3 * 16 * 64 * 8
     assert L.llama_sample_scratch_bytes(1, 1, 1) == 8
     assert L.llama_sample_scratch_bytes(0, V, 1) == 0
     assert L.llama_sample_scratch_bytes(-1, V, 1) == lm.E_SHAPE
     assert L.llama_sample_scratch_bytes(1, 0, 1) == lm.E_SHAPE
     assert L.llama_sample_scratch_bytes(1, V, 0) == lm.E_CONFIG
     assert L.llama_sample_scratch_bytes(1, V, 257) == lm.E_UNSUPPORTED
-    assert L.llama_sample_scratch_bytes(1, 262144, 256) == 64 * 256 * 8
+    assert L.llama_sample_scratch_bytes(1, 262144, 256) == 32 * 256 * 8
     assert L.llama_sample_scratch_bytes(1, 262145, 256) == lm.E_UNSUPPORTED
-    assert L.llama_sample_scratch_bytes(1, 524288, 128) == 128 * 128 * 8
+    assert L.llama_sample_scratch_bytes(1, 524288, 128) == 64 * 128 * 8
     fake = 1 << 40
     big = 1 << 30
 
@@ -175,6 +175,6 @@ def test_sample_scratch_bytes_and_argument_checks(L):
     assert smp(ids=None) == lm.E_NULL
     assert smp(seeds=None) == lm.E_NULL
     assert smp(scratch=None) == lm.E_NULL
-    assert smp(nbytes=32 * 64 * 8 - 1) == lm.E_WORKSPACE
+    assert smp(nbytes=16 * 64 * 8 - 1) == lm.E_WORKSPACE
     assert smp(scratch=fake + 4) == lm.E_WORKSPACE
     assert smp(B=0, logits=None, ids=None, scratch=None) == lm.OK
