@@ -8,16 +8,26 @@
 //
 //   k_topk_chunk   block (c, b): the 8192 logits of chunk c of row b, 32 keys per thread in
 //                  registers; their K2 largest (K2 = k rounded up to a power of two), sorted, out.
-//   k_sample_rows  block b: the nchunk lists of row b, the K2 largest of them, then one wavefront
-//                  does the draw.
+//   k_sample_rows  block b: the nchunk lists of row b, the K2 largest of them, then the draw.
 //
-// Selection of the K2 largest of a block's keys (block_select) sorts only what can be among them.
-// Each wavefront sorts its 64 per-thread maxima in registers and takes the m-th largest, m =
-// ceil(K2/4); T, the smallest of the four, has at least K2 keys at or above it (m distinct maxima in
-// each wavefront), so every key of the answer is >= T.  The keys >= T are appended to LDS (positions
-// from ballots, one LDS atomic per wavefront) and sorted: in registers by one wavefront when there
-// are at most 256, else by a bitonic network over LDS.  If more than the LDS buffer holds pass T (only
-// for adversarial orders), the buffer's K2-th largest becomes the new T and the keys are scanned again.
+// Selection of the K2 largest of a block's keys (block_select) looks closely only at what can be
+// among them.  Each thread takes the maxima of G disjoint groups of its keys (G = 1, 2, 4 as K2 <= 64,
+// 128, 256); each wavefront finds (a lower bound on) the m-th largest of its 64*G maxima, m =
+// ceil(K2/4), by a bitwise search with ballots; T, the smallest of the four, has at least K2 keys at
+// or above it (m distinct maxima in each wavefront), so every key of the answer is >= T.  The keys >= T are appended to LDS
+// (offsets from a wavefront prefix sum built from ballots of the count bits, one LDS atomic per
+// wavefront) and each finds its rank by counting the held keys above it (LDS broadcast reads); ranks
+// below K2 are the sorted answer.  More than 1024 survivors go through a bitonic network over LDS
+// instead, and if more than the buffer holds pass T (adversarial orders only), the buffer's K2-th
+// largest becomes the new T and the keys are scanned again.
+//
+// The draw keeps the page's F32 order: each candidate's weight exp(v/temp − top/temp) (the
+// exponential computed in double and rounded once, i.e. the correctly rounded F32 value), one
+// running sum from 0 in candidate order (one thread; the others wait), Z = the last running sum,
+// lim = p*Z, kept = the candidates up to the first one after which the running sum is not below lim,
+// z = the running sum of the last kept one, target = u*z, and the draw is the first kept candidate
+// whose running sum is above target, or the last kept one.  Every partial sum the page forms (total,
+// kept.go, pick.go) is one of these running sums, so the comparisons see the same F32 values.
 #include "common.h"
 
 namespace lm {
@@ -74,38 +84,45 @@ __device__ __forceinline__ int below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// bitonic sort, descending, of the 64*R keys of one wavefront (element r*64 + lane in a[r])
+// the m-th largest (m >= 1) of the keys v[0..R) of the wavefront's 64 lanes (distinct keys, 0 = empty;
+// 0 when fewer than m are nonzero): the largest x with at least m keys >= x, built from the top bit.
+// The high words (the logits) are searched first; the low words (the ids) only when more than a few
+// keys share the high word found, so for logits without ties the result is x with a zero low word,
+// still a bound with at least m keys at or above it.
 template <int R>
-__device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[R]) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ uint64_t wave_mth_largest(const uint64_t (&v)[R], int m) {
+  uint32_t hi[R], lo[R];
 #pragma unroll
-  for (int size = 2; size <= 64 * R; size <<= 1) {
+  for (int r = 0; r < R; ++r) {
+    hi[r] = (uint32_t)(v[r] >> 32);
+    lo[r] = (uint32_t)v[r];
+  }
+  uint32_t xh = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = xh | (1u << bit);
+    int n = 0;
 #pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 64) {
-        const int rs = stride >> 6;
+    for (int r = 0; r < R; ++r) n += __popcll(__ballot(hi[r] >= c));
+    if (n >= m) xh = c;
+  }
+  int above = 0, equal = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r & rs) continue;
-          const bool desc = ((r * 64 + lane) & size) == 0;
-          const uint64_t x = a[r], y = a[r | rs];
-          if ((x < y) == desc) {
-            a[r] = y;
-            a[r | rs] = x;
-          }
-        }
-      } else {
+  for (int r = 0; r < R; ++r) {
+    above += __popcll(__ballot(hi[r] > xh));
+    equal += __popcll(__ballot(hi[r] == xh));
+  }
+  uint32_t xl = 0;
+  if (equal > 4) {
+    const int need = m - above;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = xl | (1u << bit);
+      int n = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint64_t o = shfl_xor64(a[r], stride);
-          const bool desc = ((r * 64 + lane) & size) == 0;
-          const bool low = (lane & stride) == 0;
-          const bool keep_max = low == desc;
-          a[r] = keep_max ? (a[r] > o ? a[r] : o) : (a[r] < o ? a[r] : o);
-        }
-      }
+      for (int r = 0; r < R; ++r) n += __popcll(__ballot(hi[r] == xh && lo[r] >= c));
+      if (n >= need) xl = c;
     }
   }
+  return ((uint64_t)xh << 32) | xl;
 }
 
 // bitonic sort, descending, of s[0..n) (n a power of two) by the whole block
@@ -127,57 +144,75 @@ __device__ __forceinline__ void lds_sort_desc(uint64_t *s, int n) {
   __syncthreads();
 }
 
-template <int R>
-__device__ __forceinline__ void wave0_sort(uint64_t *buf) {
-  uint64_t a[R];
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int r = 0; r < R; ++r) a[r] = buf[r * 64 + lane];
-  wave_sort_desc<R>(a);
-#pragma unroll
-  for (int r = 0; r < R; ++r) buf[r * 64 + lane] = a[r];
-}
+constexpr int kRankMax = 1024;  // survivors ranked by counting; more are sorted by the network
 
 struct SelectLds {
   uint64_t buf[kCap];
   uint64_t wt[kT / 64];
+  unsigned long long tmin;
   int count;
 };
 
-// The K2 largest of the block's keys (thread t holds key[j]; 0 = empty), sorted descending, into
-// L.buf[0..K2) (0 past the real keys).  Every thread of the block calls it.
-template <int NPT>
-__device__ void block_select(const uint64_t (&key)[NPT], int K2, SelectLds &L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t mx[1] = {0ull};
+template <int G, int NPT>
+__device__ __forceinline__ uint64_t wave_threshold(const uint64_t (&key)[NPT], int m) {
+  uint64_t mx[G];
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) mx[0] = key[j] > mx[0] ? key[j] : mx[0];
-  wave_sort_desc<1>(mx);
+  for (int g = 0; g < G; ++g) mx[g] = 0ull;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) mx[j % G] = key[j] > mx[j % G] ? key[j] : mx[j % G];
+  return wave_mth_largest<G>(mx, m);
+}
+
+// A lower bound T >= 1 on the K2-th largest of the block's keys (thread t holds key[j]; 0 = empty):
+// the smallest over the wavefronts of the m-th largest of their group maxima (at least K2 keys are
+// >= T), or 1 when there are fewer nonzero keys than that finds.  Ends with a barrier.
+template <int NPT>
+__device__ uint64_t maxima_threshold(const uint64_t (&key)[NPT], int K2, SelectLds &L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = (K2 + 3) / 4;
-  const uint64_t tw = readlane64(mx[0], m - 1);
+  const uint64_t tw = K2 <= 64 ? wave_threshold<1>(key, m)
+                               : K2 <= 128 ? wave_threshold<2>(key, m) : wave_threshold<4>(key, m);
   if (lane == 0) L.wt[wave] = tw;
-  if (tid == 0) L.count = 0;
   __syncthreads();
   uint64_t T = L.wt[0];
 #pragma unroll
   for (int w = 1; w < kT / 64; ++w) T = L.wt[w] < T ? L.wt[w] : T;
-  if (T == 0ull) T = 1ull;
+  return T == 0ull ? 1ull : T;
+}
+
+// The K2 largest of the block's keys (thread t holds key[j]; 0 = empty), sorted descending, into
+// dst[0..K2) (0 past the real keys), given T >= 1 with at least K2 keys >= T or every nonzero key >= T;
+// dst may be global or LDS memory.  Every thread of the block calls it with the same T; it ends with a
+// barrier.
+template <int NPT>
+__device__ void block_select(const uint64_t (&key)[NPT], uint64_t T, int K2, SelectLds &L, uint64_t *dst) {
+  static_assert(NPT <= 32, "pass masks are 32 bits");
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) L.count = 0;
+  __syncthreads();
   int cnt;
   for (;;) {
-    int total = 0;
+    uint32_t pm = 0;
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) total += __popcll(__ballot(key[j] >= T));
-    int base = 0;
-    if (lane == 0 && total) base = atomicAdd(&L.count, total);
-    base = __shfl(base, 0);
+    for (int j = 0; j < NPT; ++j) pm |= (key[j] >= T ? 1u : 0u) << j;
+    const int c = __popc(pm);
+    // exclusive prefix and total of c over the wavefront, one ballot per bit of c (c <= 32)
+    int off = 0, tot = 0;
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      const bool pass = key[j] >= T;
-      const uint64_t bm = __ballot(pass);
-      const int pos = base + below(bm);
-      if (pass && pos < kCap) L.buf[pos] = key[j];
-      base += __popcll(bm);
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t bm = __ballot((c >> bit) & 1);
+      off += below(bm) << bit;
+      tot += __popcll(bm) << bit;
     }
+    int base = 0;
+    if (lane == 0 && tot) base = atomicAdd(&L.count, tot);
+    int pos = __shfl(base, 0) + off;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j)
+      if ((pm >> j) & 1u) {
+        if (pos < kCap) L.buf[pos] = key[j];
+        ++pos;
+      }
     __syncthreads();
     cnt = L.count;
     if (cnt <= kCap) break;
@@ -188,23 +223,30 @@ __device__ void block_select(const uint64_t (&key)[NPT], int K2, SelectLds &L) {
     if (tid == 0) L.count = 0;
     __syncthreads();
   }
-  int n = 64;
-  while (n < cnt || n < K2) n <<= 1;
-  for (int i = cnt + tid; i < n; i += kT) L.buf[i] = 0ull;
-  __syncthreads();
-  if (n <= 256) {
-    if (wave == 0) {
-      if (n == 64)
-        wave0_sort<1>(L.buf);
-      else if (n == 128)
-        wave0_sort<2>(L.buf);
-      else
-        wave0_sort<4>(L.buf);
-    }
+  if (cnt <= kRankMax) {
+    const int c8 = (cnt + 7) & ~7;
+    if (tid < c8 - cnt) L.buf[cnt + tid] = 0ull;
     __syncthreads();
+    const ulonglong2 *b2 = reinterpret_cast<const ulonglong2 *>(L.buf);
+    for (int i = tid; i < cnt; i += kT) {
+      const uint64_t me = L.buf[i];
+      int r = 0;
+      for (int j = 0; j < c8 / 2; j += 4) {
+        const ulonglong2 p0 = b2[j], p1 = b2[j + 1], p2 = b2[j + 2], p3 = b2[j + 3];
+        r += (p0.x > me) + (p0.y > me) + (p1.x > me) + (p1.y > me) + (p2.x > me) + (p2.y > me) + (p3.x > me) +
+             (p3.y > me);
+      }
+      if (r < K2) dst[r] = me;
+    }
+    for (int i = cnt + tid; i < K2; i += kT) dst[i] = 0ull;
   } else {
+    int n = 1;
+    while (n < cnt) n <<= 1;
+    for (int i = cnt + tid; i < n; i += kT) L.buf[i] = 0ull;
     lds_sort_desc(L.buf, n);
+    for (int i = tid; i < K2; i += kT) dst[i] = L.buf[i];
   }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kT) void k_topk_chunk(const float *logits, int64_t ld, int V, int K2, uint64_t *cand) {
@@ -215,12 +257,13 @@ __global__ __launch_bounds__(kT) void k_topk_chunk(const float *logits, int64_t 
   uint64_t key[kChunk / kT];
 #pragma unroll
   for (int j = 0; j < kChunk / kT; ++j) {
+    // branch-free, so every load is issued before any is used (the index is clamped into the row)
     const int id = base + j * kT + (int)threadIdx.x;
-    key[j] = id < V ? cand_key(row[id], id) : 0ull;
+    const float v = row[id < V ? id : V - 1];
+    key[j] = cand_key(v, id) & (0ull - (uint64_t)(id < V));
   }
-  block_select<kChunk / kT>(key, K2, L);
-  uint64_t *out = cand + ((int64_t)b * nchunk + c) * K2;
-  for (int j = threadIdx.x; j < K2; j += kT) out[j] = L.buf[j];
+  const uint64_t T = maxima_threshold<kChunk / kT>(key, K2, L);
+  block_select<kChunk / kT>(key, T, K2, L, cand + ((int64_t)b * nchunk + c) * K2);
 }
 
 __device__ __forceinline__ float lane_of(const float (&r)[4], int j) {
@@ -248,50 +291,78 @@ __device__ __forceinline__ int first_set(const bool (&f)[4], int none) {
 template <int NPT>
 __global__ __launch_bounds__(kT) void k_sample_rows(SampleArgs a) {
   __shared__ SelectLds L;
-  const int b = blockIdx.x;
+  __shared__ uint64_t top[kSampleMaxK];
+  __shared__ float wv[kSampleMaxK], Sv[kSampleMaxK];
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int K2 = a.K2, total = a.nchunk * K2;
   const uint64_t *src = a.cand + (int64_t)b * total;
   uint64_t key[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const int i = j * kT + (int)threadIdx.x;
-    key[j] = i < total ? src[i] : 0ull;
+    const int i = j * kT + tid;
+    key[j] = src[i < total ? i : total - 1] & (0ull - (uint64_t)(i < total));
   }
-  block_select<NPT>(key, K2, L);
-  if (threadIdx.x >= 64) return;
+  // each list is sorted, so q = ceil(K2 / nl) entries of each of nl lists are >= the smallest of their
+  // q-th entries: T.  A last chunk holding fewer than q logits is left out of the bound.
+  int nl = a.nchunk, q = (K2 + nl - 1) / nl;
+  if (nl > 1 && a.V - (nl - 1) * kChunk < q) {
+    nl -= 1;
+    q = (K2 + nl - 1) / nl;
+  }
+  if (tid == 0) L.tmin = ~0ull;
+  __syncthreads();
+  uint64_t tl = ~0ull;
+  for (int c = tid; c < nl; c += kT) {
+    const uint64_t e = src[(int64_t)c * K2 + q - 1];
+    tl = e < tl ? e : tl;
+  }
+  if (tl != ~0ull) atomicMin(&L.tmin, (unsigned long long)tl);
+  __syncthreads();
+  const uint64_t T = L.tmin;
+  block_select<NPT>(key, T == 0ull ? 1ull : T, K2, L, top);
 
-  const int lane = threadIdx.x;
   const int keff = a.k < a.V ? a.k : a.V;
   const float temp = a.temp;
-  const float top = from_order((uint32_t)(L.buf[0] >> 32));
-  float w[4], S[4];
+  const float topv = from_order((uint32_t)(top[0] >> 32));
+  if (tid < kSampleMaxK) {
+    float w = 0.f;
+    if (tid < keff) {
+      const float v = from_order((uint32_t)(top[tid] >> 32));
+      const float qv = v / temp;
+      const float qt = topv / temp;
+      const float d = qv - qt;
+      w = (float)exp((double)d);
+    }
+    wv[tid] = w;
+  }
+  __syncthreads();
+  // running sums in candidate order, one after another (adding the zero weights past keff changes no
+  // sum that is used)
+  if (tid == 0) {
+    float acc = 0.f;
+    const float4 *w4 = reinterpret_cast<const float4 *>(wv);
+    for (int j = 0; j < keff; j += 4) {
+      const float4 q = w4[j >> 2];
+      const float s0 = acc + q.x;
+      const float s1 = s0 + q.y;
+      const float s2 = s1 + q.z;
+      const float s3 = s2 + q.w;
+      *reinterpret_cast<float4 *>(Sv + j) = make_float4(s0, s1, s2, s3);
+      acc = s3;
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
+  float S[4];
   int id[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int j = 64 * q + lane;
-    w[q] = 0.f;
-    S[q] = 0.f;
-    id[q] = -1;
-    if (j < keff) {
-      const uint64_t key = L.buf[j];
-      const float v = from_order((uint32_t)(key >> 32));
-      id[q] = (int)(0xFFFFFFFFu - (uint32_t)key);
-      const float qv = v / temp;
-      const float qt = top / temp;
-      const float d = qv - qt;
-      w[q] = (float)exp((double)d);
-    }
+    S[q] = Sv[j];
+    id[q] = j < keff ? (int)(0xFFFFFFFFu - (uint32_t)top[j]) : -1;
   }
-  // running sums in candidate order; lane l of group q keeps the one that ends at candidate 64q+l
-  float acc = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int n = keff - 64 * q < 64 ? keff - 64 * q : 64;
-    for (int l = 0; l < n; ++l) {
-      acc = acc + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[q]), l));
-      if (lane == l) S[q] = acc;
-    }
-  }
+  const float acc = Sv[keff - 1];
   const float Z = acc;
   const float lim = a.p * Z;
   bool f[4];

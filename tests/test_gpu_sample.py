@@ -5,7 +5,7 @@ the same precision and order (weights from the correctly rounded exponential, on
 candidate order, the page's strict comparisons), so the drawn ids, their logits and the top-k lists
 must be identical, element by element.  Logits are seeded and synthetic: normal rows with the scale of
 an LM head's output and a few outliers, rows with heavy ties (few distinct values, both zeros), rows of
-one value.  Sizes: the 128256-token vocabulary at 1, 4 and 64 rows, ragged chunk edges, the largest
+one value, and two patterns that push the kernels' candidate bound onto its slow paths.  Sizes: the 128256-token vocabulary at 1, 4 and 64 rows, ragged chunk edges, the largest
 vocabulary allowed for k = 256, strided rows, k above V.
 """
 import numpy as np
@@ -34,6 +34,19 @@ def _logits(rng, B, V, kind):
         return x
     if kind == "flat":
         return np.full((B, V), 0.37, dtype=F32)
+    # the two below defeat the kernel's first-pass bound (per-wavefront maxima of threads that take
+    # every 256th logit): in "lopsided" three of four wavefronts see only large values, so far more
+    # keys pass the bound than its buffer holds and the bound is raised; in "sparse" 1152 of every
+    # 8192 logits are large, so the survivors are sorted by the bitonic network
+    t = np.arange(V) % 256
+    if kind == "lopsided":
+        x = rng.standard_normal((B, V)).astype(F32)
+        x[:, t < 192] += F32(100.0)
+        return x
+    if kind == "sparse":
+        x = rng.standard_normal((B, V)).astype(F32)
+        x[:, (t < 192) & (t % 64 < 12)] += F32(100.0)
+        return x
     raise ValueError(kind)
 
 
@@ -85,6 +98,10 @@ CASES = [
     (2, 262144, "normal", 0.9, 256, 0.99),
     (3, 1000, "flat", 0.8, 64, 0.5),
     (2, 100, "normal", 2.0, 256, 1.0),
+    (2, 128256, "lopsided", 1.0, 256, 0.9),
+    (2, 128256, "sparse", 1.0, 200, 0.9),
+    (2, 128256, "lopsided", 1.0, 100, 0.9),
+    (2, 128256, "sparse", 1.0, 64, 0.9),
 ]
 
 
