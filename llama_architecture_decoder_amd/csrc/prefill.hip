@@ -30,11 +30,14 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // 32 through double-buffered LDS.  Wave (wm, wn) owns 64 x 128 of the block as 2 x 4 tiles of 32 x 32, so
 // each k step reads 2 (x hi, lo) A fragments and 4 B fragments from LDS for 16 MFMAs: the LDS traffic per
 // MFMA (reads + the staging writes) stays well under what the LDS delivers while the matrix cores run.
+// Two blocks share a CU (80 KB of LDS each, at most 256 registers per lane), so one block's matrix work
+// covers the other's wait for its next tiles: measured 7% faster over the 4096-position prefill than one
+// block per CU with more registers.
 constexpr int kTM = 128, kTN = 256, kTK = 32;
 constexpr int kRowA = kTK + 8;  // LDS row of a tile: 40 bf16 = 80 bytes (16-byte reads of 16 rows hit distinct banks)
 
 template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_tiled(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
   constexpr int AC = 2 * kTM * (kTK / 8) / kThreads;  // 16-byte chunks of A (hi and lo) per thread per stage
   constexpr int BC = kTN * (kTK / 8) / kThreads;      // of B
