@@ -50,8 +50,9 @@ enum {
   LLAMA_E_NULL = -5,        /* a required pointer is NULL */
   LLAMA_E_WORKSPACE = -6,   /* workspace too small, not initialised, or initialised for another config */
   LLAMA_E_HIP = -7,         /* a HIP runtime call or launch failed */
-  LLAMA_E_UNSUPPORTED = -8  /* valid but not built: head not in {64,128}, g not in {1,2,3,4,8}, dim or f not a
+  LLAMA_E_UNSUPPORTED = -8, /* valid but not built: head not in {64,128}, g not in {1,2,3,4,8}, dim or f not a
                                multiple of 8 or too wide, max_seq > 131072 */
+  LLAMA_E_PAGE = -9         /* a page table entry outside the pool (sticky device flag, see llama_status) */
 };
 
 /*
@@ -172,6 +173,30 @@ int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv
                   int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream);
 
 /*
+ * Paged cache (nest card `decode_paged` / `prefill_paged`: with one cache row, that row is a pool of
+ * positions in pages of 64, and request b's positions lie in the pages its table row lists).  Cache row 0
+ * of `kv` is the pool: kv->max_seq pool positions (a multiple of 64), npool = kv->max_seq / 64 pages, the
+ * same page numbering in every layer and kv head.  Position p of a request with table row T (device
+ * int32 [pages]) lives at pool position T[p / 64] * 64 + p % 64.  The table is read on the device: an
+ * entry outside [0, npool) writes no key or value, reads page 0 instead, and sets the sticky status
+ * (llama_status returns LLAMA_E_PAGE); the caller keeps the entries a step reaches valid.  Pages may be
+ * shared by requests for reading (a common prefix); two requests writing one slot in one call race.
+ * Needs a bf16 cache and the matrix-core attention (head 64 or 128 with its g; else E_UNSUPPORTED).
+ *
+ * llama_decode_step_paged: as llama_decode_step for B <= 64 requests, request b's table row at
+ * table + b * pages (device int32 [B][pages]), its token at pos_host[b] < pages * 64 (E_POS beyond) and
+ * below the workspace's max_seq; B is bounded by the workspace's max_batch, not by kv->rows.
+ * llama_prefill_paged: as llama_prefill for one request whose table row is `table` [pages]
+ * (pos0 + S <= pages * 64).
+ */
+int llama_decode_step_paged(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                            const int32_t *pos_host, int32_t B, const int32_t *table, int32_t pages, float *logits,
+                            int32_t *next, const llama_ws *ws, void *stream);
+int llama_prefill_paged(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *table,
+                        int32_t pages, const int32_t *tokens, int32_t S, int32_t pos0, float *logits_last,
+                        int32_t *next, const llama_ws *ws, void *stream);
+
+/*
  * Final RMSNorm + LM head + argmax of B hidden states (device F32 [B][dim], the last layer's output
  * before the final norm): main.bend head_of and argmax.  logits [B][vocab] optional, argmax [B] required.
  */
@@ -219,7 +244,8 @@ enum {
 int llama_profile_enable(int on);
 int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms);
 
-/* Synchronise `stream` and return the sticky device-side status (LLAMA_OK or LLAMA_E_TOKEN), then clear it. */
+/* Synchronise `stream` and return the sticky device-side status (LLAMA_OK, LLAMA_E_TOKEN, or LLAMA_E_PAGE when
+ * no token was out of range), then clear it. */
 int llama_status(const llama_ws *ws, void *stream);
 
 /* Static description of a return code. */

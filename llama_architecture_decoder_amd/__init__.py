@@ -19,9 +19,10 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "llama_mi355x.h")
 
 F32, BF16 = 0, 1
 OK = 0
-E_CONFIG, E_POS, E_TOKEN, E_SHAPE, E_NULL, E_WORKSPACE, E_HIP, E_UNSUPPORTED = -1, -2, -3, -4, -5, -6, -7, -8
+E_CONFIG, E_POS, E_TOKEN, E_SHAPE, E_NULL, E_WORKSPACE, E_HIP, E_UNSUPPORTED, E_PAGE = -1, -2, -3, -4, -5, -6, -7, -8, -9
 ERROR_NAMES = {0: "OK", -1: "E_CONFIG", -2: "E_POS", -3: "E_TOKEN", -4: "E_SHAPE", -5: "E_NULL",
-               -6: "E_WORKSPACE", -7: "E_HIP", -8: "E_UNSUPPORTED"}
+               -6: "E_WORKSPACE", -7: "E_HIP", -8: "E_UNSUPPORTED", -9: "E_PAGE"}
+PAGE_SIZE = 64
 
 
 class LlamaError(RuntimeError):
@@ -90,6 +91,8 @@ def lib():
     L.llama_decode_step_traced.argtypes = [pc, pw, pk, vp, ctypes.POINTER(i32), vp, vp, ps, vp, i64, vp]
     L.llama_prefill.argtypes = [pc, pw, pk, i32, vp, i32, i32, vp, vp, ps, vp]
     L.lm_head_argmax.argtypes = [pc, pw, vp, i32, vp, vp, ps, vp]
+    L.llama_decode_step_paged.argtypes = [pc, pw, pk, vp, ctypes.POINTER(i32), i32, vp, i32, vp, vp, ps, vp]
+    L.llama_prefill_paged.argtypes = [pc, pw, pk, vp, i32, vp, i32, i32, vp, vp, ps, vp]
     L.llama_status.argtypes = [ps, vp]
     L.llama_sample_scratch_bytes.argtypes = [i32, i32, i32]
     L.llama_sample_scratch_bytes.restype = i64
@@ -214,13 +217,17 @@ class Decoder:
     """One model on one GPU: weights, a cache of `rows` rows and a workspace, with the C ABI's calls."""
 
     def __init__(self, cfg, host_weights: Dict[str, object], rows: int = 1, max_seq: Optional[int] = None,
-                 max_prefill: int = 0, device="cuda", weights: Optional[DeviceWeights] = None):
+                 max_prefill: int = 0, device="cuda", weights: Optional[DeviceWeights] = None,
+                 ws_rows: Optional[int] = None, ws_seq: Optional[int] = None):
+        """rows x max_seq: the cache (for a paged cache: rows=1 and max_seq = pool positions); ws_rows and
+        ws_seq size the workspace (default: the cache's), e.g. requests per step and their longest
+        position + 1 over a page pool."""
         self.cfg = cfg
         self.c = make_cfg(cfg)
         self.max_seq = max_seq or cfg.max_seq
         self.w = weights if weights is not None else DeviceWeights(cfg, host_weights, device)
         self.kv = KVCache(cfg, rows, self.max_seq, device)
-        self.ws = Workspace(cfg, rows, self.max_seq, max_prefill, device)
+        self.ws = Workspace(cfg, ws_rows or rows, ws_seq or self.max_seq, max_prefill, device)
         self.device = device
 
     # --- calls -----------------------------------------------------------------------------
@@ -267,6 +274,25 @@ class Decoder:
                                  tokens.data_ptr(), int(tokens.numel()), pos0, _ptr(logits), _ptr(next_tok),
                                  ctypes.byref(self.ws.rec), _stream_handle(stream))
         _check(rc, "llama_prefill")
+
+    def decode_paged(self, tokens, pos: Sequence[int], table, logits=None, next_tok=None, stream=None) -> None:
+        """A step of B requests in a paged cache: cache row 0 is the page pool, request b's positions lie
+        in the pages of table[b] (device int32 [B][pages])."""
+        B = len(pos)
+        parr = (ctypes.c_int32 * B)(*[int(p) for p in pos])
+        rc = lib().llama_decode_step_paged(ctypes.byref(self.c), ctypes.byref(self.w.rec), ctypes.byref(self.kv.rec),
+                                           tokens.data_ptr(), parr, B, table.data_ptr(), int(table.shape[-1]),
+                                           _ptr(logits), _ptr(next_tok), ctypes.byref(self.ws.rec),
+                                           _stream_handle(stream))
+        _check(rc, "llama_decode_step_paged")
+
+    def prefill_paged(self, tokens, table_row, pos0: int = 0, logits=None, next_tok=None, stream=None) -> None:
+        """One request's prompt into the page pool, its pages listed in table_row (device int32 [pages])."""
+        rc = lib().llama_prefill_paged(ctypes.byref(self.c), ctypes.byref(self.w.rec), ctypes.byref(self.kv.rec),
+                                       table_row.data_ptr(), int(table_row.shape[-1]), tokens.data_ptr(),
+                                       int(tokens.numel()), pos0, _ptr(logits), _ptr(next_tok),
+                                       ctypes.byref(self.ws.rec), _stream_handle(stream))
+        _check(rc, "llama_prefill_paged")
 
     def lm_head_argmax(self, hidden, logits=None, argmax=None, stream=None):
         B = hidden.shape[0]

@@ -322,6 +322,9 @@ struct Ctx {
   WsLayout L;
   hipStream_t s;
   char *base;
+  // paged cache (decode: table [B][pages]; prefill: one row's table [pages]); row 0 of kv is the pool
+  const int32_t *table = nullptr;
+  int pages = 0, npages = 0;
   template <typename T>
   T *at(size_t off) const {
     return reinterpret_cast<T *>(base + off);
@@ -537,7 +540,10 @@ int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int r
   pa.heads = (int)(d.kv * d.g);
   pa.half = (int)d.half;
   pa.max_seq = x.kv->max_seq;
-  pa.row = row;
+  pa.row = x.table ? 0 : row;
+  pa.table = x.table;
+  pa.npages = x.npages;
+  pa.status = x.at<int>(x.L.status);
   pa.pos0 = pos0;
   pa.S = S;
   pa.rope_cs = x.at<float>(x.L.rope_cs);
@@ -607,6 +613,10 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   aa.max_seq = x.kv->max_seq;
   aa.half = (int)d.half;
   aa.row0 = row0;
+  aa.table = x.table;
+  aa.pages = x.pages;
+  aa.npages = x.npages;
+  aa.status = x.at<int>(x.L.status);
   aa.out = att;
   aa.out_stride = H;
   aa.part_o = x.at<float>(x.L.part_o);
@@ -626,6 +636,10 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   ra.dim = H;
   ra.kvw = KW;
   ra.row0 = row0;
+  ra.table = x.table;
+  ra.pages = x.pages;
+  ra.npages = x.npages;
+  ra.status = x.at<int>(x.L.status);
   ra.rope_cs = x.at<float>(x.L.rope_cs);
   ra.rope_sn = x.at<float>(x.L.rope_sn);
   for (int b = 0; b < B; ++b) ra.pos[b] = pos[b];
@@ -643,6 +657,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.ra = ra;
       a.ra.qrot = ra.qrot + (size_t)b * H;
       a.ra.row0 = row0 + b;
+      if (x.table) a.ra.table = x.table + (size_t)b * x.pages;  // the GEMV's one token row is row b
       a.ra.pos[0] = pos[b];
       a.x = xs + (size_t)b * H;
       a.gain = lw.ln1;
@@ -767,6 +782,7 @@ const char *llama_strerror(int code) {
     case LLAMA_E_WORKSPACE: return "workspace too small or not initialised for this config";
     case LLAMA_E_HIP: return "HIP runtime error";
     case LLAMA_E_UNSUPPORTED: return "not supported by this build";
+    case LLAMA_E_PAGE: return "a page table entry outside the cache's page pool";
     default: return "unknown error";
   }
 }
@@ -889,21 +905,14 @@ int llama_decode_step_traced(const llama_cfg *c, const llama_weights *w, const l
   return decode_common(c, w, kv, tokens, pos_host, 1, logits, next, ws, stream, trace);
 }
 
-int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, int32_t row, const int32_t *tokens,
-                  int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream) {
-  if (!kv || !tokens || !w || !ws) return LLAMA_E_NULL;
-  int rc = check_cfg(c);
-  if (rc) return rc;
-  if ((rc = check_kv(c, kv))) return rc;
-  if (S <= 0 || row < 0 || row >= kv->rows) return LLAMA_E_SHAPE;
-  if (pos0 < 0 || (int64_t)pos0 + S > kv->max_seq) return LLAMA_E_POS;
-  Ctx x;
-  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
-  if ((int64_t)pos0 + S > ws->max_seq) return LLAMA_E_POS;
-  if (prefill_tiled_ok(c) && ws->max_prefill >= 2 && S >= 2) {
+// the prompt of one cache row (or of one paged row when x.table is set) after the argument checks
+static int prefill_common(const Ctx &x, const int32_t *tokens, int32_t S, int32_t pos0, int32_t row,
+                          float *logits_last, int32_t *next) {
+  int rc;
+  if (prefill_tiled_ok(x.c) && x.ws->max_prefill >= 2 && S >= 2) {
     // chunks of at most max_prefill positions, each attending to everything before it in the cache
-    for (int32_t c0 = 0; c0 < S; c0 += ws->max_prefill) {
-      const int32_t n = S - c0 < ws->max_prefill ? S - c0 : ws->max_prefill;
+    for (int32_t c0 = 0; c0 < S; c0 += x.ws->max_prefill) {
+      const int32_t n = S - c0 < x.ws->max_prefill ? S - c0 : x.ws->max_prefill;
       const bool last = c0 + n == S;
       rc = run_prefill_rows(x, tokens + c0, n, pos0 + c0, row, last ? logits_last : nullptr, last ? next : nullptr,
                             last);
@@ -920,6 +929,71 @@ int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv
     if (rc) return rc;
   }
   return LLAMA_OK;
+}
+
+int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, int32_t row, const int32_t *tokens,
+                  int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream) {
+  if (!kv || !tokens || !w || !ws) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if (S <= 0 || row < 0 || row >= kv->rows) return LLAMA_E_SHAPE;
+  if (pos0 < 0 || (int64_t)pos0 + S > kv->max_seq) return LLAMA_E_POS;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if ((int64_t)pos0 + S > ws->max_seq) return LLAMA_E_POS;
+  return prefill_common(x, tokens, S, pos0, row, logits_last, next);
+}
+
+// paged cache checks: a table, whole pages in the pool, and the matrix-core attention (a wavefront's
+// positions, and a prefill key tile, are one page)
+static int check_paging(const llama_cfg *c, const llama_kv *kv, const int32_t *table, int32_t pages) {
+  if (!table) return LLAMA_E_NULL;
+  if (pages < 1 || kv->max_seq % kPageSize != 0) return LLAMA_E_SHAPE;
+  if (!attention_paged_supported(c->kv_dtype, 2 * c->half, c->g)) return LLAMA_E_UNSUPPORTED;
+  return LLAMA_OK;
+}
+
+int llama_decode_step_paged(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *tokens,
+                            const int32_t *pos_host, int32_t B, const int32_t *table, int32_t pages, float *logits,
+                            int32_t *next, const llama_ws *ws, void *stream) {
+  if (!kv || !tokens || !pos_host || !w || !ws) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if ((rc = check_paging(c, kv, table, pages))) return rc;
+  if (B <= 0 || B > kMaxBatch) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos_host[b] < 0 || (int64_t)pos_host[b] >= (int64_t)pages * kPageSize) return LLAMA_E_POS;
+  if (logits && ((uintptr_t)logits & 3u)) return LLAMA_E_SHAPE;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if (B > ws->max_batch) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos_host[b] >= ws->max_seq) return LLAMA_E_POS;
+  x.table = table;
+  x.pages = pages;
+  x.npages = kv->max_seq / kPageSize;
+  return run_step(x, tokens, pos_host, B, 0, logits, next, true, nullptr);
+}
+
+int llama_prefill_paged(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *table,
+                        int32_t pages, const int32_t *tokens, int32_t S, int32_t pos0, float *logits_last,
+                        int32_t *next, const llama_ws *ws, void *stream) {
+  if (!kv || !tokens || !w || !ws) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if ((rc = check_paging(c, kv, table, pages))) return rc;
+  if (S <= 0) return LLAMA_E_SHAPE;
+  if (pos0 < 0 || (int64_t)pos0 + S > (int64_t)pages * kPageSize) return LLAMA_E_POS;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if ((int64_t)pos0 + S > ws->max_seq) return LLAMA_E_POS;
+  x.table = table;
+  x.pages = pages;
+  x.npages = kv->max_seq / kPageSize;
+  return prefill_common(x, tokens, S, pos0, 0, logits_last, next);
 }
 
 int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidden, int32_t B, float *logits,
@@ -1021,7 +1095,7 @@ int llama_status(const llama_ws *ws, void *stream) {
   if (hipMemcpy(&flag, ws->base, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LLAMA_E_HIP;
   if (flag) {
     if (launch_zero(ws->base, 64, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) return LLAMA_E_HIP;
-    return LLAMA_E_TOKEN;
+    return (flag & 1) ? LLAMA_E_TOKEN : LLAMA_E_PAGE;
   }
   return LLAMA_OK;
 }

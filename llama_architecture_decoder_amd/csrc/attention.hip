@@ -22,6 +22,8 @@
 // staged once per block in LDS.  Each wavefront keeps its scores in registers and forms its own
 // softmax pieces (max, exp-sum, exp-weighted V sum) with cross-lane permutes; the 4 wavefronts are
 // combined through LDS.
+#include <type_traits>
+
 #include "common.h"
 
 namespace lm {
@@ -348,9 +350,18 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float o_g[NG][G][D];
   __shared__ __attribute__((aligned(16))) bf16_t k_s[4][16 * S::KROW];  // each wave's 16 keys in turn
 
-  const size_t head_off = ((size_t)(a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
+  const size_t head_off = ((size_t)(a.table ? 0 : a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
   const bf16_t *Kh = reinterpret_cast<const bf16_t *>(a.kc) + head_off;
   const bf16_t *Vh = reinterpret_cast<const bf16_t *>(a.vc) + head_off;
+  // paged cache: the wave's positions (clamped to t) lie in one page, so one table entry places them all
+  static_assert(kPageSize % NPW == 0, "a wavefront's positions must lie in one page");
+  int pg0 = 0;
+  if (a.table) {
+    const int pe = min(pw0, t);
+    const int sl = page_slot(a.table + (size_t)b * a.pages, pe, a.npages, a.status);
+    pg0 = sl < 0 ? 0 : sl - pe % kPageSize;
+  }
+  auto phys = [&](int p) { return a.table ? pg0 + p % kPageSize : p; };
 
   // (1) loads, oldest first: the queries (lane l: head l%16 of the group, numbers 32 ks + 8(l/16) .. +8),
   // then keys and values in row slices (lane l: 16 bytes at 8 (l%LPR) of row l/LPR of PPI rows, so a load
@@ -369,20 +380,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   if (KROWS) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int p = min(pw0 + PPI * i + vg, t);
+      const int p = phys(min(pw0 + PPI * i + vg, t));
       kr[i] = load_stream16(Kh + (size_t)p * D + 8 * vl);
     }
   } else {
 #pragma unroll
     for (int gi = 0; gi < NGI; ++gi) {
-      const int p = min(pw0 + 16 * gi + qrow, t);
+      const int p = phys(min(pw0 + 16 * gi + qrow, t));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kb[gi][ks] = load_stream16(Kh + (size_t)p * D + 32 * ks + qh8);
     }
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int p = min(pw0 + PPI * i + vg, t);
+    const int p = phys(min(pw0 + PPI * i + vg, t));
     vr[i] = load_stream16(Vh + (size_t)p * D + 8 * vl);
   }
 
@@ -647,6 +658,22 @@ static int chunk_d(int g) {
 int attention_chunk(int kvdtype, int head, int g) {
   if (kvdtype == LLAMA_BF16) return head == 64 ? chunk_d<bf16_t, 64>(g) : chunk_d<bf16_t, 128>(g);
   return head == 64 ? chunk_d<float, 64>(g) : chunk_d<float, 128>(g);
+}
+
+int attention_paged_supported(int kvdtype, int head, int g) {
+  if (kvdtype != LLAMA_BF16 || !attention_supported(head, g)) return 0;
+  auto ok = [](auto d, int gg) {
+    constexpr int D = decltype(d)::value;
+    switch (gg) {
+      case 1: return use_mfma<bf16_t, D, 1>();
+      case 2: return use_mfma<bf16_t, D, 2>();
+      case 3: return use_mfma<bf16_t, D, 3>();
+      case 4: return use_mfma<bf16_t, D, 4>();
+      case 8: return use_mfma<bf16_t, D, 8>();
+    }
+    return false;
+  };
+  return head == 64 ? ok(std::integral_constant<int, 64>{}, g) : ok(std::integral_constant<int, 128>{}, g);
 }
 
 int attention_supported(int head, int g) {

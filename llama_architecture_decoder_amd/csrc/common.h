@@ -236,7 +236,25 @@ struct RopeAppend {
   int row0;                        // cache row of token row 0
   const float *rope_cs, *rope_sn;  // [max_seq][half]
   int pos[kMaxBatch];              // position of each token row
+  // paged cache (table != nullptr): cache row 0 is a pool of max_seq positions in pages of kPageSize;
+  // token row t's position p lies at pool position page_slot(table + t*pages, p)
+  const int32_t *table;
+  int pages, npages;               // entries per table row, pages in the pool
+  int *status;                     // sticky flag word: bit 1 = a table entry outside the pool
 };
+
+// Paged caches: positions of a row lie in pages of kPageSize consecutive pool positions, page i of the
+// row being pool page tr[i] (nest card `decode_paged` / `prefill_paged`: row b's positions lie in the
+// pages table[b] lists).  An entry outside the pool sets bit 1 of the status word and yields -1.
+constexpr int kPageSize = 64;
+__device__ __forceinline__ int page_slot(const int32_t *tr, int p, int npages, int *status) {
+  const int pg = tr[p / kPageSize];
+  if (pg < 0 || pg >= npages) {
+    if (status) atomicOr(status, 2);
+    return -1;
+  }
+  return pg * kPageSize + p % kPageSize;
+}
 
 // logical row L of the stacked q|k|v rows -> the weight row it reads: inside the q and k heads,
 // logical rows 2i and 2i+1 of a head are rows i and i + half
@@ -271,7 +289,13 @@ __device__ __forceinline__ void rope_append(const RopeAppend &ra, float *y, int 
   const bool is_k = P < qk;
   const int r = is_k ? P - ra.dim : P - qk;  // row within the k (or v) heads
   const int j = r >> dshift, d = r & (D - 1);
-  const size_t off = (((size_t)(ra.row0 + t) * (ra.kvw >> dshift) + j) * ra.max_seq + p) * D + d;
+  int crow = ra.row0 + t, slot = p;
+  if (ra.table) {  // the pool row; an entry outside the pool writes nothing
+    crow = 0;
+    slot = page_slot(ra.table + (size_t)t * ra.pages, p, ra.npages, ra.status);
+    if (slot < 0) return;
+  }
+  const size_t off = (((size_t)crow * (ra.kvw >> dshift) + j) * ra.max_seq + slot) * D + d;
   void *base = is_k ? ra.kc : ra.vc;
   if (ra.kv_bf16)
     reinterpret_cast<bf16_t *>(base)[off] = f32_to_bf16(out);
@@ -354,6 +378,10 @@ struct AttnArgs {
   int direct;          // set by the launcher: one chunk per row, outputs written normalised
   float scale;         // 1/sqrt(head)
   int pos[kMaxBatch];
+  // paged cache (as RopeAppend): row b's position p at pool position page_slot(table + b*pages, p) of row 0
+  const int32_t *table;
+  int pages, npages;
+  int *status;
 };
 
 // Prefill of S positions of one cache row (bf16 cache): RoPE + append and causal attention
@@ -366,6 +394,10 @@ struct PrefillArgs {
   float *out;          // [S][out_stride] attention output, heads concatenated
   int out_stride;
   float scale;         // 1/sqrt(head)
+  // paged cache: `row` is 0 and position p lies at pool position page_slot(table, p)
+  const int32_t *table;
+  int npages;
+  int *status;
 };
 
 // Kernel timing: when the host sets `start`/`stop`, the next launch records them from its own dispatch
@@ -395,6 +427,7 @@ int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is in
 // rows' positions in a.pos[0..B-1], tmax = their maximum
 hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int tmax, hipStream_t s);
 int attention_supported(int head, int g);
+int attention_paged_supported(int kvdtype, int head, int g);  // the matrix-core kernel (whole pages per wave)
 int attention_chunk(int kvdtype, int head, int g);
 // device-scope stores and loads (the scope bits on the instruction keep them coherent across the XCDs'
 // L2 caches: a store is written through, a load does not hit a stale line)

@@ -192,6 +192,9 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool
 __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
   const int i = blockIdx.x, p = a.pos0 + i;
   const int half = a.half, D = 2 * half;
+  // the cache slot of position p: itself in row a.row, or its place in the page pool (row 0); an entry
+  // outside the pool writes no key or value
+  const int slot = a.table ? page_slot(a.table, p, a.npages, a.status) : p;
   float *row = a.qkv + (size_t)i * a.qkv_stride;
   const float *cs = a.rope_cs + (size_t)p * half, *sn = a.rope_sn + (size_t)p * half;
   const int nq = a.heads * half, nk = a.kv * half;
@@ -205,16 +208,17 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
     if (isq) {
       src[d] = nlo;
       src[d + half] = nhi;
-    } else {
-      bf16_t *kd = a.kc + ((size_t)(a.row * a.kv + h) * a.max_seq + p) * D;
+    } else if (slot >= 0) {
+      bf16_t *kd = a.kc + ((size_t)(a.row * a.kv + h) * a.max_seq + slot) * D;
       kd[d] = f32_to_bf16(nlo);
       kd[d + half] = f32_to_bf16(nhi);
     }
   }
+  if (slot < 0) return;
   const float *v = row + a.heads * D + a.kv * D;
   for (int k = threadIdx.x; k < a.kv * D; k += kThreads) {
     const int h = k / D, d = k - h * D;
-    a.vc[((size_t)(a.row * a.kv + h) * a.max_seq + p) * D + d] = f32_to_bf16(v[k]);
+    a.vc[((size_t)(a.row * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(v[k]);
   }
 }
 
@@ -292,19 +296,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   constexpr int KPT = (KCH + kThreads - 1) / kThreads;
   constexpr int VCH = (kKT / 4) * (D / 8);    // (4 keys x 8 numbers) pieces of the V tile
   u32x4 kreg[KPT], vreg[4];
+  // paged cache: a tile's positions k0 .. k0+63 (k0 a multiple of the page size, clamped to last_pos)
+  // lie in one page
+  static_assert(kKT == kPageSize, "a key tile is one page");
   auto fetch = [&](int k0) {
+    int base = k0;  // cache slot of position k0
+    if (a.table) {
+      const int sl = page_slot(a.table, k0, a.npages, a.status);
+      base = sl < 0 ? 0 : sl;
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * kThreads;
       if (KCH % kThreads == 0 || c < KCH) {
         const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-        kreg[i] = load16(Kh + (size_t)min(k0 + r, last_pos) * D + cc);
+        kreg[i] = load16(Kh + (size_t)(base + min(k0 + r, last_pos) - k0) * D + cc);
       }
     }
     if (tid < VCH) {
       const int dc = tid % (D / 8), kq = tid / (D / 8);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vreg[u] = load16(Vh + (size_t)min(k0 + 4 * kq + u, last_pos) * D + dc * 8);
+      for (int u = 0; u < 4; ++u)
+        vreg[u] = load16(Vh + (size_t)(base + min(k0 + 4 * kq + u, last_pos) - k0) * D + dc * 8);
     }
   };
   auto stash = [&](int buf) {

@@ -20,7 +20,7 @@ def test_header_declares_the_boundary():
     for need in ("llama_decode_step", "llama_prefill", "kv_cache_alloc", "lm_head_argmax", "llama_kv_cache_bytes",
                  "llama_workspace_bytes", "llama_workspace_init", "llama_status", "llama_strerror",
                  "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version", "llama_sample",
-                 "llama_sample_scratch_bytes"):
+                 "llama_sample_scratch_bytes", "llama_decode_step_paged", "llama_prefill_paged"):
         assert need in names, need
 
 
@@ -178,3 +178,53 @@ def test_sample_scratch_bytes_and_argument_checks(L):
     assert smp(nbytes=16 * 64 * 8 - 1) == lm.E_WORKSPACE
     assert smp(scratch=fake + 4) == lm.E_WORKSPACE
     assert smp(B=0, logits=None, ids=None, scratch=None) == lm.OK
+
+
+def test_paged_calls_reject_before_any_device_work(L):
+    """The paged entry points' argument errors, decided on the host (fake device pointers are never read)."""
+    fake = 1 << 40
+    ws = lm.llama_ws(fake, 1 << 30, 4, 1024, 0, 0, 0)  # never initialised: reached only after the checks
+    pos = (ctypes.c_int32 * 3)(0, 0, 0)
+
+    def setup(cfg, max_seq=1024, dtype=None):
+        c = _c(cfg)
+        kvd = lm.BF16 if cfg.kvdtype == "bf16" else lm.F32
+        kv = lm.llama_kv(fake, fake, 1, max_seq, cfg.layers, cfg.kv, 2 * cfg.half, kvd if dtype is None else dtype)
+        lw = (lm.llama_layer_w * cfg.layers)()
+        for l in range(cfg.layers):
+            for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "w_gate", "w_up", "w_down"):
+                setattr(lw[l], f, fake)
+        return c, kv, lm.llama_weights(fake, fake, fake, lw), lw
+
+    cfg = configs.truncated(configs.LLAMA31_8B, 1)
+    c, kv, w, lw = setup(cfg)
+
+    def dec(B, p, pages=4, table=fake, kvr=kv):
+        for i, v in enumerate(p):
+            pos[i] = v
+        return L.llama_decode_step_paged(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kvr), fake, pos, B, table,
+                                         pages, None, None, ctypes.byref(ws), None)
+
+    assert dec(1, [0], table=None) == lm.E_NULL
+    assert dec(1, [0], pages=0) == lm.E_SHAPE
+    assert dec(0, [0]) == lm.E_SHAPE
+    assert dec(1, [256]) == lm.E_POS          # 4 pages hold positions 0..255
+    assert dec(2, [3, -1]) == lm.E_POS
+    _, odd_pool, _, _ = setup(cfg, max_seq=1000)
+    assert dec(1, [0], kvr=odd_pool) == lm.E_SHAPE   # the pool is not whole pages
+    assert dec(1, [255]) == lm.E_WORKSPACE           # valid arguments, uninitialised workspace
+    f32 = configs.SMOLLM2_135M                       # F32 cache: the paged attention needs bf16
+    c2, kv2, w2, _ = setup(f32)
+    assert L.llama_decode_step_paged(ctypes.byref(c2), ctypes.byref(w2), ctypes.byref(kv2), fake, pos, 1, fake, 4,
+                                     None, None, ctypes.byref(ws), None) == lm.E_UNSUPPORTED
+
+    def pf(S, p0, pages=4, table=fake):
+        return L.llama_prefill_paged(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), table, pages, fake, S, p0,
+                                     None, None, ctypes.byref(ws), None)
+
+    assert pf(4, 0, table=None) == lm.E_NULL
+    assert pf(0, 0) == lm.E_SHAPE
+    assert pf(4, 253) == lm.E_POS
+    assert pf(4, -1) == lm.E_POS
+    assert pf(4, 252) == lm.E_WORKSPACE
+    assert L.llama_strerror(lm.E_PAGE)
