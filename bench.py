@@ -318,6 +318,107 @@ def time_secondary(args, lm, synth, configs, c3=None):
     return res3
 
 
+def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax=512, new=128):
+    """Continuous batching over a paged cache (the pages' serving workload): n_req requests with prompts of
+    uniform random length in [pmin, pmax] and `new` greedy tokens each, at most `conc` in flight.  Each
+    request gets a slot; its prompt runs through llama_prefill_paged as soon as a slot is free (the
+    prefill's argmax is its first new token, written straight into the slot's entry of the device token
+    array), then every step runs llama_decode_step_paged over all slots (idle ones at position 0 of a
+    scratch page).  Pages (64 positions) come from a free list when a prompt is admitted and when a row
+    reaches a new page, and go back when its request finishes; the page table is rewritten on the device
+    from a ring of pinned host buffers, so the host never waits for the GPU.  Tokens/s = n_req * new /
+    (time from the first admission to the last step)."""
+    import numpy as np
+    import torch
+    PAGE = lm.PAGE_SIZE
+    per_req = (pmax + new + PAGE - 1) // PAGE
+    npool = conc * per_req + 1  # page 0: the idle slots' scratch page
+    dec = lm.Decoder(cfg, None, rows=1, max_seq=npool * PAGE, max_prefill=pmax, weights=dev_weights, ws_rows=conc,
+                     ws_seq=per_req * PAGE)
+    lens = synth.int_range("serve/prompt_lens", n_req, pmin, pmax).astype(np.int64)
+    flat = np.zeros((n_req, pmax), dtype=np.int32)
+    for r in range(n_req):
+        flat[r, :lens[r]] = synth.tokens(cfg, f"serve/prompt/{r}", int(lens[r]))
+    prompts = torch.from_numpy(flat).cuda()
+    tokens = torch.zeros(conc, dtype=torch.int32, device="cuda")
+    table = np.zeros((conc, per_req), dtype=np.int32)
+    table_dev = torch.zeros((conc, per_req), dtype=torch.int32, device="cuda")
+    ring = [torch.empty((conc, per_req), dtype=torch.int32, pin_memory=True) for _ in range(8)]
+    ring_ev = [None] * len(ring)
+    ring_i = [0]
+
+    def upload():
+        i = ring_i[0] % len(ring)
+        ring_i[0] += 1
+        if ring_ev[i] is not None:
+            ring_ev[i].synchronize()
+        ring[i].numpy()[...] = table
+        table_dev.copy_(ring[i], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        ring_ev[i] = ev
+
+    free = list(range(1, npool))
+    req = [-1] * conc
+    pos = [0] * conc
+    gen = [0] * conc
+    pages = [[] for _ in range(conc)]
+    nxt, done, steps, prefills = 0, 0, 0, 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    e0.record()
+    while done < n_req:
+        changed = False
+        for s in range(conc):
+            if req[s] < 0 and nxt < n_req:
+                r, L = nxt, int(lens[nxt])
+                nxt += 1
+                need = (L + PAGE - 1) // PAGE
+                pages[s] = [free.pop() for _ in range(need)]
+                table[s, :] = 0
+                table[s, :need] = pages[s]
+                upload()
+                dec.prefill_paged(prompts[r, :L], table_dev[s], pos0=0, next_tok=tokens[s:s + 1])
+                prefills += 1
+                req[s], pos[s], gen[s] = r, L, 1
+        for s in range(conc):
+            if req[s] >= 0 and pos[s] // PAGE >= len(pages[s]):
+                pages[s].append(free.pop())
+                table[s, len(pages[s]) - 1] = pages[s][-1]
+                changed = True
+        if changed:
+            upload()
+        dec.decode_paged(tokens, [pos[s] if req[s] >= 0 else 0 for s in range(conc)], table_dev, None, tokens)
+        steps += 1
+        for s in range(conc):
+            if req[s] < 0:
+                continue
+            pos[s] += 1
+            gen[s] += 1
+            if gen[s] == new:
+                free.extend(pages[s])
+                pages[s] = []
+                table[s, :] = 0
+                req[s] = -1
+                done += 1
+    e1.record()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    if dec.status() != 0:
+        raise RuntimeError("device status flag set during the serving run")
+    gpu_s = e0.elapsed_time(e1) * 1e-3
+    out = {"workload": f"{n_req} requests, prompts uniform in [{pmin}, {pmax}] tokens, {new} greedy new tokens each, "
+                       f"at most {conc} in flight; paged bf16 cache ({npool} pages of {PAGE}); {cfg.name} shape",
+           "value": round(n_req * new / gpu_s, 1), "unit": "tokens/s", "seconds": round(gpu_s, 3),
+           "host_seconds": round(host_s, 3), "decode_steps": steps, "prefills": prefills,
+           "prompt_tokens": int(lens.sum())}
+    log(f"serving: {out['value']} tok/s ({gpu_s:.2f} s, {steps} steps)")
+    del dec, prompts
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_sample(lm, vocab, reps=200):
     """Sampling (temperature 0.6, top-k 50, top-p 0.9) over synthetic F32 logits resident in HBM, for 1
     and 64 rows of the vocabulary.  The time per call is the span from the start of its first kernel to
@@ -365,6 +466,8 @@ def main():
                     help="time only the batch-32 long-context decode (for profiling its kernels)")
     ap.add_argument("--secondary-only", action="store_true",
                     help="time only the 1.7B-shaped decode (for profiling its kernels)")
+    ap.add_argument("--serving-only", action="store_true",
+                    help="time only the paged continuous-batching workload (for profiling its kernels)")
     ap.add_argument("--sample-only", action="store_true",
                     help="time only sampling over the 8B vocabulary (for profiling its kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -392,6 +495,10 @@ def main():
         return
     if args.sample_only:
         print(json.dumps({"sampling": time_sample(lm, cfg.vocab)}), flush=True)
+        return
+    if args.serving_only:
+        dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
+        print(json.dumps({"serving": time_serving(cfg, lm, synth, dec.w)}), flush=True)
         return
     if args.prefill_only or args.batched_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
@@ -453,6 +560,7 @@ def main():
         log(f"prefill {c5.prompt_len}: {result['prefill']['ms_per_prefill']:.1f} ms, "
             f"{result['prefill']['tflops']:.0f} TFLOP/s")
         result["sampling"] = time_sample(lm, cfg.vocab)
+        result["serving"] = time_serving(cfg, lm, synth, dec.w)
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:

@@ -200,6 +200,14 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
     need(S.gu, 2 * d.f);
     need(S.down, d.dim);
   }
+  // the matrix-core prefill's K-slice partial sums (short prompts), for every chunk size up to prows
+  for (int32_t m = 128; prows >= 2 && m < prows + 128; m += 128) {
+    const int M = m < prows ? m : prows;
+    const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f;
+    const size_t n[4] = {gemm_tiled_part_floats(M, H + 2 * KW, H, false), gemm_tiled_part_floats(M, H, H, false),
+                         gemm_tiled_part_floats(M, F, H, true), gemm_tiled_part_floats(M, H, F, false)};
+    for (size_t v : n) part = v > part ? v : part;
+  }
   L.part = take(sizeof(float) * part);
   L.total = o;
   return L;
@@ -530,6 +538,7 @@ int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int r
     ga.ldy = ldy;
     ga.res = res;
     ga.ldres = ldy;
+    ga.part = x.at<float>(x.L.part);  // short chunks split K (sized for every chunk up to max_prefill)
     return hip_rc(launch_gemm_tiled(epi, ga, x.s, true));
   };
   PrefillArgs pa = {};

@@ -350,6 +350,8 @@ struct GemmArgs {
   int tiles_per_slice; // set by the launcher
   bf16_t *ohi, *olo;   // EPI_SWIGLU: the output as the next product's operands [mpad][ldo]
   int ldo;
+  // k_gemm_tiled: K slices (set by the launcher); more than one leaves partial sums in `part` for a reduce
+  int kslices;
 };
 
 // x[t] += sum_s part[s][t][:], then the next product's operands from rmsnorm(x[t], gain)
@@ -449,6 +451,10 @@ hipError_t launch_gemm_rows(GemvEpi epi, GemmArgs a, int S, hipStream_t s, bool 
 hipError_t launch_rows_reduce_norm(int gdtype, const RowsNormArgs &a, hipStream_t s, bool last);
 // many token rows (prefill): 128 x 128 tiles; the operands need gemm_tiled_rows(M) rows (zero-padded)
 int gemm_tiled_rows(int M);
+// K slices of a tiled product of M rows (more than one when the tiles alone would not fill the GPU) and
+// the partial-sum floats they need in GemmArgs::part (0 for one slice)
+int gemm_tiled_kslices(int M, int N, int K, bool swiglu);
+size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu);
 hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
 hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last);

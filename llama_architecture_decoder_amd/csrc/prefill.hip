@@ -96,7 +96,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nst = a.K / kTK;
+  // K slice blockIdx.z of gridDim.z: steps kz0 .. kz0 + nst - 1
+  const int nst = a.K / kTK / (int)gridDim.z;
+  const int kz = (int)blockIdx.z * nst * kTK;
+#pragma unroll
+  for (int i = 0; i < AC; ++i) ga[i] += kz;
+#pragma unroll
+  for (int i = 0; i < BC; ++i) gb[i] += kz;
   fetch(0);
   stash(0);
   __syncthreads();
@@ -133,6 +139,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
   }
 
   // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each tile
+  if (gridDim.z > 1) {
+    // a K slice: raw sums to part[z][t][n] (SwiGLU: gate at n, up at N + n); k_tiled_reduce finishes
+    const int nout = SW ? 2 * a.N : a.N;
+    float *pz = a.part + (size_t)blockIdx.z * a.M * nout;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = SW ? n0 + wn * 64 + (j & 1) * 32 + l32 : n0 + wn * 128 + j * 32 + l32;
+          if (n < a.N) pz[(size_t)t * nout + (SW && j >= 2 ? a.N : 0) + n] = acc[i][j][r];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -163,20 +187,79 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
     }
 }
 
+// The K slices' partial sums of a tiled product, added in slice order, then its epilogue: thread =
+// two consecutive outputs of token row blockIdx.y.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void k_tiled_reduce(GemmArgs a, int S) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  const int t = blockIdx.y;
+  const int n = 2 * (blockIdx.x * kThreads + threadIdx.x);
+  if (n >= a.N) return;
+  const int nout = SW ? 2 * a.N : a.N;
+  const float *pp = a.part + (size_t)t * nout + n;
+  const size_t zs = (size_t)a.M * nout;
+  float v0 = 0.f, v1 = 0.f, u0 = 0.f, u1 = 0.f;
+  for (int z = 0; z < S; ++z) {
+    const float2 p = *reinterpret_cast<const float2 *>(pp + z * zs);
+    v0 += p.x;
+    v1 += p.y;
+    if (SW) {
+      const float2 q = *reinterpret_cast<const float2 *>(pp + z * zs + a.N);
+      u0 += q.x;
+      u1 += q.y;
+    }
+  }
+  float *y = a.y + (size_t)t * a.ldy + n;
+  if (SW) {
+    y[0] = (v0 / (1.0f + expf(-v0))) * u0;
+    y[1] = (v1 / (1.0f + expf(-v1))) * u1;
+  } else {
+    if (EPI == EPI_RESID) {
+      v0 += a.res[(size_t)t * a.ldres + n];
+      v1 += a.res[(size_t)t * a.ldres + n + 1];
+    }
+    y[0] = v0;
+    y[1] = v1;
+  }
+}
+
 int gemm_tiled_rows(int M) { return (M + kTM - 1) / kTM * kTM; }
 
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last) {
-  if (a.K % kTK != 0 || a.M <= 0) return hipErrorInvalidValue;
+int gemm_tiled_kslices(int M, int N, int K, bool swiglu) {
+  const int blocks = ((M + kTM - 1) / kTM) * ((N + (swiglu ? kTN / 2 : kTN) - 1) / (swiglu ? kTN / 2 : kTN));
+  const int steps = K / kTK;
+  int ks = 1;
+  // two blocks per CU: aim for 512, keep at least 8 steps of K per slice
+  while (blocks * ks < 512 && ks < 16 && N % 2 == 0 && steps % (2 * ks) == 0 && steps / (2 * ks) >= 8) ks *= 2;
+  return ks;
+}
+
+size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu) {
+  const int ks = gemm_tiled_kslices(M, N, K, swiglu);
+  return ks > 1 ? (size_t)ks * M * (swiglu ? 2 * (size_t)N : (size_t)N) : 0;
+}
+
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last) {
+  if (a0.K % kTK != 0 || a0.M <= 0) return hipErrorInvalidValue;
+  GemmArgs a = a0;
   const int mt = (a.M + kTM - 1) / kTM;
+  const bool sw = epi == EPI_SWIGLU;
+  a.kslices = a.part ? gemm_tiled_kslices(a.M, a.N, a.K, sw) : 1;
+  const int ks = a.kslices;
+  const dim3 rg((a.N / 2 + kThreads - 1) / kThreads, a.M);
   switch (epi) {
     case EPI_STORE:
-      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt), dim3(kThreads), s, false, last, a);
+      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, false, last && ks == 1, a);
+      if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
     case EPI_RESID:
-      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt), dim3(kThreads), s, false, last, a);
+      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, false, last && ks == 1, a);
+      if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
     case EPI_SWIGLU:
-      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt), dim3(kThreads), s, false, last, a);
+      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt, ks), dim3(kThreads), s, false,
+             last && ks == 1, a);
+      if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
     default:
       return hipErrorInvalidValue;
