@@ -282,9 +282,12 @@ struct ProfScope {
   ~ProfScope() {
     if (!e0) return;
     LaunchEvents &ev = launch_events();
-    const bool used = ev.used;
+    const bool used = ev.used, stop_used = ev.stop_used;
     ev = LaunchEvents();
     if (!used) return;  // nothing was launched (an error path): drop the pair
+    // a scope whose launches took only the start event (an operand split whose product belongs to the
+    // next scope) ends where its work ends on the stream
+    if (!stop_used && hipEventRecord(e1, s) != hipSuccess) return;
     prof().marks.push_back({cls, {e0, e1}});
   }
 };

@@ -407,7 +407,8 @@ struct PrefillArgs {
 // several kernels gives `start` to the first and `stop` to the last.  Cleared once used.
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
-  bool used = false;
+  bool used = false;       // some launch took an event
+  bool stop_used = false;  // a launch took `stop`
 };
 LaunchEvents &launch_events();
 
@@ -417,6 +418,7 @@ inline void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, bool first, b
   hipEvent_t e0 = first ? ev.start : nullptr, e1 = last ? ev.stop : nullptr;
   if (e0 || e1) {
     ev.used = true;
+    if (e1) ev.stop_used = true;
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
   } else {
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
