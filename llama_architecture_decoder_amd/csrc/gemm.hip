@@ -12,8 +12,9 @@
 //
 // k_gemm_rows: block (bx, s) owns 128 consecutive outputs (wave w: outputs 32w .. +32 as two 16-row
 // tiles; SwiGLU: 64 outputs, wave w's tiles are the gate and the up rows of outputs 16w .. +16) over the
-// s-th slice of K.  X tiles of 128 columns are staged in LDS once for the 4 waves (double buffered); each
-// wave keeps the weight loads of the next two tiles in flight while it multiplies the current one.  The
+// s-th slice of K.  X tiles of 128 columns are staged in LDS once for the 4 waves (double buffered up to
+// 2 token tiles); each wave keeps the weight loads of the next two tiles (one at 4 token tiles) in flight
+// while it multiplies the current one.  The
 // weights are loaded in 256-byte runs of a row (the MFMA layout would give 64-byte pieces of 16 rows per
 // load, which streams from HBM markedly slower) and rearranged through the wave's own LDS tile.  With one slice
 // the epilogue runs in the kernel; with several, each slice writes its partial sums and a reduce kernel
@@ -88,14 +89,15 @@ __device__ __forceinline__ const bf16_t *weight_row(const GemmArgs &a, int n, in
   return reinterpret_cast<const bf16_t *>(a.w[seg]) + (size_t)(wr - a.rs[seg]) * a.K;
 }
 
-// Blocks per CU: two up to 3 token tiles (3 tiles keep one X buffer to fit: 40 rows decode 9% faster than
-// with one block of two buffers), one at 4 tiles (two would spill registers, measured slower).
+// Two blocks per CU: from 3 token tiles on, one X buffer (to fit the LDS) and, at 4 tiles, the weights
+// requested one tile ahead instead of two (to fit the registers without spilling).  Measured against
+// one block per CU with two buffers: 40-row decode 9% faster, 64-row decode 10% faster.
 template <int MT, int EPI, bool PART>
-__global__ __launch_bounds__(kThreads, MT <= 3 ? 2 : 1) void k_gemm_rows(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_rows(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
   constexpr int ROWS = SW ? kRowsOut / 2 : kRowsOut;
   constexpr int XCH = MT * 16 * kRT / 8 / kThreads;  // 16-byte chunks of one X array per thread per tile (= MT)
-  constexpr int XB = MT == 3 ? 1 : 2;  // X tile buffers
+  constexpr int XB = MT >= 3 ? 1 : 2;  // X tile buffers
   __shared__ __attribute__((aligned(16))) bf16_t xs[XB][2][MT * 16 * kLdt];  // [buffer][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t ws[4][32 * kLdt];          // each wave's weight tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -182,9 +184,10 @@ __global__ __launch_bounds__(kThreads, MT <= 3 ? 2 : 1) void k_gemm_rows(GemmArg
   // one tile: the X tile after it (LDS, distance 1) and the weights two tiles ahead (registers, a ring of
   // three) are requested first, X before weights so that waiting for X leaves the weights in flight; LDS
   // barriers do not wait for global loads
+  constexpr int WD = MT >= 4 ? 1 : 2;  // how many tiles ahead the weights are requested
   auto step = [&](int t, const u32x4 (&wcur)[8], u32x4 (&wahead)[8]) {
     if (t + 1 < nt) load_x(t + 1);
-    if (t + 2 < nt) load_w(wahead, t + 2);
+    if (t + WD < nt) load_w(wahead, t + WD);
     compute(XB == 2 ? (t & 1) : 0, wcur);
     if (t + 1 < nt) {
       if (XB == 1) lds_barrier();  // every wave is done with the one X tile
@@ -194,15 +197,23 @@ __global__ __launch_bounds__(kThreads, MT <= 3 ? 2 : 1) void k_gemm_rows(GemmArg
   };
   load_x(0);
   load_w(w0, 0);
-  if (nt > 1) load_w(w1, 1);
+  if (WD == 2 && nt > 1) load_w(w1, 1);
   stash_x(0);
   lds_barrier();
-  for (int t = 0; t < nt; t += 3) {
-    step(t, w0, w2);
-    if (t + 1 >= nt) break;
-    step(t + 1, w1, w0);
-    if (t + 2 >= nt) break;
-    step(t + 2, w2, w1);
+  if constexpr (WD == 2) {
+    for (int t = 0; t < nt; t += 3) {
+      step(t, w0, w2);
+      if (t + 1 >= nt) break;
+      step(t + 1, w1, w0);
+      if (t + 2 >= nt) break;
+      step(t + 2, w2, w1);
+    }
+  } else {
+    for (int t = 0; t < nt; t += 2) {
+      step(t, w0, w1);
+      if (t + 1 >= nt) break;
+      step(t + 1, w1, w0);
+    }
   }
 
   // lane holds C[token 4(lane/16) + r][output l16] of tile (m, j)
