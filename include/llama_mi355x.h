@@ -173,6 +173,20 @@ int llama_prefill(const llama_cfg *c, const llama_weights *w, const llama_kv *kv
                   int32_t S, int32_t pos0, float *logits_last, int32_t *next, const llama_ws *ws, void *stream);
 
 /*
+ * Greedy generation that stops early (nest card `generate_until`): for B rows of the cache, starting from
+ * token[b] (device int32 [B]) at position pos_host[b], up to max_new decode steps; step i writes its
+ * argmax tokens to produced[i][0..B) (device int32 [max_new][B], step-major) and feeds them to step i+1
+ * at positions pos_host[b] + i + 1.  The loop ends after the first step at which every row's token equals
+ * eos, or after max_new steps; *count (host) gets the steps taken and produced[count..max_new) is zeroed.
+ * The host waits for each step (the stopping test), so unlike llama_decode_step this call returns when
+ * the work is done.  Errors as llama_decode_step, plus E_POS when pos_host[b] + max_new exceeds the
+ * cache or workspace max_seq, E_SHAPE for max_new <= 0, E_NULL for produced or count NULL.
+ */
+int llama_generate_until(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *token,
+                         const int32_t *pos_host, int32_t B, int32_t max_new, int32_t eos, int32_t *produced,
+                         int32_t *count, const llama_ws *ws, void *stream);
+
+/*
  * Paged cache (nest card `decode_paged` / `prefill_paged`: with one cache row, that row is a pool of
  * positions in pages of 64, and request b's positions lie in the pages its table row lists).  Cache row 0
  * of `kv` is the pool: kv->max_seq pool positions (a multiple of 64), npool = kv->max_seq / 64 pages, the

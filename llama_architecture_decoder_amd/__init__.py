@@ -92,6 +92,8 @@ def lib():
     L.llama_prefill.argtypes = [pc, pw, pk, i32, vp, i32, i32, vp, vp, ps, vp]
     L.lm_head_argmax.argtypes = [pc, pw, vp, i32, vp, vp, ps, vp]
     L.llama_decode_step_paged.argtypes = [pc, pw, pk, vp, ctypes.POINTER(i32), i32, vp, i32, vp, vp, ps, vp]
+    L.llama_generate_until.argtypes = [pc, pw, pk, vp, ctypes.POINTER(i32), i32, i32, i32, vp,
+                                       ctypes.POINTER(i32), ps, vp]
     L.llama_prefill_paged.argtypes = [pc, pw, pk, vp, i32, vp, i32, i32, vp, vp, ps, vp]
     L.llama_status.argtypes = [ps, vp]
     L.llama_sample_scratch_bytes.argtypes = [i32, i32, i32]
@@ -274,6 +276,21 @@ class Decoder:
                                  tokens.data_ptr(), int(tokens.numel()), pos0, _ptr(logits), _ptr(next_tok),
                                  ctypes.byref(self.ws.rec), _stream_handle(stream))
         _check(rc, "llama_prefill")
+
+    def generate_until(self, token, pos: Sequence[int], max_new: int, eos: int, produced=None, stream=None):
+        """Greedy steps from token (device int32 [B]) at positions pos until every row produces eos or max_new
+        steps; returns (produced device int32 [max_new][B], steps taken)."""
+        torch = _torch()
+        B = len(pos)
+        if produced is None:
+            produced = torch.empty((max_new, B), dtype=torch.int32, device=self.device)
+        parr = (ctypes.c_int32 * B)(*[int(p) for p in pos])
+        n = ctypes.c_int32(0)
+        rc = lib().llama_generate_until(ctypes.byref(self.c), ctypes.byref(self.w.rec), ctypes.byref(self.kv.rec),
+                                        token.data_ptr(), parr, B, int(max_new), int(eos), produced.data_ptr(),
+                                        ctypes.byref(n), ctypes.byref(self.ws.rec), _stream_handle(stream))
+        _check(rc, "llama_generate_until")
+        return produced, int(n.value)
 
     def decode_paged(self, tokens, pos: Sequence[int], table, logits=None, next_tok=None, stream=None) -> None:
         """A step of B requests in a paged cache: cache row 0 is the page pool, request b's positions lie

@@ -917,6 +917,47 @@ int llama_decode_step_traced(const llama_cfg *c, const llama_weights *w, const l
   return decode_common(c, w, kv, tokens, pos_host, 1, logits, next, ws, stream, trace);
 }
 
+int llama_generate_until(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *token,
+                         const int32_t *pos_host, int32_t B, int32_t max_new, int32_t eos, int32_t *produced,
+                         int32_t *count, const llama_ws *ws, void *stream) {
+  if (!kv || !token || !pos_host || !w || !ws || !produced || !count) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if (B <= 0 || B > kv->rows || B > kMaxBatch || max_new <= 0) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos_host[b] < 0 || (int64_t)pos_host[b] + max_new > kv->max_seq) return LLAMA_E_POS;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  if (B > ws->max_batch) return LLAMA_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if ((int64_t)pos_host[b] + max_new > ws->max_seq) return LLAMA_E_POS;
+  // step i reads the previous step's tokens (the caller's for i = 0) and writes produced[i][0..B); the
+  // host waits for each step to see whether every row produced eos (the loop's scalar state)
+  int32_t pos[kMaxBatch], last[kMaxBatch];
+  *count = 0;
+  int32_t n = 0;
+  for (; n < max_new; ++n) {
+    for (int b = 0; b < B; ++b) pos[b] = pos_host[b] + n;
+    const int32_t *in = n == 0 ? token : produced + (size_t)(n - 1) * B;
+    if ((rc = run_step(x, in, pos, B, 0, nullptr, produced + (size_t)n * B, true, nullptr))) return rc;
+    if (hipStreamSynchronize(x.s) != hipSuccess) return LLAMA_E_HIP;
+    if (hipMemcpy(last, produced + (size_t)n * B, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess)
+      return LLAMA_E_HIP;
+    bool all = true;
+    for (int b = 0; b < B; ++b) all = all && last[b] == eos;
+    if (all) {
+      ++n;
+      break;
+    }
+  }
+  *count = n;
+  if (n < max_new && (rc = hip_rc(launch_zero(produced + (size_t)n * B, sizeof(int32_t) * (size_t)(max_new - n) * B,
+                                             x.s))))
+    return rc;
+  return LLAMA_OK;
+}
+
 // the prompt of one cache row (or of one paged row when x.table is set) after the argument checks
 static int prefill_common(const Ctx &x, const int32_t *tokens, int32_t S, int32_t pos0, int32_t row,
                           float *logits_last, int32_t *next) {

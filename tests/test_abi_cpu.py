@@ -20,7 +20,8 @@ def test_header_declares_the_boundary():
     for need in ("llama_decode_step", "llama_prefill", "kv_cache_alloc", "lm_head_argmax", "llama_kv_cache_bytes",
                  "llama_workspace_bytes", "llama_workspace_init", "llama_status", "llama_strerror",
                  "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version", "llama_sample",
-                 "llama_sample_scratch_bytes", "llama_decode_step_paged", "llama_prefill_paged"):
+                 "llama_sample_scratch_bytes", "llama_decode_step_paged", "llama_prefill_paged",
+                 "llama_generate_until"):
         assert need in names, need
 
 
