@@ -419,6 +419,30 @@ def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax
     return out
 
 
+def time_long_context(cfg, lm, synth, dev_weights, steps=8, max_seq=131072):
+    """Batch-1 decode at the end of the full rope-scaled context: positions max_seq - steps .. max_seq - 1
+    of a max_seq cache whose earlier positions hold seeded random keys and values (filled on the device).
+    Bytes per token: all weights, the LM head and the K/V rows read (~33 GB at the 8B shape)."""
+    import torch
+    dec = lm.Decoder(cfg, None, rows=1, max_seq=max_seq, weights=dev_weights)
+    p0 = max_seq - steps
+    synth.fill_cache_device(cfg, dec.kv.k.data_ptr(), dec.kv.v.data_ptr(), 1, max_seq, [p0])
+    torch.cuda.synchronize()
+    first = int(synth.tokens(cfg, "bench/long", 1)[0])
+    ev_ms, _, _ = time_decode(dec, cfg, p0, steps, 1, first)
+    # the warm-up step wrote position p0; the timed steps rewrite p0 .. max_seq - 1
+    ms = ev_ms / steps
+    b = sum(token_bytes(cfg, p0 + i) for i in range(steps)) / steps
+    out = {"workload": f"{cfg.name}-shaped decode, batch 1, bf16, positions {p0}..{max_seq - 1} of MaxSeq {max_seq} "
+                       f"(0..{p0 - 1} pre-filled random)", "value": round(1e3 / ms, 2), "unit": "tokens/s",
+           "ms_per_step": round(ms, 4), "bytes_per_token": int(b),
+           "hbm_fraction": round(b / (ms * 1e-3) / HBM_PEAK, 4)}
+    log(f"long context: {out['value']} tok/s, hbm {out['hbm_fraction']}")
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_sample(lm, vocab, reps=200):
     """Sampling (temperature 0.6, top-k 50, top-p 0.9) over synthetic F32 logits resident in HBM, for 1
     and 64 rows of the vocabulary.  The time per call is the span from the start of its first kernel to
@@ -466,6 +490,8 @@ def main():
                     help="time only the batch-32 long-context decode (for profiling its kernels)")
     ap.add_argument("--secondary-only", action="store_true",
                     help="time only the 1.7B-shaped decode (for profiling its kernels)")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the batch-1 decode at the end of a 131072-position cache")
     ap.add_argument("--serving-only", action="store_true",
                     help="time only the paged continuous-batching workload (for profiling its kernels)")
     ap.add_argument("--sample-only", action="store_true",
@@ -495,6 +521,10 @@ def main():
         return
     if args.sample_only:
         print(json.dumps({"sampling": time_sample(lm, cfg.vocab)}), flush=True)
+        return
+    if args.long_only:
+        dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
+        print(json.dumps({"long_context": time_long_context(cfg, lm, synth, dec.w)}), flush=True)
         return
     if args.serving_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
@@ -561,6 +591,7 @@ def main():
             f"{result['prefill']['tflops']:.0f} TFLOP/s")
         result["sampling"] = time_sample(lm, cfg.vocab)
         result["serving"] = time_serving(cfg, lm, synth, dec.w)
+        result["long_context"] = time_long_context(cfg, lm, synth, dec.w)
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:
