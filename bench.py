@@ -318,45 +318,60 @@ def time_secondary(args, lm, synth, configs, c3=None):
     return res3
 
 
-def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax=512, new=128):
+def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax=512, new=128, pass_tokens=2048):
     """Continuous batching over a paged cache (the pages' serving workload): n_req requests with prompts of
     uniform random length in [pmin, pmax] and `new` greedy tokens each, at most `conc` in flight.  Each
-    request gets a slot; its prompt runs through llama_prefill_paged as soon as a slot is free (the
-    prefill's argmax is its first new token, written straight into the slot's entry of the device token
-    array), then every step runs llama_decode_step_paged over all slots (idle ones at position 0 of a
-    scratch page).  Pages (64 positions) come from a free list when a prompt is admitted and when a row
-    reaches a new page, and go back when its request finishes; the page table is rewritten on the device
-    from a ring of pinned host buffers, so the host never waits for the GPU.  Tokens/s = n_req * new /
-    (time from the first admission to the last step)."""
+    request gets a slot; the prompts of all requests admitted at one step (every free slot takes the next
+    request) run as one llama_prefill_packed call over the page pool, packed end to end (the argmax after
+    each prompt is its first new token, scattered into the slots' entries of the device token array); then
+    every step runs llama_decode_step_paged over all slots (idle ones at position 0 of a scratch page).
+    Pages (64 positions) come from a free list when a prompt is admitted and when a row reaches a new page,
+    and go back when its request finishes; page tables and slot lists reach the device from rings of
+    pinned host buffers, so the host never waits for the GPU.  Tokens/s = n_req * new / (time from the
+    first admission to the last step)."""
     import numpy as np
     import torch
     PAGE = lm.PAGE_SIZE
     per_req = (pmax + new + PAGE - 1) // PAGE
     npool = conc * per_req + 1  # page 0: the idle slots' scratch page
-    dec = lm.Decoder(cfg, None, rows=1, max_seq=npool * PAGE, max_prefill=pmax, weights=dev_weights, ws_rows=conc,
-                     ws_seq=per_req * PAGE)
+    dec = lm.Decoder(cfg, None, rows=1, max_seq=npool * PAGE, max_prefill=pass_tokens, weights=dev_weights,
+                     ws_rows=conc, ws_seq=per_req * PAGE)
     lens = synth.int_range("serve/prompt_lens", n_req, pmin, pmax).astype(np.int64)
-    flat = np.zeros((n_req, pmax), dtype=np.int32)
-    for r in range(n_req):
-        flat[r, :lens[r]] = synth.tokens(cfg, f"serve/prompt/{r}", int(lens[r]))
-    prompts = torch.from_numpy(flat).cuda()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    prompts = torch.from_numpy(np.concatenate([synth.tokens(cfg, f"serve/prompt/{r}", int(lens[r]))
+                                               for r in range(n_req)])).cuda()
     tokens = torch.zeros(conc, dtype=torch.int32, device="cuda")
+    first = torch.zeros(conc, dtype=torch.int32, device="cuda")
     table = np.zeros((conc, per_req), dtype=np.int32)
     table_dev = torch.zeros((conc, per_req), dtype=torch.int32, device="cuda")
-    ring = [torch.empty((conc, per_req), dtype=torch.int32, pin_memory=True) for _ in range(8)]
-    ring_ev = [None] * len(ring)
-    ring_i = [0]
+    ptable_dev = torch.zeros((conc, per_req), dtype=torch.int32, device="cuda")  # admitted requests' rows
+    slots_dev = torch.zeros(conc, dtype=torch.int64, device="cuda")
+
+    class Ring:
+        """Pinned host buffers for host-to-device copies that never make the host wait for the GPU."""
+
+        def __init__(self, shape, dtype, n=8):
+            self.buf = [torch.empty(shape, dtype=dtype, pin_memory=True) for _ in range(n)]
+            self.ev = [None] * n
+            self.i = 0
+
+        def put(self, dst, src):
+            i = self.i % len(self.buf)
+            self.i += 1
+            if self.ev[i] is not None:
+                self.ev[i].synchronize()
+            b = self.buf[i].numpy()
+            b[...] = 0
+            b[:src.shape[0]] = src
+            dst.copy_(self.buf[i], non_blocking=True)
+            self.ev[i] = torch.cuda.Event()
+            self.ev[i].record()
+
+    tables, ptables, slot_lists = (Ring((conc, per_req), torch.int32), Ring((conc, per_req), torch.int32),
+                                   Ring(conc, torch.int64))
 
     def upload():
-        i = ring_i[0] % len(ring)
-        ring_i[0] += 1
-        if ring_ev[i] is not None:
-            ring_ev[i].synchronize()
-        ring[i].numpy()[...] = table
-        table_dev.copy_(ring[i], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        ring_ev[i] = ev
+        tables.put(table_dev, table)
 
     free = list(range(1, npool))
     req = [-1] * conc
@@ -370,6 +385,7 @@ def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax
     e0.record()
     while done < n_req:
         changed = False
+        adm = []
         for s in range(conc):
             if req[s] < 0 and nxt < n_req:
                 r, L = nxt, int(lens[nxt])
@@ -378,10 +394,18 @@ def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax
                 pages[s] = [free.pop() for _ in range(need)]
                 table[s, :] = 0
                 table[s, :need] = pages[s]
-                upload()
-                dec.prefill_paged(prompts[r, :L], table_dev[s], pos0=0, next_tok=tokens[s:s + 1])
-                prefills += 1
                 req[s], pos[s], gen[s] = r, L, 1
+                adm.append(s)
+        if adm:
+            # the admitted requests are consecutive, so their prompts are one range of the packed array
+            upload()
+            ptables.put(ptable_dev, table[adm])
+            slot_lists.put(slots_dev, np.asarray(adm, dtype=np.int64))
+            r0, r1 = req[adm[0]], req[adm[-1]] + 1
+            dec.prefill_packed(prompts[offs[r0]:offs[r1]], [(0, 0, int(lens[req[s]])) for s in adm],
+                               table=ptable_dev[:len(adm)], next_tok=first)
+            tokens.index_copy_(0, slots_dev[:len(adm)], first[:len(adm)])
+            prefills += 1
         for s in range(conc):
             if req[s] >= 0 and pos[s] // PAGE >= len(pages[s]):
                 pages[s].append(free.pop())
@@ -411,7 +435,8 @@ def time_serving(cfg, lm, synth, dev_weights, n_req=256, conc=64, pmin=128, pmax
     out = {"workload": f"{n_req} requests, prompts uniform in [{pmin}, {pmax}] tokens, {new} greedy new tokens each, "
                        f"at most {conc} in flight; paged bf16 cache ({npool} pages of {PAGE}); {cfg.name} shape",
            "value": round(n_req * new / gpu_s, 1), "unit": "tokens/s", "seconds": round(gpu_s, 3),
-           "host_seconds": round(host_s, 3), "decode_steps": steps, "prefills": prefills,
+           "host_seconds": round(host_s, 3), "decode_steps": steps, "prefill_calls": prefills,
+           "prefill_pass_tokens": pass_tokens,
            "prompt_tokens": int(lens.sum())}
     log(f"serving: {out['value']} tok/s ({gpu_s:.2f} s, {steps} steps)")
     del dec, prompts

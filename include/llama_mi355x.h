@@ -211,6 +211,34 @@ int llama_prefill_paged(const llama_cfg *c, const llama_weights *w, const llama_
                         int32_t *next, const llama_ws *ws, void *stream);
 
 /*
+ * Packed prefill (nest cards `prefill_packed` and `prefill_paged`): the prompts of nseg <= 64 requests
+ * packed end to end in `tokens` (device int32, segment 0's tokens first), no padding between them.
+ * Segment s is seg_len[s] >= 1 consecutive positions seg_pos0[s] .. of one request; its keys and values go
+ * to that request's cache and each of its positions attends over the request's positions 0 .. itself
+ * (those already in the cache and those of the segment), never over another segment's request.
+ *   table NULL  the request is cache row seg_row[s] (host int32 [nseg], each in [0, kv->rows));
+ *               seg_pos0[s] + seg_len[s] <= kv->max_seq.
+ *   table set   the paged pool of llama_decode_step_paged: segment s is the request of table row s
+ *               (device int32 [nseg][pages]); seg_row is not read; seg_pos0[s] + seg_len[s] <= pages * 64.
+ * With seg_pos0[s] = 0 for every segment this is the pages' packed prefill exactly (each prompt sees
+ * only itself); a later start continues a request after positions it already holds (a chunk, or pages
+ * shared with another request).  Segments of one request must not overlap in positions; two segments
+ * writing one cache slot race.  The bf16 matrix-core path packs up to the workspace's max_prefill
+ * positions per pass (a segment that does not fit continues in the next pass); other configs run the
+ * segments one after another as llama_prefill.
+ *   logits  device F32 [nseg][vocab], segment s's logits after its last position (optional)
+ *   next    device int32 [nseg], their argmax (optional)
+ * seg_row (table NULL), seg_pos0 and seg_len are host arrays, read before the call returns.  Errors
+ * (nothing enqueued): E_NULL, E_SHAPE (nseg outside [1, 64], a length < 1, a row outside the cache,
+ * misaligned logits), E_POS (a segment past its room or the workspace's max_seq), E_UNSUPPORTED (paged
+ * without the matrix-core attention), and those of llama_prefill.
+ */
+int llama_prefill_packed(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *table,
+                         int32_t pages, const int32_t *tokens, int32_t nseg, const int32_t *seg_row,
+                         const int32_t *seg_pos0, const int32_t *seg_len, float *logits, int32_t *next,
+                         const llama_ws *ws, void *stream);
+
+/*
  * Final RMSNorm + LM head + argmax of B hidden states (device F32 [B][dim], the last layer's output
  * before the final norm): main.bend head_of and argmax.  logits [B][vocab] optional, argmax [B] required.
  */

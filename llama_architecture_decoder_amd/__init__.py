@@ -95,6 +95,7 @@ def lib():
     L.llama_generate_until.argtypes = [pc, pw, pk, vp, ctypes.POINTER(i32), i32, i32, i32, vp,
                                        ctypes.POINTER(i32), ps, vp]
     L.llama_prefill_paged.argtypes = [pc, pw, pk, vp, i32, vp, i32, i32, vp, vp, ps, vp]
+    L.llama_prefill_packed.argtypes = [pc, pw, pk, vp, i32, vp, i32, vp, vp, vp, vp, vp, ps, vp]
     L.llama_status.argtypes = [ps, vp]
     L.llama_sample_scratch_bytes.argtypes = [i32, i32, i32]
     L.llama_sample_scratch_bytes.restype = i64
@@ -310,6 +311,22 @@ class Decoder:
                                        int(tokens.numel()), pos0, _ptr(logits), _ptr(next_tok),
                                        ctypes.byref(self.ws.rec), _stream_handle(stream))
         _check(rc, "llama_prefill_paged")
+
+    def prefill_packed(self, tokens, segments, table=None, logits=None, next_tok=None, stream=None) -> None:
+        """Several prompts packed end to end in tokens (device int32), segments = [(row, pos0, length)] in
+        that order: each writes its own request's cache and attends only over that request.  With table
+        (device int32 [len(segments)][pages]) segment s is the paged request of table row s and its row is
+        not read.  logits [len(segments)][vocab] / next_tok [len(segments)] get each segment's last-position
+        logits and argmax."""
+        n = len(segments)
+        rows = (ctypes.c_int32 * n)(*[int(r) for r, _, _ in segments])
+        pos0 = (ctypes.c_int32 * n)(*[int(p) for _, p, _ in segments])
+        lens = (ctypes.c_int32 * n)(*[int(m) for _, _, m in segments])
+        rc = lib().llama_prefill_packed(ctypes.byref(self.c), ctypes.byref(self.w.rec), ctypes.byref(self.kv.rec),
+                                        _ptr(table), int(table.shape[-1]) if table is not None else 0,
+                                        tokens.data_ptr(), n, rows, pos0, lens, _ptr(logits), _ptr(next_tok),
+                                        ctypes.byref(self.ws.rec), _stream_handle(stream))
+        _check(rc, "llama_prefill_packed")
 
     def lm_head_argmax(self, hidden, logits=None, argmax=None, stream=None):
         B = hidden.shape[0]

@@ -7,12 +7,14 @@
 // Every check that the host can make happens before the first launch, so an error leaves the caches
 // and outputs untouched (main.bend's room proof before KV.push; needle's validation before use).
 #include <math.h>
+#include <stdint.h>
 
 #include <cmath>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -487,12 +489,22 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
   return LLAMA_OK;
 }
 
-// Prompt positions pos0 .. pos0+S-1 of cache row `row`, all S at once per layer (S <= the workspace's
-// max_prefill): matrix-core products over the S rows, RoPE + append of the S positions, causal
-// attention over the cache.  The LM head runs on the last position only when want_head.
-int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int row, float *logits, int32_t *next,
-                     bool want_head) {
+// One piece of a packed pass: len consecutive positions pos0 .. of cache row `row` (paged: of table row
+// `row`); out >= 0 asks for the logits / next token after its last position at entry `out`.
+struct PackSeg {
+  int row, pos0, len, out;
+};
+
+// One pass over S packed positions (S <= the workspace's max_prefill), nseg pieces end to end in `tokens`:
+// matrix-core products over the S rows, RoPE + append of every position into its own request's cache,
+// causal attention of each piece over its request's positions.  The LM head runs on the last position of
+// each piece that asks for it.
+int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, int nseg, float *logits,
+                     int32_t *next) {
   const Dims &d = x.d;
+  if (nseg < 1 || nseg > kMaxSegments) return LLAMA_E_SHAPE;
+  int S = 0;
+  for (int i = 0; i < nseg; ++i) S += segs[i].len;
   const int H = (int)d.dim, KW = (int)d.kvw, F = (int)d.f;
   const int mpad = gemm_tiled_rows(S);
   float *xs = x.at<float>(x.L.x);
@@ -552,12 +564,20 @@ int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int r
   pa.heads = (int)(d.kv * d.g);
   pa.half = (int)d.half;
   pa.max_seq = x.kv->max_seq;
-  pa.row = x.table ? 0 : row;
   pa.table = x.table;
+  pa.pages = x.pages;
   pa.npages = x.npages;
   pa.status = x.at<int>(x.L.status);
-  pa.pos0 = pos0;
   pa.S = S;
+  pa.nseg = nseg;
+  pa.seg_start[0] = 0;
+  pa.seg_tile[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    pa.seg_start[i + 1] = pa.seg_start[i] + segs[i].len;
+    pa.seg_tile[i + 1] = pa.seg_tile[i] + (segs[i].len + kPrefillQT - 1) / kPrefillQT;
+    pa.seg_pos0[i] = segs[i].pos0;
+    pa.seg_row[i] = segs[i].row;
+  }
   pa.rope_cs = x.at<float>(x.L.rope_cs);
   pa.rope_sn = x.at<float>(x.L.rope_sn);
   pa.out = att;
@@ -593,8 +613,16 @@ int run_prefill_rows(const Ctx &x, const int32_t *tokens, int S, int pos0, int r
       if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs))) return rc;
     }
   }
-  if (!want_head || (!logits && !next)) return LLAMA_OK;
-  return run_lm_head(x, xs + (size_t)(S - 1) * H, 0, logits, next);
+  if (!logits && !next) return LLAMA_OK;
+  // one LM head per finished piece; they share the argmax partials, in stream order
+  for (int i = 0; i < nseg; ++i) {
+    const int o = segs[i].out;
+    if (o < 0) continue;
+    rc = run_lm_head(x, xs + (size_t)(pa.seg_start[i + 1] - 1) * H, 0,
+                     logits ? logits + (size_t)o * d.vocab : nullptr, next ? next + o : nullptr);
+    if (rc) return rc;
+  }
+  return LLAMA_OK;
 }
 
 // One step for B rows at positions pos[b] of cache rows row0 + b.  want_head = run the LM head.
@@ -966,10 +994,8 @@ static int prefill_common(const Ctx &x, const int32_t *tokens, int32_t S, int32_
     // chunks of at most max_prefill positions, each attending to everything before it in the cache
     for (int32_t c0 = 0; c0 < S; c0 += x.ws->max_prefill) {
       const int32_t n = S - c0 < x.ws->max_prefill ? S - c0 : x.ws->max_prefill;
-      const bool last = c0 + n == S;
-      rc = run_prefill_rows(x, tokens + c0, n, pos0 + c0, row, last ? logits_last : nullptr, last ? next : nullptr,
-                            last);
-      if (rc) return rc;
+      const PackSeg piece = {row, pos0 + c0, n, c0 + n == S ? 0 : -1};
+      if ((rc = run_prefill_pass(x, tokens + c0, &piece, 1, logits_last, next))) return rc;
     }
     return LLAMA_OK;
   }
@@ -1047,6 +1073,86 @@ int llama_prefill_paged(const llama_cfg *c, const llama_weights *w, const llama_
   x.pages = pages;
   x.npages = kv->max_seq / kPageSize;
   return prefill_common(x, tokens, S, pos0, 0, logits_last, next);
+}
+
+int llama_prefill_packed(const llama_cfg *c, const llama_weights *w, const llama_kv *kv, const int32_t *table,
+                         int32_t pages, const int32_t *tokens, int32_t nseg, const int32_t *seg_row,
+                         const int32_t *seg_pos0, const int32_t *seg_len, float *logits, int32_t *next,
+                         const llama_ws *ws, void *stream) {
+  if (!kv || !tokens || !w || !ws || !seg_pos0 || !seg_len || (!table && !seg_row)) return LLAMA_E_NULL;
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  if ((rc = check_kv(c, kv))) return rc;
+  if (table && (rc = check_paging(c, kv, table, pages))) return rc;
+  if (nseg < 1 || nseg > kMaxSegments) return LLAMA_E_SHAPE;
+  const int64_t room = table ? (int64_t)pages * kPageSize : (int64_t)kv->max_seq;
+  int64_t total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (seg_len[i] <= 0) return LLAMA_E_SHAPE;
+    if (!table && (seg_row[i] < 0 || seg_row[i] >= kv->rows)) return LLAMA_E_SHAPE;
+    if (seg_pos0[i] < 0 || (int64_t)seg_pos0[i] + seg_len[i] > room) return LLAMA_E_POS;
+    total += seg_len[i];
+  }
+  if (total > INT32_MAX) return LLAMA_E_SHAPE;
+  if (logits && ((uintptr_t)logits & 3u)) return LLAMA_E_SHAPE;
+  Ctx x;
+  if ((rc = make_ctx(c, w, kv, ws, stream, &x))) return rc;
+  for (int i = 0; i < nseg; ++i)
+    if ((int64_t)seg_pos0[i] + seg_len[i] > ws->max_seq) return LLAMA_E_POS;
+  if (table) {
+    x.table = table;
+    x.pages = pages;
+    x.npages = kv->max_seq / kPageSize;
+  }
+  const Dims &d = x.d;
+  if (!(prefill_tiled_ok(c) && ws->max_prefill >= 2)) {
+    // no matrix-core prefill for this config: segment after segment through the per-prompt path
+    const int32_t *tok = tokens;
+    for (int i = 0; i < nseg; ++i) {
+      Ctx xs = x;
+      if (table) xs.table = table + (size_t)i * pages;
+      rc = prefill_common(xs, tok, seg_len[i], seg_pos0[i], table ? 0 : seg_row[i],
+                          logits ? logits + (size_t)i * d.vocab : nullptr, next ? next + i : nullptr);
+      if (rc) return rc;
+      tok += seg_len[i];
+    }
+    return LLAMA_OK;
+  }
+  // passes of at most max_prefill packed positions; a segment that does not fit continues in the next
+  // pass (its later positions attend to the earlier ones through the cache)
+  PackSeg piece[kMaxSegments];
+  int np = 0, fill = 0, seg = 0, done = 0;  // done: positions of segment `seg` already in a pass
+  const int32_t *pass_tokens = tokens;
+  while (seg < nseg) {
+    const int take = std::min(seg_len[seg] - done, ws->max_prefill - fill);
+    const bool ends = done + take == seg_len[seg];
+    piece[np++] = {table ? seg : seg_row[seg], seg_pos0[seg] + done, take, ends ? seg : -1};
+    fill += take;
+    done += take;
+    if (ends) {
+      ++seg;
+      done = 0;
+    }
+    if (fill == ws->max_prefill || seg == nseg) {
+      if (fill == 1) {
+        // a one-position pass: the decode kernels
+        const PackSeg &p = piece[0];
+        Ctx xs = x;
+        if (table) xs.table = table + (size_t)p.row * pages;
+        const bool head = p.out >= 0;
+        rc = run_step(xs, pass_tokens, &p.pos0, 1, table ? 0 : p.row,
+                      head && logits ? logits + (size_t)p.out * d.vocab : nullptr, head && next ? next + p.out : nullptr,
+                      head, nullptr);
+      } else {
+        rc = run_prefill_pass(x, pass_tokens, piece, np, logits, next);
+      }
+      if (rc) return rc;
+      pass_tokens += fill;
+      np = 0;
+      fill = 0;
+    }
+  }
+  return LLAMA_OK;
 }
 
 int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidden, int32_t B, float *logits,

@@ -387,20 +387,45 @@ struct AttnArgs {
 };
 
 // Prefill of S positions of one cache row (bf16 cache): RoPE + append and causal attention
+// Prompts packed end to end (nest card `prefill_packed` / `prefill_paged`): the pass's S positions are
+// nseg segments, segment s being packed rows seg_start[s] .. seg_start[s+1]-1, consecutive positions
+// seg_pos0[s] .. of one request, whose keys and values go to cache row seg_row[s] (or, paged, to the pool
+// slots of table row seg_row[s]) and whose queries attend over that request's positions 0 .. their own.
+constexpr int kMaxSegments = 64;
+constexpr int kPrefillQT = 32;  // query positions per prefill attention block
 struct PrefillArgs {
   float *qkv;          // [S][qkv_stride]: q [dim] (rotated in place), k [kvw], v [kvw]
   int qkv_stride;
   bf16_t *kc, *vc;     // this layer's cache: [rows][kv][max_seq][head]
-  int kv, g, heads, half, max_seq, row, pos0, S;
+  int kv, g, heads, half, max_seq, S;
   const float *rope_cs, *rope_sn;  // [max_seq][half]
   float *out;          // [S][out_stride] attention output, heads concatenated
   int out_stride;
   float scale;         // 1/sqrt(head)
-  // paged cache: `row` is 0 and position p lies at pool position page_slot(table, p)
+  // paged cache: every segment's cache row is 0 and its position p lies at pool position
+  // page_slot(table + seg_row[s] * pages, p)
   const int32_t *table;
-  int npages;
+  int pages, npages;
   int *status;
+  int nseg;
+  int seg_start[kMaxSegments + 1];  // seg_start[0] = 0, seg_start[nseg] = S
+  int seg_tile[kMaxSegments + 1];   // first query tile of each segment; seg_tile[nseg] = all tiles
+  int seg_pos0[kMaxSegments];
+  int seg_row[kMaxSegments];
 };
+
+// the segment holding packed index i of a sorted start list (start[0] = 0, n >= 1 entries)
+__device__ __forceinline__ int segment_of(const int *start, int n, int i) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (i >= start[mid])
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
 
 // Kernel timing: when the host sets `start`/`stop`, the next launch records them from its own dispatch
 // packet (hipExtLaunchKernel), so they bracket exactly the kernel's execution; a launcher that issues

@@ -268,16 +268,19 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
 }
 
 // ------------------------------------------------------------------ RoPE + cache append ----
-// Block i = prompt position pos0 + i: the query heads are rotated in place in the qkv rows; the key
-// heads are rotated and, with the value heads, stored at that position of the cache (bf16 with
-// round-to-nearest-even).  Each pair (d, d + half) uses rot_lo / rot_hi (main.bend rope) with the
-// position's cos/sin from the table.
+// Block i = packed row i, position p of its segment's request: the query heads are rotated in place in
+// the qkv rows; the key heads are rotated and, with the value heads, stored at that position of the
+// request's cache (bf16 with round-to-nearest-even).  Each pair (d, d + half) uses rot_lo / rot_hi
+// (main.bend rope) with the position's cos/sin from the table.
 __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
-  const int i = blockIdx.x, p = a.pos0 + i;
+  const int i = blockIdx.x;
+  const int sg = segment_of(a.seg_start, a.nseg, i);
+  const int p = a.seg_pos0[sg] + i - a.seg_start[sg];
+  const int crow = a.table ? 0 : a.seg_row[sg];
   const int half = a.half, D = 2 * half;
-  // the cache slot of position p: itself in row a.row, or its place in the page pool (row 0); an entry
+  // the cache slot of position p: itself in row crow, or its place in the page pool (row 0); an entry
   // outside the pool writes no key or value
-  const int slot = a.table ? page_slot(a.table, p, a.npages, a.status) : p;
+  const int slot = a.table ? page_slot(a.table + (size_t)a.seg_row[sg] * a.pages, p, a.npages, a.status) : p;
   float *row = a.qkv + (size_t)i * a.qkv_stride;
   const float *cs = a.rope_cs + (size_t)p * half, *sn = a.rope_sn + (size_t)p * half;
   const int nq = a.heads * half, nk = a.kv * half;
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
       src[d] = nlo;
       src[d + half] = nhi;
     } else if (slot >= 0) {
-      bf16_t *kd = a.kc + ((size_t)(a.row * a.kv + h) * a.max_seq + slot) * D;
+      bf16_t *kd = a.kc + ((size_t)(crow * a.kv + h) * a.max_seq + slot) * D;
       kd[d] = f32_to_bf16(nlo);
       kd[d + half] = f32_to_bf16(nhi);
     }
@@ -301,20 +304,22 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
   const float *v = row + a.heads * D + a.kv * D;
   for (int k = threadIdx.x; k < a.kv * D; k += kThreads) {
     const int h = k / D, d = k - h * D;
-    a.vc[((size_t)(a.row * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(v[k]);
+    a.vc[((size_t)(crow * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(v[k]);
   }
 }
 
 // ------------------------------------------------------------------ causal attention ----
-// Block (query tile qt of 32 positions, kv head j, head quarter z): wave w takes query head
-// j*g + 4z + w (idle when that is >= g; it still helps stage the tiles).  Per key tile of 64 positions:
+// Block (query tile of 32 consecutive positions of one segment, kv head j, head quarter z): wave w takes
+// query head j*g + 4z + w (idle when that is >= g; it still helps stage the tiles); the keys are the
+// segment's request's positions 0 .. the query's own, from its cache row or its pages.  Per key tile of
+// 64 positions:
 //   S^T[key][q] = K Q^T (K from LDS as the A operand, the wave's rotated queries as bf16 hi + lo B
 //   fragments held in registers), so each lane owns one query column: 32 of the tile's 64 scores, the
 //   other 32 in lane ^ 32.  Softmax with a running maximum in base 2 (scores times scale * log2(e)).
 //   O^T[d][q] += V^T P^T: P^T is the score accumulator itself, split into bf16 hi + lo; the 16 keys a
 //   B fragment covers are taken in the order the accumulator holds them (a sum does not care), and
 //   V^T fragments are read from an LDS copy of V stored transposed, in the same key order.
-constexpr int kQT = 32;   // query positions per block
+constexpr int kQT = kPrefillQT;  // query positions per block
 constexpr int kKT = 64;   // key positions per tile
 
 template <int D>
@@ -333,23 +338,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t s_k[2][kKT * F::KROW];   // double buffered
   __shared__ __attribute__((aligned(16))) bf16_t s_vt[2][D * F::VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nqt = gridDim.x;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // the longest tiles first
+  // query tile: the tiles of the segments in order (each segment's own tiles of kQT positions, the last
+  // one ragged), taken from the end so that the longest tiles start first
+  const int tile_id = (int)gridDim.x - 1 - (int)blockIdx.x;
+  const int sg = segment_of(a.seg_tile, a.nseg, tile_id);
+  const int qt = tile_id - a.seg_tile[sg];
+  const int r0 = a.seg_start[sg], len = a.seg_start[sg + 1] - r0, pos0 = a.seg_pos0[sg];
+  const int crow = a.table ? 0 : a.seg_row[sg];
+  const int32_t *tr = a.table ? a.table + (size_t)a.seg_row[sg] * a.pages : nullptr;
   const int j = blockIdx.y;
   const int hi_in_group = blockIdx.z * 4 + wave;
   const bool active = hi_in_group < a.g;
   const int head = j * a.g + (active ? hi_in_group : 0);
   const int l32 = lane & 31, hsel = lane >> 5;
-  const int q_i = qt * kQT + l32;                 // prompt index of this lane's query
-  const int q_pos = a.pos0 + min(q_i, a.S - 1);   // its cache position (tail lanes repeat the last)
-  const int last_pos = a.pos0 + min(qt * kQT + kQT - 1, a.S - 1);
-  const bf16_t *Kh = a.kc + (size_t)(a.row * a.kv + j) * a.max_seq * D;
-  const bf16_t *Vh = a.vc + (size_t)(a.row * a.kv + j) * a.max_seq * D;
+  const int q_i = qt * kQT + l32;                     // index of this lane's query in its segment
+  const int q_row = r0 + min(q_i, len - 1);           // its packed row (tail lanes repeat the last)
+  const int q_pos = pos0 + min(q_i, len - 1);         // its cache position
+  const int last_pos = pos0 + min(qt * kQT + kQT - 1, len - 1);
+  const bf16_t *Kh = a.kc + (size_t)(crow * a.kv + j) * a.max_seq * D;
+  const bf16_t *Vh = a.vc + (size_t)(crow * a.kv + j) * a.max_seq * D;
 
   // the wave's rotated queries as B fragments: lane holds q[q_i][16 ks + 8 hsel .. +8], hi and lo
   u32x4 qh[F::KS], ql[F::KS];
   {
-    const float *q = a.qkv + (size_t)min(q_i, a.S - 1) * a.qkv_stride + head * D;
+    const float *q = a.qkv + (size_t)q_row * a.qkv_stride + head * D;
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks) {
       const float4 v0 = *reinterpret_cast<const float4 *>(q + ks * 16 + hsel * 8);
@@ -384,8 +396,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   static_assert(kKT == kPageSize, "a key tile is one page");
   auto fetch = [&](int k0) {
     int base = k0;  // cache slot of position k0
-    if (a.table) {
-      const int sl = page_slot(a.table, k0, a.npages, a.status);
+    if (tr) {
+      const int sl = page_slot(tr, k0, a.npages, a.status);
       base = sl < 0 ? 0 : sl;
     }
 #pragma unroll
@@ -500,9 +512,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
     __syncthreads();
   }
 
-  if (active && q_i < a.S) {
+  if (active && q_i < len) {
     const float inv = 1.0f / l_run;
-    float *out = a.out + (size_t)q_i * a.out_stride + head * D;
+    float *out = a.out + (size_t)q_row * a.out_stride + head * D;
 #pragma unroll
     for (int t = 0; t < F::DT; ++t)
 #pragma unroll
@@ -511,12 +523,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
 }
 
 hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last) {
+  if (a.nseg < 1 || a.nseg > kMaxSegments || a.seg_start[a.nseg] != a.S) return hipErrorInvalidValue;
   launch(k_rope_rows, dim3(a.S), dim3(kThreads), s, first, last, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last) {
-  const dim3 g((a.S + kQT - 1) / kQT, a.kv, (a.g + 3) / 4);
+  if (a.nseg < 1 || a.nseg > kMaxSegments || a.seg_start[a.nseg] != a.S) return hipErrorInvalidValue;
+  const dim3 g(a.seg_tile[a.nseg], a.kv, (a.g + 3) / 4);
   if (a.half == 64)
     launch(k_attn_prefill<128>, g, dim3(kThreads), s, first, last, a);
   else if (a.half == 32)

@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
                  "llama_workspace_bytes", "llama_workspace_init", "llama_status", "llama_strerror",
                  "llama_decode_step_traced", "llama_trace_floats", "llama_abi_version", "llama_sample",
                  "llama_sample_scratch_bytes", "llama_decode_step_paged", "llama_prefill_paged",
-                 "llama_generate_until"):
+                 "llama_generate_until", "llama_prefill_packed"):
         assert need in names, need
 
 
@@ -229,3 +229,38 @@ def test_paged_calls_reject_before_any_device_work(L):
     assert pf(4, -1) == lm.E_POS
     assert pf(4, 252) == lm.E_WORKSPACE
     assert L.llama_strerror(lm.E_PAGE)
+
+
+def test_packed_prefill_rejects_before_any_device_work(L):
+    """llama_prefill_packed's argument errors, decided on the host from the segment lists (fake device
+    pointers are never read)."""
+    fake = 1 << 40
+    ws = lm.llama_ws(fake, 1 << 30, 4, 1024, 256, 0, 0)  # never initialised: reached only after the checks
+    cfg = configs.truncated(configs.LLAMA31_8B, 1)
+    c = _c(cfg)
+    kv = lm.llama_kv(fake, fake, 3, 1024, cfg.layers, cfg.kv, 2 * cfg.half, lm.BF16)
+    lw = (lm.llama_layer_w * cfg.layers)()
+    for l in range(cfg.layers):
+        for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "w_gate", "w_up", "w_down"):
+            setattr(lw[l], f, fake)
+    w = lm.llama_weights(fake, fake, fake, lw)
+
+    def pk(segs, table=None, pages=0, rows=True, logits=None):
+        n = len(segs)
+        arr = lambda k: (ctypes.c_int32 * max(n, 1))(*[int(s[k]) for s in segs])
+        return L.llama_prefill_packed(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), table, pages, fake, n,
+                                      arr(0) if rows else None, arr(1), arr(2), logits, None, ctypes.byref(ws), None)
+
+    assert pk([(0, 0, 4)], rows=False) == lm.E_NULL           # contiguous rows need seg_row
+    assert pk([]) == lm.E_SHAPE
+    assert pk([(0, 0, 1)] * 65) == lm.E_SHAPE                 # at most 64 segments
+    assert pk([(0, 0, 4), (1, 0, 0)]) == lm.E_SHAPE           # empty segment
+    assert pk([(0, 0, 4), (3, 0, 4)]) == lm.E_SHAPE           # row outside the cache
+    assert pk([(0, 0, 4), (1, -1, 4)]) == lm.E_POS
+    assert pk([(0, 0, 4), (2, 1021, 4)]) == lm.E_POS          # past max_seq 1024
+    assert pk([(0, 0, 4)], logits=fake + 2) == lm.E_SHAPE     # misaligned logits
+    assert pk([(0, 0, 4), (1, 1020, 4), (0, 4, 9)]) == lm.E_WORKSPACE  # valid; uninitialised workspace
+    # paged: segment s is table row s, seg_row unread; room = pages * 64
+    assert pk([(0, 0, 4)], table=fake, pages=0, rows=False) == lm.E_SHAPE
+    assert pk([(0, 250, 7)], table=fake, pages=4, rows=False) == lm.E_POS
+    assert pk([(0, 250, 6), (9, 0, 5)], table=fake, pages=4, rows=False) == lm.E_WORKSPACE
