@@ -223,6 +223,276 @@ __global__ __launch_bounds__(kThreads) void k_tiled_reduce(GemmArgs a, int S) {
   }
 }
 
+// ------------------------------------------------------------------ large-tile product ----
+// Long prompts (M of at least 1024 rows): 256x256 block tiles, 8 waves of 64x128 (2x4 MFMA 32x32x16
+// tiles, the same per-wave work as k_gemm_tiled), one block per CU.  The operand tiles of a K step (A hi,
+// A lo, B: 256 rows x 32 bf16 each, 48 KB) go from global memory straight into LDS (global_load_lds, 16
+// bytes a lane, no registers), three stages deep, so a step's loads are issued two steps before it is
+// multiplied.  A row of a tile is 64 bytes = 4 chunks of 16; chunk c of row r is stored at position
+// c ^ ((r / 4) % 4): the loads write whole 1 KB runs, and the MFMA operand reads (32 rows, one chunk
+// each, two chunks a lane pair) run at the conflict-free rate (measured: 6.6 cycles per wavefront read
+// on this layout and on 80-byte padded rows, 17 on plain 64-byte rows, ~8.7 for swizzles that use row
+// bit 1).  Blocks map to tiles in groups of 4 M x 8
+// N tiles, one group per XCD at a time, so the operands a group shares stay in that XCD's L2.
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kBWaves = 8;  // waves of the large-tile kernel (4 or 8; measured the same)
+constexpr int kBTile = kBM * kBK;       // bf16 per operand tile of a stage
+constexpr int kBGroupM = 4, kBGroupN = 8, kXcds = 8;
+
+__device__ __forceinline__ int bswz(int row) { return (row >> 2) & 3; }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at LDS byte address
+// lds + 16 l (lds is the same for the whole wavefront, passed in M0).  Issued as inline assembly: the
+// compiler then adds no wait of its own for these loads (it cannot tell which stage buffer a pending one
+// writes at the loop head, and would wait for all); the kernel waits for them explicitly (wait_vm).  M0
+// is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(const bf16_t *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)(p);
+}
+
+// s_waitcnt for at most N vector-memory operations in flight and no LDS operation in flight (gfx9
+// encoding; expcnt left at its maximum)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// the workgroup barrier without a memory fence, after wait_vm: every wave's loads into the stage about to
+// be read are complete and every wave's reads of earlier stages have returned (so a buffer refilled after
+// the barrier is no longer being read); the compiler may not move memory accesses across it (it may move
+// the products, which only touch registers)
+__device__ __forceinline__ void bar_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct BigPlan {
+  int mt, nt, groups_m, groups_n, blocks, kslices;
+};
+
+static BigPlan big_plan(int M, int N, int K, bool swiglu) {
+  BigPlan p;
+  const int tn = swiglu ? kBN / 2 : kBN;
+  p.mt = (M + kBM - 1) / kBM;
+  p.nt = (N + tn - 1) / tn;
+  p.groups_m = (p.mt + kBGroupM - 1) / kBGroupM;
+  p.groups_n = (p.nt + kBGroupN - 1) / kBGroupN;
+  const int groups = (p.groups_m * p.groups_n + kXcds - 1) / kXcds * kXcds;
+  p.blocks = groups * kBGroupM * kBGroupN;
+  const int tiles = p.mt * p.nt, steps = K / kBK;
+  p.kslices = 1;
+  // one block per CU: at least two rounds of 256 tiles, keep at least 32 steps of K per slice
+  while (tiles * p.kslices < 512 && p.kslices < 8 && N % 2 == 0 && steps % (2 * p.kslices) == 0 &&
+         steps / (2 * p.kslices) >= 32)
+    p.kslices *= 2;
+  return p;
+}
+
+// NW waves: 8 (4 x 2 waves of 64 x 128, two per SIMD) or 4 (2 x 2 waves of 128 x 128, one per SIMD with
+// 256 accumulators, a quarter fewer operand reads per product)
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan plan) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int WM = NW / 2, TMW = kBM / WM, MI = TMW / 32;  // waves along M, rows per wave, 32-row tiles
+  constexpr int SPW = 16 / NW, LPW = 3 * SPW;                  // 1 KB segments per operand, loads per wave
+  // three stages, each [A hi | A lo | B]
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[3 * kBTile];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[3 * kBTile];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[3 * kBTile];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile of this block: XCD x (= block % 8) takes groups x, x + 8, ...; a group is 4 M x 8 N tiles
+  const int b = blockIdx.x, x = b % kXcds, l = b / kXcds;
+  const int gi = (l / (kBGroupM * kBGroupN)) * kXcds + x, w = l % (kBGroupM * kBGroupN);
+  const int tm = (gi % plan.groups_m) * kBGroupM + w % kBGroupM;
+  const int tnn = (gi / plan.groups_m) * kBGroupN + w / kBGroupM;
+  if (tm >= plan.mt || tnn >= plan.nt) return;
+  const int m0 = tm * kBM;
+  const int n0 = tnn * (SW ? kBN / 2 : kBN);
+
+  // this thread's LPW 16-byte loads of a stage: wave segment g = part * NW + wave (1 KB = 16 rows) of
+  // operand o (0 A hi, 1 A lo, 2 B); lane -> row 16 g + lane / 4, stored position lane % 4
+  const bf16_t *gp[LPW];
+  uint32_t lo[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int o = i / SPW, g = (i % SPW) * NW + wave;
+    const int row = g * 16 + (lane >> 2), c = (lane & 3) ^ bswz(row);
+    lo[i] = (uint32_t)(o * kBTile + g * 512) * 2;  // byte offset of the wavefront's 1 KB within the stage
+    if (o < 2) {
+      const int t = min(m0 + row, a.M - 1);
+      gp[i] = (o ? a.xlo : a.xhi) + (size_t)t * a.ldx + c * 8;
+    } else if (SW) {
+      const int n = min(n0 + (row & 127), a.N - 1);
+      gp[i] = reinterpret_cast<const bf16_t *>(row < 128 ? a.w[0] : a.w[1]) + (size_t)n * a.K + c * 8;
+    } else {
+      const int n = min(n0 + row, a.N - 1);
+      const int seg = n >= a.rs[2] ? 2 : (n >= a.rs[1] ? 1 : 0);
+      gp[i] = reinterpret_cast<const bf16_t *>(a.w[seg]) + (size_t)(n - a.rs[seg]) * a.K + c * 8;
+    }
+  }
+  // K slice blockIdx.y of gridDim.y
+  const int nst = a.K / kBK / (int)gridDim.y;
+  const int kz = (int)blockIdx.y * nst * kBK;
+  const uint32_t sb0 = lds_addr(st0), sb1 = lds_addr(st1), sb2 = lds_addr(st2);
+  auto issue = [&](uint32_t stage, int k) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) lds_load16(gp[i] + kz + k, stage + lo[i]);
+  };
+
+  f32x16 acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int l32 = lane & 31, hsel = lane >> 5;
+  int arow[MI], brow[4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) arow[i] = wm * TMW + i * 32 + l32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    brow[j] = SW ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32) : (wn * 128 + j * 32 + l32);
+  // the operand reads of the step's second half are issued while its first half multiplies, so only the
+  // first reads' latency is exposed (at most 15 LDS reads can be counted in flight, hence two groups)
+  auto compute = [&](const bf16_t *stage) {
+    u32x4 ah[2][MI], al[2][MI], bf[2][4];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = kk * 2 + hsel;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[kk][j] = *reinterpret_cast<const u32x4 *>(stage + 2 * kBTile + brow[j] * kBK + ((c ^ bswz(brow[j])) << 3));
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int off = arow[i] * kBK + ((c ^ bswz(arow[i])) << 3);
+        ah[kk][i] = *reinterpret_cast<const u32x4 *>(stage + off);
+        al[kk][i] = *reinterpret_cast<const u32x4 *>(stage + kBTile + off);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ah[kk][i], bf[kk][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(al[kk][i], bf[kk][j], acc[i][j]);
+    }
+    // schedule: the first half's reads, a quarter of the products, the second half's reads, the rest
+    constexpr int R = 2 * MI + 4, P = 8 * MI;
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, P / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, P + P / 2, 0);
+  };
+  // step t multiplies stage t % 3; its loads were issued two steps earlier.  At step t the wave waits
+  // for its own loads of stage t (those of stage t + 1, issued later, may still be in flight), then the
+  // barrier makes every wave's part visible and ends every read of stage t - 1, whose buffer the loads
+  // of stage t + 2 then refill.
+  issue(sb0, 0);
+  if (nst > 1) issue(sb1, kBK);
+  // steady state (every step refills): straight-line code, so the compiler's own wait for loads into
+  // LDS sees which buffer each pending load writes and adds none
+  int t = 0;
+  for (; t + 4 < nst; t += 3) {
+    wait_vm<LPW>();
+    bar_nofence();
+    issue(sb2, (t + 2) * kBK);
+    compute(st0);
+    wait_vm<LPW>();
+    bar_nofence();
+    issue(sb0, (t + 3) * kBK);
+    compute(st1);
+    wait_vm<LPW>();
+    bar_nofence();
+    issue(sb1, (t + 4) * kBK);
+    compute(st2);
+  }
+  // the last two to four steps (stages t and t + 1 are in st0 and st1)
+  auto step = [&](const bf16_t *cur, uint32_t refill, int u) {
+    if (u + 1 < nst)
+      wait_vm<LPW>();
+    else
+      wait_vm<0>();
+    bar_nofence();
+    if (u + 2 < nst) issue(refill, (u + 2) * kBK);
+    compute(cur);
+  };
+  for (; t < nst; t += 3) {
+    step(st0, sb2, t);
+    if (t + 1 < nst) step(st1, sb0, t + 1);
+    if (t + 2 < nst) step(st2, sb1, t + 2);
+  }
+
+  // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile
+  if (gridDim.y > 1) {
+    const int nout = SW ? 2 * a.N : a.N;
+    float *pz = a.part + (size_t)blockIdx.y * a.M * nout;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + wm * TMW + i * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+        if (t >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = SW ? n0 + wn * 64 + (j & 1) * 32 + l32 : n0 + wn * 128 + j * 32 + l32;
+          if (n < a.N) pz[(size_t)t * nout + (SW && j >= 2 ? a.N : 0) + n] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = m0 + wm * TMW + i * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+      if (t >= a.M) continue;
+      if (SW) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int n = n0 + wn * 64 + jj * 32 + l32;
+          if (n < a.N) {
+            const float gt = acc[i][jj][r], up = acc[i][2 + jj][r];
+            a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 128 + j * 32 + l32;
+          if (n >= a.N) continue;
+          float *y = a.y + (size_t)t * a.ldy + n;
+          if (EPI == EPI_RESID)
+            *y = a.res[(size_t)t * a.ldres + n] + acc[i][j][r];
+          else
+            *y = acc[i][j][r];
+        }
+      }
+    }
+}
+
+// the large-tile kernel for M of at least 1024 rows and enough tiles for the chip
+static bool use_big(int M, int N, int K, bool swiglu) {
+  if (M < 1024 || K % kBK != 0) return false;
+  const BigPlan p = big_plan(M, N, K, swiglu);
+  return p.mt * p.nt * p.kslices >= 512;
+}
+
 int gemm_tiled_rows(int M) { return (M + kTM - 1) / kTM * kTM; }
 
 int gemm_tiled_kslices(int M, int N, int K, bool swiglu) {
@@ -235,7 +505,7 @@ int gemm_tiled_kslices(int M, int N, int K, bool swiglu) {
 }
 
 size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu) {
-  const int ks = gemm_tiled_kslices(M, N, K, swiglu);
+  const int ks = use_big(M, N, K, swiglu) ? big_plan(M, N, K, swiglu).kslices : gemm_tiled_kslices(M, N, K, swiglu);
   return ks > 1 ? (size_t)ks * M * (swiglu ? 2 * (size_t)N : (size_t)N) : 0;
 }
 
@@ -244,9 +514,33 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
   GemmArgs a = a0;
   const int mt = (a.M + kTM - 1) / kTM;
   const bool sw = epi == EPI_SWIGLU;
+  const dim3 rg((a.N / 2 + kThreads - 1) / kThreads, a.M);
+  if (use_big(a.M, a.N, a.K, sw)) {
+    BigPlan p = big_plan(a.M, a.N, a.K, sw);
+    if (!a.part) p.kslices = 1;
+    a.kslices = p.kslices;
+    const int ks = a.kslices;
+    const dim3 g(p.blocks, ks);
+    switch (epi) {
+      case EPI_STORE:
+        launch(k_gemm_big<EPI_STORE, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
+        break;
+      case EPI_RESID:
+        launch(k_gemm_big<EPI_RESID, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
+        break;
+      case EPI_SWIGLU:
+        launch(k_gemm_big<EPI_SWIGLU, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   a.kslices = a.part ? gemm_tiled_kslices(a.M, a.N, a.K, sw) : 1;
   const int ks = a.kslices;
-  const dim3 rg((a.N / 2 + kThreads - 1) / kThreads, a.M);
   switch (epi) {
     case EPI_STORE:
       launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, false, last && ks == 1, a);

@@ -4,7 +4,8 @@ The prompt's positions go through each layer together: tiled MFMA products over 
 of every position, causal attention over the cache.  Compared with the oracle's position-by-position
 prefill: last-position logits within max|d| 2e-2, argmax equal outside near-ties, every appended K/V
 slot within bf16 rounding.  Cases cover ragged row tiles (S not a multiple of 128 or 32), a prompt that
-continues a filled cache (pos0 > 0), prompts longer than the workspace's chunk, and g = 3 / head 64.
+continues a filled cache (pos0 > 0), prompts longer than the workspace's chunk, g = 3 / head 64, and a
+2800-position prompt whose products take the 256x256-tile kernel (every epilogue, K split in slices).
 At the full 8B size the prefill is checked against the GPU's own decode path (prefill of S positions
 equals S decode steps), which the decode tests tie to the oracle.
 """
@@ -44,6 +45,7 @@ CASES = [
     ("llama31_8b", 2, 300, 0, 128, 1024),          # three chunks: 128, 128, 44
     ("smollm2_135m_bf16", 3, 257, 0, 512, 1024),   # g = 3, head 64
     ("llama31_8b", 1, 2, 5, 64, 256),              # the smallest prompt that takes this path
+    ("llama31_8b", 2, 2800, 0, 2800, 3072),        # large tiles (11 row tiles, the last ragged), split K
 ]
 
 
