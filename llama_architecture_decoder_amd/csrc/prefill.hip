@@ -232,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void k_tiled_reduce(GemmArgs a, int S) {
 // c ^ ((r / 4) % 4): the loads write whole 1 KB runs, and the MFMA operand reads (32 rows, one chunk
 // each, two chunks a lane pair) run at the conflict-free rate (measured: 6.6 cycles per wavefront read
 // on this layout and on 80-byte padded rows, 17 on plain 64-byte rows, ~8.7 for swizzles that use row
-// bit 1).  Blocks map to tiles in groups of 4 M x 8
-// N tiles, one group per XCD at a time, so the operands a group shares stay in that XCD's L2.
+// bit 1).  Tiles are ordered in groups of 4 M x 8 N tiles and each XCD takes an equal run of that
+// order, so the operands a group shares stay in that XCD's L2 and no XCD has more tiles than another.
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kBWaves = 8;  // waves of the large-tile kernel (4 or 8; measured the same)
 constexpr int kBTile = kBM * kBK;       // bf16 per operand tile of a stage
@@ -275,7 +275,7 @@ __device__ __forceinline__ void bar_nofence() {
 }
 
 struct BigPlan {
-  int mt, nt, groups_m, groups_n, blocks, kslices;
+  int mt, nt, groups_m, groups_n, per_xcd, blocks, kslices;
 };
 
 static BigPlan big_plan(int M, int N, int K, bool swiglu) {
@@ -285,8 +285,9 @@ static BigPlan big_plan(int M, int N, int K, bool swiglu) {
   p.nt = (N + tn - 1) / tn;
   p.groups_m = (p.mt + kBGroupM - 1) / kBGroupM;
   p.groups_n = (p.nt + kBGroupN - 1) / kBGroupN;
-  const int groups = (p.groups_m * p.groups_n + kXcds - 1) / kXcds * kXcds;
-  p.blocks = groups * kBGroupM * kBGroupN;
+  const int order = p.groups_m * p.groups_n * kBGroupM * kBGroupN;  // tiles in grouped order
+  p.per_xcd = (order + kXcds - 1) / kXcds;
+  p.blocks = p.per_xcd * kXcds;
   const int tiles = p.mt * p.nt, steps = K / kBK;
   p.kslices = 1;
   // one block per CU: at least two rounds of 256 tiles, keep at least 32 steps of K per slice
@@ -310,12 +311,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile of this block: XCD x (= block % 8) takes groups x, x + 8, ...; a group is 4 M x 8 N tiles
+  // tile of this block: the tiles in grouped order (groups of 4 M x 8 N tiles, M fastest inside a group)
+  // are cut into 8 equal runs; XCD x (= block % 8, the dispatch order) takes run x in order
   const int b = blockIdx.x, x = b % kXcds, l = b / kXcds;
-  const int gi = (l / (kBGroupM * kBGroupN)) * kXcds + x, w = l % (kBGroupM * kBGroupN);
+  const int q = x * plan.per_xcd + l;
+  const int gi = q / (kBGroupM * kBGroupN), w = q % (kBGroupM * kBGroupN);
   const int tm = (gi % plan.groups_m) * kBGroupM + w % kBGroupM;
   const int tnn = (gi / plan.groups_m) * kBGroupN + w / kBGroupM;
-  if (tm >= plan.mt || tnn >= plan.nt) return;
+  if (gi >= plan.groups_m * plan.groups_n || tm >= plan.mt || tnn >= plan.nt) return;
   const int m0 = tm * kBM;
   const int n0 = tnn * (SW ? kBN / 2 : kBN);
 
