@@ -554,50 +554,56 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
 // Merge of the chunk partials of one (row, kv head), in chunk order (a separate launch: the kernel
 // boundary makes the partials visible without cache-wide fences inside the attention kernel).
 // Block (og, j, b) produces 64 consecutive outputs of query head i = og*64/head of group j:
-// M = max_c m_c, w_c = exp(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L.  The 256 threads are
-// 4 chunk groups x 64 outputs; the 4 groups' sums are combined in a fixed order.
-template <int G, int D>
-__global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) {
-  constexpr int PER = 16;  // partials per thread loaded up front (chunks 0..63); more in a loop
+// M = max_c m_c, w_c = exp(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L.  The NW waves are NW
+// chunk groups x 64 outputs (wave w takes chunks w, w + NW, ...); their sums are combined in a fixed
+// order.  Every load is issued before the first use: NW * PER chunks in one memory round trip (NW = 16
+// for long contexts: 512 chunks took 34 us per layer in 8 rounds with 4 waves).
+template <int G, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
+  constexpr int NT = NW * 64;
+  constexpr int PER = NW >= 16 ? 32 : 16;  // partials per thread loaded up front; more in a loop
+  constexpr int MLR = (kAttnMaxChunks + NT - 1) / NT;
   const int og = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
   const int nact = t / chunk + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = (og * 64) / D, d = (og * 64) % D + lane;
   __shared__ float w_s[kAttnMaxChunks];
-  __shared__ float red[4];
-  __shared__ float acc_s[4][64];
+  __shared__ float red[NW];
+  __shared__ float acc_s[NW][64];
   const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
   const float *pml0 = a.part_ml + slot * (size_t)(G * 2);
   const float *po0 = a.part_o + slot * (size_t)(G * D);
-  // every load first: this thread's (m, l) of chunks tid, tid + 256 and its output's partial o of
-  // chunks wave, wave + 4, ..., wave + 60 (independent of the maxima: one memory round trip)
-  float mv[2], lv[2];
+  // every load first: this thread's (m, l) of chunks tid, tid + NT, ... and its output's partial o of
+  // chunks wave, wave + NW, ... (independent of the maxima: one memory round trip)
+  float mv[MLR], lv[MLR];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int cc = min(tid + k * kThreads, nact - 1);
+  for (int k = 0; k < MLR; ++k) {
+    const int cc = min(tid + k * NT, nact - 1);
     mv[k] = pml0[(size_t)cc * G * 2 + 2 * i];
     lv[k] = pml0[(size_t)cc * G * 2 + 2 * i + 1];
   }
   float ov[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int cc = wave + 4 * k;
+    const int cc = wave + NW * k;
     if (cc < nact) ov[k] = po0[(size_t)cc * G * D + i * D + d];
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (tid + k * kThreads < nact) M = fmaxf(M, mv[k]);
+  for (int k = 0; k < MLR; ++k)
+    if (tid + k * NT < nact) M = fmaxf(M, mv[k]);
   M = wave_max(M);
   if (lane == 0) red[wave] = M;
   lds_barrier();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
   lds_barrier();
   float L = 0.f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int cc = tid + k * kThreads;
+  for (int k = 0; k < MLR; ++k) {
+    const int cc = tid + k * NT;
     if (cc < nact) {
       const float w = __builtin_amdgcn_exp2f(mv[k] - M);  // maxima are in base 2
       w_s[cc] = w;
@@ -607,24 +613,31 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a, int chunk) 
   L = wave_sum(L);
   if (lane == 0) red[wave] = L;
   lds_barrier();
-  L = (red[0] + red[1]) + (red[2] + red[3]);
+  {
+    float s2 = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s2 += red[w];
+    L = s2;
+  }
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int cc = wave + 4 * k;
+    const int cc = wave + NW * k;
     if (cc < nact) acc = fmaf(w_s[cc], ov[k], acc);
   }
-  for (int base = 4 * PER; base < nact; base += 4 * PER) {
+  for (int base = NW * PER; base < nact; base += NW * PER) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int cc = base + wave + 4 * k;
+      const int cc = base + wave + NW * k;
       if (cc < nact) acc = fmaf(w_s[cc], po0[(size_t)cc * G * D + i * D + d], acc);
     }
   }
   acc_s[wave][lane] = acc;
   lds_barrier();
   if (wave == 0) {
-    const float sum = (acc_s[0][lane] + acc_s[1][lane]) + (acc_s[2][lane] + acc_s[3][lane]);
+    float sum = acc_s[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sum += acc_s[w][lane];
     a.out[(size_t)b * a.out_stride + (size_t)(j * G + i) * D + d] = sum / L;
   }
 }
@@ -709,8 +722,13 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
     else
       launch(k_attn<KT, D, G, false>, grid, dim3(kThreads), s, true, !merge, a);
   }
-  if (merge && !self)
-    launch(k_attn_merge<G, D>, dim3(G * D / 64, a.kv, B), dim3(kThreads), s, false, true, a, chunk);
+  if (merge && !self) {
+    const dim3 mg(G * D / 64, a.kv, B);
+    if (nch_launch > 64)
+      launch(k_attn_merge<G, D, 16>, mg, dim3(16 * 64), s, false, true, a, chunk);
+    else
+      launch(k_attn_merge<G, D, 4>, mg, dim3(kThreads), s, false, true, a, chunk);
+  }
   return hipGetLastError();
 }
 

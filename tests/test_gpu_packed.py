@@ -140,3 +140,35 @@ def test_packed_paged_shared_prefix_parity():
         written[s] = True
     assert np.array_equal(gk[:, 0, :, ~written, :], before_k[:, 0, :, ~written, :])
     assert np.array_equal(gv[:, 0, :, ~written, :], before_v[:, 0, :, ~written, :])
+
+
+@pytest.mark.timeout(600)
+def test_packed_f32_model_runs_segment_by_segment():
+    """An F32 model (no matrix-core prefill): the packed call runs each segment as its own prefill; logits
+    within the F32 tolerance, each segment's appended K/V within F32 rounding of the oracle's."""
+    import llama_architecture_decoder_amd as lm
+    cfg = configs.truncated(configs.SMOLLM2_135M, 3)
+    w = weights(cfg)
+    segs = [(1, 0, 9), (0, 4, 5), (2, 0, 1)]
+    rows, max_seq = 3, 64
+    om = oracle.Model(cfg, w, rows=rows, max_seq=max_seq)
+    synth.fill_cache_rows(cfg, om.kc, om.vc, 0, 4, cache_row=0)
+    dec = lm.Decoder(cfg, w, rows=rows, max_seq=max_seq)
+    dec.kv.k.copy_(torch.from_numpy(om.kc))
+    dec.kv.v.copy_(torch.from_numpy(om.vc))
+    toks = [synth.tokens(cfg, f"packed/f32/{i}", n) for i, (_, _, n) in enumerate(segs)]
+    logits = torch.empty((len(segs), cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(len(segs), dtype=torch.int32, device="cuda")
+    dec.prefill_packed(torch.from_numpy(np.concatenate(toks)).cuda(), segs, logits=logits, next_tok=nxt)
+    got, gid = logits.cpu().numpy(), nxt.cpu().numpy()
+    assert dec.status() == 0
+    for i, (r, p0, n) in enumerate(segs):
+        _, ref = om.prefill(toks[i], pos0=p0, row=r)
+        check_logits(cfg, got[i], ref, f"f32 segment {i}")
+        check_argmax(cfg, int(gid[i]), ref, f"f32 segment {i}")
+    torch.cuda.synchronize()
+    gk, gv = dec.kv.k.cpu().numpy(), dec.kv.v.cpu().numpy()
+    for r, p0, n in segs:
+        for nm, g, o in (("K", gk, om.kc), ("V", gv, om.vc)):
+            d = float(np.abs(g[:, r, :, p0:p0 + n] - o[:, r, :, p0:p0 + n]).max())
+            assert d <= 1e-4 * max(1.0, float(np.abs(o[:, r, :, p0:p0 + n]).max())), f"{nm} row {r}: {d}"
