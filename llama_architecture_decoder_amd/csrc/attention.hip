@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
 // M = max_c m_c, w_c = exp(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L.  The NW waves are NW
 // chunk groups x 64 outputs (wave w takes chunks w, w + NW, ...); their sums are combined in a fixed
 // order.  Every load is issued before the first use: NW * PER chunks in one memory round trip (NW = 16
-// for long contexts: 512 chunks took 34 us per layer in 8 rounds with 4 waves).
+// for one long row: 512 chunks took 34 us per layer in 8 rounds with 4 waves, 6.7 us in one with 16).
 template <int G, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
   constexpr int NT = NW * 64;
@@ -723,8 +723,10 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
       launch(k_attn<KT, D, G, false>, grid, dim3(kThreads), s, true, !merge, a);
   }
   if (merge && !self) {
+    // 16 waves only when the merge has fewer blocks than the chip has CUs (one row): at 32 rows (2048
+    // blocks of ~125 chunks) the 4-wave blocks were faster (11.8 vs 30.4 us per layer)
     const dim3 mg(G * D / 64, a.kv, B);
-    if (nch_launch > 64)
+    if (nch_launch > 64 && (long)mg.x * mg.y * mg.z < 256)
       launch(k_attn_merge<G, D, 16>, mg, dim3(16 * 64), s, false, true, a, chunk);
     else
       launch(k_attn_merge<G, D, 4>, mg, dim3(kThreads), s, false, true, a, chunk);
