@@ -528,7 +528,7 @@ def main():
                          "copy kernel of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build measures the single-GPU decode step "
+        print(f"bench.py runs on one GPU only: it measures the single-GPU decode step "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
         sys.exit(2)
 

@@ -90,7 +90,7 @@ int check_cfg(const llama_cfg *c) {
   }
   const Dims d = dims_of(c);
   if (d.dim > (1 << 20) || d.f > (1 << 22) || d.layers > 4096 || d.vocab > (1 << 26)) return LLAMA_E_CONFIG;
-  // what this build implements
+  // shapes the kernels are instantiated for
   if (!attention_supported((int)d.head, c->g)) return LLAMA_E_UNSUPPORTED;
   if (d.dim % 8 || d.f % 8) return LLAMA_E_UNSUPPORTED;
   if (!gemv_supported(c->weight_dtype, (int)d.dim) || !gemv_supported(c->weight_dtype, (int)d.f))
@@ -821,7 +821,7 @@ const char *llama_strerror(int code) {
     case LLAMA_E_NULL: return "required pointer is NULL";
     case LLAMA_E_WORKSPACE: return "workspace too small or not initialised for this config";
     case LLAMA_E_HIP: return "HIP runtime error";
-    case LLAMA_E_UNSUPPORTED: return "not supported by this build";
+    case LLAMA_E_UNSUPPORTED: return "not supported by this library";
     case LLAMA_E_PAGE: return "a page table entry outside the cache's page pool";
     default: return "unknown error";
   }
