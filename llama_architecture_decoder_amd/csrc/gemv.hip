@@ -79,29 +79,32 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 
   __shared__ float red[4][NV];
   __shared__ float ss_w[4];
+  // Every load below is unconditional (indices clamped, unwanted values zeroed afterwards): the wait
+  // counter then sees one straight sequence (cos/sin, x, gains, weights), so the norm prologue waits for
+  // x and the gains only, not for the weights behind them.
   __shared__ float rope_s[EPI == EPI_ROPE ? 2 * 64 : 1];  // cos | sin of the position (half <= 64)
-  if (EPI == EPI_ROPE && tid < 2 * a.ra.half) {
-    const size_t ci = (size_t)a.ra.pos[0] * a.ra.half + (tid % a.ra.half);
-    rope_s[tid] = tid < a.ra.half ? a.ra.rope_cs[ci] : a.ra.rope_sn[ci];
+  float rope_v = 0.f;
+  if (EPI == EPI_ROPE) {
+    // the table row of the position: cos for threads 0..half-1, sin for half..2*half-1 (pointers chosen
+    // from uniform values, the element index clamped)
+    const int hf = a.ra.half;
+    const float *tab = tid < hf ? a.ra.rope_cs : a.ra.rope_sn;
+    rope_v = tab[(size_t)a.ra.pos[0] * hf + min(tid < hf ? tid : tid - hf, hf - 1)];
   }
 
-  // ---- the input slice of this thread: chunks j*256 + tid
+  // ---- the input slice of this thread: chunks j*256 + tid (a chunk past K reads the last chunk and is
+  // zeroed)
   float xr[KCH][E];
 #pragma unroll
   for (int j = 0; j < KCH; ++j) {
-    const int ci = j * kThreads + tid;
-    if (ci < nchunk) {
+    const int ci = min(j * kThreads + tid, nchunk - 1);
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        float4 v = *reinterpret_cast<const float4 *>(a.x + (size_t)ci * E + e);
-        xr[j][e + 0] = v.x;
-        xr[j][e + 1] = v.y;
-        xr[j][e + 2] = v.z;
-        xr[j][e + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) xr[j][e] = 0.f;
+    for (int e = 0; e < E; e += 4) {
+      float4 v = *reinterpret_cast<const float4 *>(a.x + (size_t)ci * E + e);
+      xr[j][e + 0] = v.x;
+      xr[j][e + 1] = v.y;
+      xr[j][e + 2] = v.z;
+      xr[j][e + 3] = v.w;
     }
   }
   // the norm gains of the slice (also independent of everything else)
@@ -136,7 +139,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   // waits for x and the gains only, and the weights stream meanwhile)
   u32x4 wv[NV][KCH];
   int grp = blockIdx.x;
-  if (grp < a.ngroups) load_group(grp, wv);
+  load_group(min(grp, a.ngroups - 1), wv);  // the launch has at most one block per group
+#pragma unroll
+  for (int j = 0; j < KCH; ++j)
+    if (j * kThreads + tid >= nchunk)
+#pragma unroll
+      for (int e = 0; e < E; ++e) xr[j][e] = 0.f;
+  if (EPI == EPI_ROPE && tid < 2 * a.ra.half) rope_s[tid] = rope_v;  // published by the norm's barrier
 
   if (NORM) {
     // RMSNorm prologue: g * (x * (1 / sqrt(sum(x^2) / K + eps)))
