@@ -1,0 +1,132 @@
+"""Summaries of rocprofv3 output for the batch-1 decode benchmark (kernel trace statistics and HBM traffic).
+
+Usage (from the repository root, after the rocprofv3 runs given in profiles/decode_8b_hbm_traffic.md):
+
+    python -m llama_architecture_decoder_amd.rocprof_summary traffic <fetch_dir> <write_dir> [out.json]
+
+reads every ``*counter_collection.csv`` under the two directories (one FETCH_SIZE run, one WRITE_SIZE run of
+``bench.py --copy-probe``), averages each counter per kernel over its dispatches, scales the counts by what
+they read for the 1 GiB plain copy (``__amd_rocclr_copyBuffer``: 1 GiB fetched, 1 GiB written) and writes
+the per-launch traffic of the decode kernels with the hash of the sources it was measured on (bench.py
+reports ``traffic`` only while that hash still matches).
+
+    python -m llama_architecture_decoder_amd.rocprof_summary stats <kernel_stats.csv>
+
+prints the kernel table (calls, average and total duration, share) of a ``--kernel-trace --stats`` run as
+markdown.
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = ["llama_architecture_decoder_amd/csrc/gemv.hip", "llama_architecture_decoder_amd/csrc/common.h"]
+COPY = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+# decode kernels of the 8B shape (bf16 weights: k_gemv<unsigned short, KCH, EPI, NORM>)
+KERNELS = {
+    "gate_up": "k_gemv<unsigned short, 2, 2, true>",
+    "down": "k_gemv<unsigned short, 7, 1, false>",
+    "qkv": "k_gemv<unsigned short, 2, 4, true>",
+    "o_proj": "k_gemv<unsigned short, 2, 1, false>",
+    "lm_head": "k_gemv<unsigned short, 2, 3, true>",
+    "attention": "k_attn_mfma<128, 4, 64, false, false>",
+}
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_means(directory: str, counter: str, largest: str = ""):
+    """{kernel name: (dispatches, mean counter value)} over every counter CSV under `directory`; for the
+    kernel named `largest`, only its dispatches within 10% of its largest value (the 1 GiB copies, not the
+    small uploads the same copy kernel also serves)."""
+    per = defaultdict(dict)  # name -> dispatch id -> summed value (a counter may come in several rows)
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                d = (fn, row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                per[name][d] = per[name].get(d, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for k, v in per.items():
+        vals = list(v.values())
+        if largest and largest in k:
+            vals = [x for x in vals if x >= 0.9 * max(vals)]
+        out[k] = (len(vals), sum(vals) / len(vals))
+    return out
+
+
+def find(means, sub):
+    hits = [(k, v) for k, v in means.items() if sub in k]
+    if len(hits) != 1:
+        raise KeyError(f"{len(hits)} kernels match {sub!r}")
+    return hits[0][1]
+
+
+def traffic(fetch_dir: str, write_dir: str, out: str):
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import configs
+    cfg = configs.LLAMA31_8B
+    fm = counter_means(fetch_dir, "FETCH_SIZE", COPY)
+    wm = counter_means(write_dir, "WRITE_SIZE", COPY)
+    ff = COPY_BYTES / 1024 / find(fm, COPY)[1]
+    wf = COPY_BYTES / 1024 / find(wm, COPY)[1]
+    t_mean = cfg.kv_fill + 4  # the mean position of the 8 profiled steps after one warm-up step
+    rec = {"kernel": "gate_up", "sources": SOURCES, "sources_sha256_16": sources_hash(),
+           "fetch_factor": ff, "write_factor": wf, "per_launch": {}}
+    rows = []
+    for cls, sub in KERNELS.items():
+        n, fk = find(fm, sub)
+        _, wk = find(wm, sub)
+        tb = (fk * ff + wk * wf) * 1024
+        ab = bench.kernel_bytes(cfg, cls, t_mean)
+        rec["per_launch"][cls] = {"fetch_kib": fk, "write_kib": wk, "traffic_bytes": tb, "algorithmic_bytes": ab,
+                                  "dispatches": n}
+        rows.append(f"| {cls} (`{sub}`) | {n} | {fk:.1f} | {wk:.1f} | {tb:,.0f} | {ab:,} | {tb / ab:.3f} |")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"copy: FETCH_SIZE {find(fm, COPY)[1]:.1f} KiB, WRITE_SIZE {find(wm, COPY)[1]:.1f} KiB per 1 GiB dispatch "
+          f"({find(fm, COPY)[0]} dispatches): fetch factor {ff:.4f}, write factor {wf:.4f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic (scaled) bytes | algorithmic bytes | "
+          "traffic / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    print("\n".join(rows))
+
+
+def stats(fn: str):
+    with open(fn, newline="") as f:
+        rows = list(csv.DictReader(f))
+    print("| kernel | calls | average us | total ms | % of GPU time |")
+    print("|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"]
+        name = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+              f"{float(r['Percentage']):.2f} |")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 4 and sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3],
+                sys.argv[4] if len(sys.argv) > 4 else os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json"))
+    elif len(sys.argv) == 3 and sys.argv[1] == "stats":
+        stats(sys.argv[2])
+    else:
+        print(__doc__)
+        sys.exit(2)
