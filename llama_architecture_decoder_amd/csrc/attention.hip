@@ -583,11 +583,13 @@ __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
     mv[k] = pml0[(size_t)cc * G * 2 + 2 * i];
     lv[k] = pml0[(size_t)cc * G * 2 + 2 * i + 1];
   }
+  // (unconditional loads, chunks past the last clamped to it and unused: a load behind a branch would make
+  // the wait counter hold the later loads until it lands, two round trips instead of one)
   float ov[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int cc = wave + NW * k;
-    if (cc < nact) ov[k] = po0[(size_t)cc * G * D + i * D + d];
+    const int cc = min(wave + NW * k, nact - 1);
+    ov[k] = po0[(size_t)cc * G * D + i * D + d];
   }
   float M = -INFINITY;
 #pragma unroll
