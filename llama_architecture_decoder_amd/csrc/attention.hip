@@ -288,7 +288,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ matrix-core scores ----
-// k_attn_mfma (bf16 cache): each wavefront takes chunk/4 consecutive positions, in groups of 16.
+// k_attn_mfma (bf16 cache): each of the NW wavefronts takes chunk/NW consecutive positions, in groups of
+// 16.
 //   Scores: S[q][p] = Q K^T with v_mfma_f32_16x16x32_bf16, A = the group's query heads (rows q < g of
 //   16; the F32 queries as bf16 hi + lo, so the products are those of the F32 values to ~2^-17) and
 //   B = K^T (lane l: position l%16, 8 consecutive numbers at 8(l/16) of a 32-wide slice).  In large
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 //   Lane l then holds S[4(l/16) + r][l%16].
 //   Softmax pieces per head over the wave's positions (max by DPP within 16-lane rows), the weights go
 //   through LDS to the layout of the V loads (lane l: position l/LPR of PPI rows, numbers 8(l%LPR) .. +8),
-//   and the weighted V sum runs on the vector units.  The wave's lane groups and the 4 waves are combined
+//   and the weighted V sum runs on the vector units.  The wave's lane groups and the NW waves are combined
 //   through LDS in a fixed order, as in k_attn.
 typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
 typedef float af32x4 __attribute__((ext_vector_type(4)));
@@ -316,24 +317,26 @@ __device__ __forceinline__ void split8(const float (&f)[8], u32x4 &hi, u32x4 &lo
   lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
-template <int D, int G, int NPW_>
+template <int D, int G, int NPW_, int NW_ = 4>
 struct MfmaAttnShape {
+  static constexpr int NW = NW_;          // wavefronts per block
   static constexpr int NPW = NPW_;        // positions per wavefront
-  static constexpr int CHUNK = 4 * NPW;   // positions per block
+  static constexpr int CHUNK = NW * NPW;  // positions per block
   static constexpr int NGI = NPW / 16;    // 16-position score groups per wavefront
   static constexpr int KS = D / 32;       // 32-wide steps of a score
   static constexpr int LPR = D / 8;       // lanes per V row (16 bytes each)
   static constexpr int PPI = 64 / LPR;    // V rows per wavefront load
   static constexpr int NV = NPW / PPI;    // V loads per lane
   static constexpr int GP = G <= 4 ? 4 : 8;  // weights per position in LDS (padded)
-  static constexpr int NG = kThreads / LPR;  // lane groups per block
+  static constexpr int NG = NW * 64 / LPR;  // lane groups per block
   static constexpr int KROW = D + 8;      // LDS row of a wave's 16-key staging tile (bf16)
-  static constexpr size_t LDS = sizeof(float) * (4 * NPW * GP + 8 * G + (size_t)NG * G * D) + 2 * 4 * 16 * KROW;
+  static constexpr size_t LDS = sizeof(float) * (NW * NPW * GP + 2 * NW * G + (size_t)NG * G * D) + 2 * NW * 16 * KROW;
 };
 
-template <int D, int G, int NPW_, bool KROWS, bool SELF>
-__global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
-  using S = MfmaAttnShape<D, G, NPW_>;
+template <int D, int G, int NPW_, bool KROWS, bool SELF, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
+  using S = MfmaAttnShape<D, G, NPW_, NW>;
+  static_assert(!SELF || NW == 4, "the in-kernel merge runs on 4 wavefronts");
   constexpr int CHUNK = S::CHUNK, NPW = S::NPW, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
   constexpr int GP = S::GP, NG = S::NG;
   static_assert(G <= 8, "at most 8 query heads per kv head (two rows of the 16-row tile)");
@@ -345,10 +348,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   const int pw0 = c * CHUNK + wave * NPW;  // this wavefront's first position
   const int p1 = min(c * CHUNK + CHUNK, t + 1);
 
-  __shared__ __attribute__((aligned(16))) float p_s[4][NPW][GP];
-  __shared__ float m_s[4][G], l_s[4][G];
+  __shared__ __attribute__((aligned(16))) float p_s[NW][NPW][GP];
+  __shared__ float m_s[NW][G], l_s[NW][G];
   __shared__ __attribute__((aligned(16))) float o_g[NG][G][D];
-  __shared__ __attribute__((aligned(16))) bf16_t k_s[4][16 * S::KROW];  // each wave's 16 keys in turn
+  __shared__ __attribute__((aligned(16))) bf16_t k_s[NW][16 * S::KROW];  // each wave's 16 keys in turn
 
   const size_t head_off = ((size_t)(a.table ? 0 : a.row0 + b) * a.kv + j) * (size_t)a.max_seq * D;
   const bf16_t *Kh = reinterpret_cast<const bf16_t *>(a.kc) + head_off;
@@ -519,12 +522,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
   // (6) the waves combined (factor 2^(m_w - M), 0 for a wave without positions), lane groups summed in
   // a fixed order
   const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
     const int q = idx / D, d = idx % D;
-    const float M = fmaxf(fmaxf(m_s[0][q], m_s[1][q]), fmaxf(m_s[2][q], m_s[3][q]));
+    float M = m_s[0][q];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, m_s[w][q]);
     float acc = 0.f, L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = (m_s[w][q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][q] - M);
       float ow = 0.f;
 #pragma unroll
@@ -712,12 +717,14 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
   const bool self = merge && !separate && (long)nch_launch * G * D <= 4096;
   if constexpr (use_mfma<KT, D, G>()) {
     // keys as whole rows (through LDS) pay off when the launch streams many blocks per CU; a launch of
-    // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout
+    // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout, and with
+    // 8 wavefronts of 32 positions rather than 4 of 64 (same chunk; one row at 8K: 14.4 vs 14.6 us per
+    // layer with the merge)
     const bool krows = (long)B * a.kv * nch_launch >= 4096;
     if (krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, true, true>, grid, dim3(kThreads), s, true, true, a);
     if (krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, true, false>, grid, dim3(kThreads), s, true, !merge, a);
     if (!krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, false, true>, grid, dim3(kThreads), s, true, true, a);
-    if (!krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, false, false>, grid, dim3(kThreads), s, true, !merge, a);
+    if (!krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw / 2, false, false, 8>, grid, dim3(8 * 64), s, true, !merge, a);
   } else {
     if (self)
       launch(k_attn<KT, D, G, true>, grid, dim3(kThreads), s, true, true, a);
