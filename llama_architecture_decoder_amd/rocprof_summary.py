@@ -35,7 +35,7 @@ KERNELS = {
     "qkv": "k_gemv<unsigned short, 2, 4, true>",
     "o_proj": "k_gemv<unsigned short, 2, 1, false>",
     "lm_head": "k_gemv<unsigned short, 2, 3, true>",
-    "attention": "k_attn_mfma<128, 4, 64, false, false>",
+    "attention": "k_attn_mfma<128, 4, 32, false, false, 8>",
 }
 
 
