@@ -191,7 +191,8 @@ def time_batched(cfg, lm, synth, dev_weights, steps, warmup):
     out = {"workload": f"{cfg.name}: llama31_8b-shaped decode, batch {B} rows, bf16 weights and KV, MaxSeq "
                        f"{cfg.max_seq}, row lengths uniform in [{cfg.len_lo}, {cfg.len_hi}] (pre-filled random), "
                        f"{steps} steps", "value": round(B * 1e3 / ms, 2), "unit": "tokens/s",
-           "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup, "dtype": "bf16",
+           "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+           "dtype": "bf16 matrix-core products (f32 activations as hi + lo), f32 accumulation",
            "hbm_fraction": round(bytes_step / (ms * 1e-3) / HBM_PEAK, 4), "bytes_per_step": int(bytes_step),
            "row_lengths": [int(lens.min()), int(lens.max())]}
     del dec
@@ -250,7 +251,8 @@ def time_prefill(cfg, lm, synth, dev_weights, reps, warmup):
     out = {"workload": f"{cfg.name}: prefill of a {S}-position random prompt at positions 0..{S - 1} of a fresh "
                        f"cache row (MaxSeq {cfg.max_seq}), bf16 weights and KV, F32 activations",
            "value": round(S * 1e3 / ms, 1), "unit": "tokens/s", "ms_per_prefill": round(ms, 3), "reps": reps,
-           "warmup": warmup, "dtype": "bf16", "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "warmup": warmup, "dtype": "bf16 matrix-core products (f32 activations as hi + lo), f32 accumulation",
+           "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
            "mfma_fraction": round(fl / (ms * 1e-3) / MFMA_BF16_PEAK, 4), "kernels": kernels}
     if gu:
         per = gu["ms"] / gu["launches"] * 1e-3
@@ -599,7 +601,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16 weights and KV cache", "data": "synthetic",
         "config": {"workload": f"llama31_8b-shaped decode, batch 1, bf16 weights and KV, F32 arithmetic, "
                                f"positions {p0}..{p0 + steps - 1} of MaxSeq {cfg.max_seq} (0..{p0 - 1} "
                                f"pre-filled random)", "batch": 1, "positions": [p0, p0 + steps - 1],
