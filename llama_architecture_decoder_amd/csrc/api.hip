@@ -444,10 +444,15 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
     na.ldo = H;
     return hip_rc(launch_rows_reduce_norm(wdt, na, x.s, true));
   };
+  aa.ohi = ahi;
+  aa.olo = alo;
+  aa.ldo = H;
   int rc;
   {
     ProfScope ps(LLAMA_K_QKV, x.s);
-    if ((rc = split(xs, x.w->layers[0].ln1))) return rc;  // layer 0's operands; later layers' come from down
+    // layer 0's operands (also the zero rows that pad the batch to a 16-row tile; nothing writes those
+    // rows afterwards); later layers' come from down
+    if ((rc = split(xs, x.w->layers[0].ln1))) return rc;
   }
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
@@ -464,8 +469,8 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
     }
     {
       ProfScope ps(LLAMA_K_O, x.s);
-      if ((rc = split(att, nullptr))) return rc;
-      if ((rc = gemm(EPI_RESID, false, lw.wo, lw.wo, lw.wo, H, H, H, S.o, nullptr, H, false, false))) return rc;
+      // the attention's outputs arrive as the O product's operands (aa.ohi / aa.olo)
+      if ((rc = gemm(EPI_RESID, false, lw.wo, lw.wo, lw.wo, H, H, H, S.o, nullptr, H, true, false))) return rc;
       if ((rc = reduce_norm(S.o, lw.ln2))) return rc;
     }
     {

@@ -28,6 +28,19 @@
 
 namespace lm {
 
+// One normalised output o of row b at column col (of the row's dim outputs), and, when asked, its
+// operand split for the batched O product (the bits k_split would give: hi = bf16(o) to nearest even,
+// lo = bf16(o - hi))
+__device__ __forceinline__ void put_out(const AttnArgs &a, int b, int col, float v) {
+  a.out[(size_t)b * a.out_stride + col] = v;
+  if (a.ohi) {
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    a.ohi[(size_t)b * a.ldo + col] = __builtin_bit_cast(uint16_t, h);
+    a.olo[(size_t)b * a.ldo + col] = __builtin_bit_cast(uint16_t, l);
+  }
+}
+
 template <typename KT, int D>
 struct AttnShape {
   static constexpr int E = Vec16<KT>::E;      // elements per 16-byte slice
@@ -130,7 +143,7 @@ __device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, si
     if (idx < G * D) {
       const int q = idx / D;
       const float L = (red_l[0][q] + red_l[1][q]) + (red_l[2][q] + red_l[3][q]);
-      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc[i] / L;
+      put_out(a, b, j * G * D + idx, acc[i] / L);
     }
   }
   if (tid == 0) __hip_atomic_store(&a.done[b * a.kv + j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       L = fmaf(f, lsum, L);
     }
     if (a.direct) {
-      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+      put_out(a, b, j * G * D + idx, acc / L);
     } else if (SELF) {
       store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
       if (d == 0) {
@@ -538,7 +551,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
       L = fmaf(f, l_s[w][q], L);
     }
     if (a.direct) {
-      a.out[(size_t)b * a.out_stride + (size_t)(j * G) * D + idx] = acc / L;
+      put_out(a, b, j * G * D + idx, acc / L);
     } else if (SELF) {
       store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
       if (d == 0) {
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
     float sum = acc_s[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += acc_s[w][lane];
-    a.out[(size_t)b * a.out_stride + (size_t)(j * G + i) * D + d] = sum / L;
+    put_out(a, b, (j * G + i) * D + d, sum / L);
   }
 }
 

@@ -378,6 +378,10 @@ struct AttnArgs {
   int nch;             // chunk slots per (row, kv head) in the partial arrays
   unsigned *done;      // [B][kv] chunks finished per (row, kv head); zero between launches
   int direct;          // set by the launcher: one chunk per row, outputs written normalised
+  // nullable: the outputs also as bf16 hi + lo matrix-core operands ([B][ldo]; hi = bf16(o), lo =
+  // bf16(o - hi)), the form the batched O product reads, so no separate split launch is needed
+  bf16_t *ohi, *olo;
+  int ldo;
   float scale;         // 1/sqrt(head)
   int pos[kMaxBatch];
   // paged cache (as RopeAppend): row b's position p at pool position page_slot(table + b*pages, p) of row 0
