@@ -29,9 +29,10 @@ constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 // the input vector fewer times (each block loads all of it); more blocks keep more loads in flight.
 // Defaults measured on MI355X at the 8B shape; LLAMA_GEMV_GRID sets all, LLAMA_GEMV_GRID_<NAME> one.
 // The LM head is not monotonic in the cap: 157 us at 384-416 blocks, 170 at 512, 172-175 at 768-2048,
-// 204 at 256 (1.05 GB); the gate/up product is fastest with one group per block (35.6 vs 35.9 us).
+// 204 at 256 (1.05 GB); the gate/up product is fastest with one group per block (35.6 vs 35.9 us); the
+// down product takes 19.5 us at 448-512 blocks, 19.7 at 768, 21-23 at 384, 576-1024.
 struct Tun {
-  int qkv = 1024, o = 512, gate_up = 4096, down = 768, lm = 384;
+  int qkv = 1024, o = 512, gate_up = 4096, down = 512, lm = 384;
   int rows_blocks = 512;  // batched rows: K slices are chosen for about this many blocks per product
   static void env(const char *name, int &v) {
     if (const char *e = getenv(name))
