@@ -14,6 +14,12 @@ reports ``traffic`` only while that hash still matches).
 
 prints the kernel table (calls, average and total duration, share) of a ``--kernel-trace --stats`` run as
 markdown.
+
+    python -m llama_architecture_decoder_amd.rocprof_summary mfma <counter_dir>
+
+prints, per matrix-core kernel of a ``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 ...`` run,
+the mean dispatch duration, the executed bf16 matrix FLOPs (MOPS x 512) per second and the busy fraction of
+the matrix pipes (busy cycles summed over the 1024 SIMDs / (duration x 2.4 GHz x 1024)).
 """
 import csv
 import glob
@@ -121,12 +127,36 @@ def stats(fn: str):
               f"{float(r['Percentage']):.2f} |")
 
 
+def mfma(directory: str, clock_ghz: float = 2.4, simds: int = 1024):
+    per = defaultdict(lambda: defaultdict(dict))
+    dur = {}
+    for fn in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                k, d = row["Kernel_Name"], (fn, row["Dispatch_Id"])
+                per[k][d][row["Counter_Name"]] = per[k][d].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+                dur[(k, d)] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    print("| kernel | dispatches | average us | executed bf16 matrix TFLOP/s | matrix pipes busy |")
+    print("|---|---|---|---|---|")
+    for k, ds in sorted(per.items(), key=lambda kv: -sum(dur[(kv[0], d)] for d in kv[1])):
+        busy = sum(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for v in ds.values()) / len(ds)
+        if busy <= 0:
+            continue
+        mops = sum(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for v in ds.values()) / len(ds)
+        t = sum(dur[(k, d)] for d in ds) / len(ds)
+        name = k if len(k) <= 60 else k[:57] + "..."
+        print(f"| `{name}` | {len(ds)} | {t / 1e3:.1f} | {mops * 512 / t / 1e3:.0f} | "
+              f"{busy / (t * clock_ghz * simds):.3f} |")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 4 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3],
                 sys.argv[4] if len(sys.argv) > 4 else os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json"))
     elif len(sys.argv) == 3 and sys.argv[1] == "stats":
         stats(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2])
     else:
         print(__doc__)
         sys.exit(2)
