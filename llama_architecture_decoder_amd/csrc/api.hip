@@ -190,7 +190,9 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.xhi = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
   L.xlo = take(sizeof(uint16_t) * (size_t)L.mpad * kmax);
   // batched rows: a second operand pair (the MLP's inner activations) and the K-slice partial sums
-  const int64_t mrows = rows_path ? (max_batch + 15) / 16 * 16 : 0;
+  // (and, for the matrix-core prefill, the down product's operands written by the gate/up product)
+  const int64_t mrows = std::max<int64_t>(rows_path ? (max_batch + 15) / 16 * 16 : 0,
+                                          prows > 0 ? gemm_tiled_rows(prows) : 0);
   L.xhi2 = take(sizeof(uint16_t) * (size_t)mrows * d.f);
   L.xlo2 = take(sizeof(uint16_t) * (size_t)mrows * d.f);
   size_t part = 0;
@@ -520,6 +522,7 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
   float *att = x.at<float>(x.L.attn);
   float *mm = x.at<float>(x.L.m);
   bf16_t *xhi = x.at<bf16_t>(x.L.xhi), *xlo = x.at<bf16_t>(x.L.xlo);
+  bf16_t *mhi = x.at<bf16_t>(x.L.xhi2), *mlo = x.at<bf16_t>(x.L.xlo2);  // the down product's operands
   const int wdt = x.c->weight_dtype;
   const int qkv_stride = H + 2 * KW;
   int rc;
@@ -542,10 +545,15 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
   };
   auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
-                  int ldy, const float *res) {
+                  int ldy, const float *res, bool mlp_in) {
     GemmArgs ga = {};
-    ga.xhi = xhi;
-    ga.xlo = xlo;
+    ga.xhi = mlp_in ? mhi : xhi;  // the down product reads the operands the gate/up product wrote
+    ga.xlo = mlp_in ? mlo : xlo;
+    if (epi == EPI_SWIGLU) {
+      ga.ohi = mhi;
+      ga.olo = mlo;
+      ga.ldo = F;
+    }
     ga.ldx = K;
     ga.w[0] = w0;
     ga.w[1] = w1;
@@ -562,7 +570,7 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     ga.res = res;
     ga.ldres = ldy;
     ga.part = x.at<float>(x.L.part);  // short chunks split K (sized for every chunk up to max_prefill)
-    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true));
+    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true, mlp_in));  // the down product opens its scope
   };
   PrefillArgs pa = {};
   pa.qkv = qkv;
@@ -596,7 +604,8 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
       if ((rc = split(xs, lw.ln1, H))) return rc;
-      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr))) return rc;
+      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, false)))
+        return rc;
     }
     pa.kc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->k, l));
     pa.vc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->v, l));
@@ -608,17 +617,16 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_O, x.s);
       if ((rc = split(att, nullptr, H))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, false))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
       if ((rc = split(xs, lw.ln2, H))) return rc;
-      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr))) return rc;
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr, false))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_DOWN, x.s);
-      if ((rc = split(mm, nullptr, F))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true))) return rc;
     }
   }
   if (!logits && !next) return LLAMA_OK;

@@ -486,7 +486,8 @@ int gemm_tiled_rows(int M);
 // the partial-sum floats they need in GemmArgs::part (0 for one slice)
 int gemm_tiled_kslices(int M, int N, int K, bool swiglu);
 size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu);
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last);
+// first: the product's launch starts the profiling scope (no operand split launched before it)
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last, bool first = false);
 hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 // argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]

@@ -36,6 +36,18 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 constexpr int kTM = 128, kTN = 256, kTK = 32;
 constexpr int kRowA = kTK + 8;  // LDS row of a tile: 40 bf16 = 80 bytes (16-byte reads of 16 rows hit distinct banks)
 
+// A SwiGLU output v of token row t, unit n: F32 into y, or (a.ohi set) straight as the down product's
+// bf16 operands, hi = bf16(v) to nearest even, lo = bf16(v - hi) (the bits k_split would give)
+__device__ __forceinline__ void swiglu_store(const GemmArgs &a, int t, int n, float v) {
+  if (a.ohi) {
+    const __bf16 h = (__bf16)v;
+    a.ohi[(size_t)t * a.ldo + n] = __builtin_bit_cast(uint16_t, h);
+    a.olo[(size_t)t * a.ldo + n] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)h));
+  } else {
+    a.y[(size_t)t * a.ldy + n] = v;
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
@@ -169,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
           const int n = n0 + wn * 64 + jj * 32 + l32;
           if (n < a.N) {
             const float gt = acc[i][jj][r], up = acc[i][2 + jj][r];
-            a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+            swiglu_store(a, t, n, (gt / (1.0f + expf(-gt))) * up);
           }
         }
       } else {
@@ -209,11 +221,13 @@ __global__ __launch_bounds__(kThreads) void k_tiled_reduce(GemmArgs a, int S) {
       u1 += q.y;
     }
   }
-  float *y = a.y + (size_t)t * a.ldy + n;
   if (SW) {
-    y[0] = (v0 / (1.0f + expf(-v0))) * u0;
-    y[1] = (v1 / (1.0f + expf(-v1))) * u1;
-  } else {
+    swiglu_store(a, t, n, (v0 / (1.0f + expf(-v0))) * u0);
+    swiglu_store(a, t, n + 1, (v1 / (1.0f + expf(-v1))) * u1);
+    return;
+  }
+  float *y = a.y + (size_t)t * a.ldy + n;
+  {
     if (EPI == EPI_RESID) {
       v0 += a.res[(size_t)t * a.ldres + n];
       v1 += a.res[(size_t)t * a.ldres + n + 1];
@@ -471,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
           const int n = n0 + wn * 64 + jj * 32 + l32;
           if (n < a.N) {
             const float gt = acc[i][jj][r], up = acc[i][2 + jj][r];
-            a.y[(size_t)t * a.ldy + n] = (gt / (1.0f + expf(-gt))) * up;
+            swiglu_store(a, t, n, (gt / (1.0f + expf(-gt))) * up);
           }
         }
       } else {
@@ -512,7 +526,7 @@ size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu) {
   return ks > 1 ? (size_t)ks * M * (swiglu ? 2 * (size_t)N : (size_t)N) : 0;
 }
 
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last) {
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last, bool first) {
   if (a0.K % kTK != 0 || a0.M <= 0) return hipErrorInvalidValue;
   GemmArgs a = a0;
   const int mt = (a.M + kTM - 1) / kTM;
@@ -526,15 +540,15 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
     const dim3 g(p.blocks, ks);
     switch (epi) {
       case EPI_STORE:
-        launch(k_gemm_big<EPI_STORE, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        launch(k_gemm_big<EPI_STORE, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
         if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
         break;
       case EPI_RESID:
-        launch(k_gemm_big<EPI_RESID, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        launch(k_gemm_big<EPI_RESID, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
         if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
         break;
       case EPI_SWIGLU:
-        launch(k_gemm_big<EPI_SWIGLU, kBWaves>, g, dim3(kBWaves * 64), s, false, last && ks == 1, a, p);
+        launch(k_gemm_big<EPI_SWIGLU, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
         if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
         break;
       default:
@@ -546,15 +560,15 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
   const int ks = a.kslices;
   switch (epi) {
     case EPI_STORE:
-      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, false, last && ks == 1, a);
+      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, first, last && ks == 1, a);
       if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
     case EPI_RESID:
-      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, false, last && ks == 1, a);
+      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, first, last && ks == 1, a);
       if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
     case EPI_SWIGLU:
-      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt, ks), dim3(kThreads), s, false,
+      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt, ks), dim3(kThreads), s, first,
              last && ks == 1, a);
       if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
       break;
