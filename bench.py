@@ -241,8 +241,11 @@ def time_prefill(cfg, lm, synth, dev_weights, reps, warmup):
     for name, cls in lm.KERNEL_CLASSES.items():
         n, kms = lm.profile_read(cls)
         if n:
-            kernels[name] = {"launches": n, "ms": round(kms, 3), "share": round(kms / ms, 4)}
+            kernels[name] = {"launches": n, "ms": round(kms, 3)}
     lm.profile_enable(False)
+    ksum = sum(k["ms"] for k in kernels.values())
+    for k in kernels.values():
+        k["share"] = round(k["ms"] / ksum, 4)  # of the summed launch time of the profiled prefill
     fl = prefill_flops(cfg, S)
     # the products: the largest share of the time; matrix-core work per launch counted algorithmically
     d, kw, f = cfg.dim, cfg.kvw, cfg.f
@@ -268,23 +271,51 @@ def time_prefill(cfg, lm, synth, dev_weights, reps, warmup):
     return out
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def omp_threads(n):
+    """Set the OpenMP thread count of the oracle's parallel loops (libgomp, loaded with the oracle)."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
 def cpu_baseline(cfg, w, kc, vc, p0, first_tok, budget_s):
-    import numpy as np
+    """The oracle's greedy decode on the host, on all usable cores and then on one (the pages' table has
+    a 1-thread and a 16-thread column), each for about budget_s seconds of wall clock."""
     import oracle
     om = oracle.Model(cfg, w, rows=1, max_seq=kc.shape[3], alloc_cache=False)
     om.kc, om.vc = kc, vc
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    tok, n, t0 = first_tok, 0, time.perf_counter()
-    while True:
-        tok, _, _, _ = om.decode(tok, p0 + n)
-        n += 1
-        el = time.perf_counter() - t0
-        log(f"oracle step {n} at position {p0 + n - 1}: {el:.1f}s")
-        if el >= budget_s:
-            break
-    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+
+    def run(threads, start_pos):
+        omp_threads(threads)
+        tok, n, t0 = first_tok, 0, time.perf_counter()
+        while True:
+            tok, _, _, _ = om.decode(tok, start_pos + n)
+            n += 1
+            el = time.perf_counter() - t0
+            log(f"oracle ({threads} threads) step {n} at position {start_pos + n - 1}: {el:.1f}s")
+            if el >= budget_s:
+                return n, el
+
+    n, el = run(cores, p0)
+    # the one-core leg starts where the first left off in the cache, at the same positions' depth
+    n1, el1 = run(1, p0)
+    omp_threads(cores)
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{cfg.name}: first {n} greedy decode steps at positions {p0}..{p0 + n - 1} "
-                      f"(same weights and pre-filled cache as the GPU run), {el:.1f}s wall"}
+                      f"(same weights and pre-filled cache as the GPU run), {el:.1f}s wall",
+            "one_core": {"value": n1 / el1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {n1} greedy decode steps at positions {p0}..{p0 + n1 - 1}, "
+                                   f"{el1:.1f}s wall"}}
 
 
 def time_secondary(args, lm, synth, configs, c3=None):
@@ -304,11 +335,12 @@ def time_secondary(args, lm, synth, configs, c3=None):
     b3 = sum(token_bytes(c3, c3.prompt_len + i) for i in range(s3)) / s3
     mean3 = c3.prompt_len + (s3 - 1) // 2
     k3 = {}
+    ksum3 = sum(kms for n, kms in prof3.values() if n)
     for name, (n, kms) in prof3.items():
         if n:
             per = kms / n
             kb = kernel_bytes(c3, name, mean3) if name != "embed" else None
-            k3[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(kms / pev3, 4),
+            k3[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(kms / ksum3, 4),
                         "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
     res3 = {"workload": f"{c3.name}-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
                                        f"then {s3} steps at positions {c3.prompt_len}..{c3.prompt_len + s3 - 1}",
@@ -582,12 +614,13 @@ def main():
     hbm_frac = bytes_tok / (ms_step * 1e-3) / HBM_PEAK
 
     kernels = {}
+    ksum = sum(ms for n, ms in prof.values() if n)
     for name, (n, ms) in prof.items():
         if n == 0:
             continue
         per = ms / n
         kb = kernel_bytes(cfg, name, int(mean_t)) if name != "embed" else None
-        kernels[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(ms / pev_ms, 4),
+        kernels[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(ms / ksum, 4),
                          "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
     dom = "gate_up"
     n, ms = prof[dom]
@@ -596,6 +629,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK, 4), "traffic": measured_traffic("gate_up"),
                 "kernel": "k_gemv<bf16, SwiGLU> (gate+up)",
+                "scope": "the dominant kernel alone; the whole step's fraction of the HBM peak is hbm_fraction",
                 "bytes_per_launch": kernel_bytes(cfg, dom), "avg_launch_us": round(avg_s * 1e6, 3)}
 
     result = {
@@ -609,6 +643,9 @@ def main():
         "hbm_fraction": round(hbm_frac, 4), "bytes_per_token": int(bytes_tok),
         "host_ms_per_step": round(host_ms / steps, 4),
         "roofline": roofline, "kernels": kernels,
+        "kernel_share_basis": "each kernel class's summed launch time over the summed time of all launches, "
+                              "from a second pass whose launches record HIP events in their dispatch packets",
+        "profiled_ms_per_step": round(pev_ms / steps, 4),
     }
     if not args.no_secondary:
         c5 = configs.LLAMA31_8B_LONG

@@ -13,8 +13,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# LLAMA_MI355X_LIB selects another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("LLAMA_MI355X_LIB") or os.path.join(_HERE, "_lib", "libllama_mi355x.so")
+LIB_PATH = os.path.join(_HERE, "_lib", "libllama_mi355x.so")  # the in-tree build, never another
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "llama_mi355x.h")
 
 F32, BF16 = 0, 1

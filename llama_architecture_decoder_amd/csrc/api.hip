@@ -27,31 +27,16 @@ constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 
 // Caps on GEMV blocks per projection (blocks walk row groups with a grid stride).  Fewer blocks read
 // the input vector fewer times (each block loads all of it); more blocks keep more loads in flight.
-// Defaults measured on MI355X at the 8B shape; LLAMA_GEMV_GRID sets all, LLAMA_GEMV_GRID_<NAME> one.
-// The LM head is not monotonic in the cap: 157 us at 384-416 blocks, 170 at 512, 172-175 at 768-2048,
-// 204 at 256 (1.05 GB); the gate/up product is fastest with one group per block (35.6 vs 35.9 us); the
-// down product takes 19.5 us at 448-512 blocks, 19.7 at 768, 21-23 at 384, 576-1024.
+// Measured on MI355X at the 8B shape: the LM head is not monotonic in the cap (157 us at 384-416
+// blocks, 170 at 512, 172-175 at 768-2048, 204 at 256; 1.05 GB); the gate/up product is fastest with
+// one group per block (35.6 vs 35.9 us); the down product takes 19.5 us at 448-512 blocks, 19.7 at
+// 768, 21-23 at 384, 576-1024.
 struct Tun {
   int qkv = 1024, o = 512, gate_up = 4096, down = 512, lm = 384;
   int rows_blocks = 512;  // batched rows: K slices are chosen for about this many blocks per product
-  static void env(const char *name, int &v) {
-    if (const char *e = getenv(name))
-      if (atoi(e) > 0) v = atoi(e);
-  }
-  Tun() {
-    int all = 0;
-    env("LLAMA_GEMV_GRID", all);
-    if (all > 0) qkv = o = gate_up = down = lm = all;
-    env("LLAMA_GEMV_GRID_QKV", qkv);
-    env("LLAMA_GEMV_GRID_O", o);
-    env("LLAMA_GEMV_GRID_GATE_UP", gate_up);
-    env("LLAMA_GEMV_GRID_DOWN", down);
-    env("LLAMA_GEMV_GRID_LM", lm);
-    env("LLAMA_ROWS_BLOCKS", rows_blocks);
-  }
 };
 const Tun &tun() {
-  static Tun t;
+  static const Tun t;
   return t;
 }
 
@@ -176,7 +161,9 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.qkv = take(sizeof(float) * rows * (d.dim + 2 * d.kvw));
   L.qrot = take(sizeof(float) * (size_t)max_batch * d.dim);
   L.attn = take(sizeof(float) * rows * d.dim);
-  L.m = take(sizeof(float) * rows * d.f);
+  // the F32 MLP activations of the GEMV path (decode rows one at a time, and the trace); the prefill's
+  // gate/up product writes the down product's operands instead
+  L.m = take(sizeof(float) * (size_t)max_batch * d.f);
   L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
   L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
   const bool rows_path = rows_ok(c, max_batch);
@@ -520,7 +507,6 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
   float *xs = x.at<float>(x.L.x);
   float *qkv = x.at<float>(x.L.qkv);
   float *att = x.at<float>(x.L.attn);
-  float *mm = x.at<float>(x.L.m);
   bf16_t *xhi = x.at<bf16_t>(x.L.xhi), *xlo = x.at<bf16_t>(x.L.xlo);
   bf16_t *mhi = x.at<bf16_t>(x.L.xhi2), *mlo = x.at<bf16_t>(x.L.xlo2);  // the down product's operands
   const int wdt = x.c->weight_dtype;
@@ -622,7 +608,8 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
       if ((rc = split(xs, lw.ln2, H))) return rc;
-      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, mm, F, nullptr, false))) return rc;
+      // silu(gate) * up goes straight to the down product's operands (mhi / mlo), never to F32
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, nullptr, F, nullptr, false))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_DOWN, x.s);

@@ -725,9 +725,8 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
   // Small merges (few chunks x few outputs per (row, kv head)) run in the attention kernel's last block
   // per (row, kv head): measured faster than a separate launch for the 1.7B shape (8 chunks x 64 outputs:
   // 7.4 vs 10.0 us per layer), slower for the 8B shape at 8K positions (32 x 512: 16.3 vs 14.6 us) and
-  // for 32 long rows.  LLAMA_ATTN_SEPARATE_MERGE forces the separate launch.
-  static const bool separate = getenv("LLAMA_ATTN_SEPARATE_MERGE") != nullptr;
-  const bool self = merge && !separate && (long)nch_launch * G * D <= 4096;
+  // for 32 long rows.
+  const bool self = merge && (long)nch_launch * G * D <= 4096;
   if constexpr (use_mfma<KT, D, G>()) {
     // keys as whole rows (through LDS) pay off when the launch streams many blocks per CU; a launch of
     // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout, and with

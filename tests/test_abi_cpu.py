@@ -77,6 +77,23 @@ def test_workspace_bytes(L):
     assert L.llama_workspace_bytes(ctypes.byref(c), 1, 1 << 20, 0) == lm.E_UNSUPPORTED
 
 
+def test_workspace_prefill_rows(L):
+    # A prompt chunk of the matrix-core prefill needs, per row: the F32 residual, q|k|v and attention rows,
+    # one bf16 hi/lo operand pair of width max(dim, f) and the down product's pair of width f; its SwiGLU
+    # output is never F32, so no [max_prefill][f] F32 buffer.  F32 models prefill through the decode
+    # kernels and need nothing per prompt row.
+    c = _c(configs.LLAMA31_8B)
+    d = configs.LLAMA31_8B
+    n2 = L.llama_workspace_bytes(ctypes.byref(c), 1, 32768, 2048)
+    n4 = L.llama_workspace_bytes(ctypes.byref(c), 1, 32768, 4096)
+    per_row = (n4 - n2) / 2048
+    rows = 4 * (2 * d.dim + d.dim + 2 * d.kvw) + 4 * max(d.dim, d.f) + 4 * d.f
+    assert rows <= per_row < rows + 2 * d.f, per_row  # (+ split-K partial sums, far below a row of f F32)
+    cf = _c(configs.SMOLLM2_1_7B)
+    assert L.llama_workspace_bytes(ctypes.byref(cf), 1, 8192, 4096) == L.llama_workspace_bytes(ctypes.byref(cf), 1,
+                                                                                              8192, 0)
+
+
 def test_kv_cache_alloc_binds_without_touching_memory(L):
     cfg = configs.SMOLLM2_135M
     c = _c(cfg)

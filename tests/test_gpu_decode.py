@@ -253,3 +253,76 @@ def test_lm_head_argmax(name):
     dec.lm_head_argmax(x, None, am[:1])
     torch.cuda.synchronize()
     assert int(am[0].item()) == 0  # all logits 0: index 0
+
+
+# LM-head rows that tie for the largest logit, in different blocks of both LM-head kernels (the batch-1
+# GEMV's grid-strided row groups of 8 and the batched product's 128-output blocks), the same block and
+# the same 16-lane row too.  The final norm keeps one coordinate only (gain 1 at c0, 0 elsewhere), so
+# every logit is W[r][c0] * n[c0] exactly and rows with equal W[r][c0] tie whatever the hidden state.
+TIE_POS = (120000, 4072, 1001, 1000)   # W[r][c0] = +1: the largest logits when n[c0] > 0
+TIE_NEG = (121000, 5072, 2001, 2000)   # W[r][c0] = -1: the largest logits when n[c0] < 0
+
+
+def _tie_weights(cfg, c0=7):
+    w = dict(weights(cfg))
+    lnf = np.zeros_like(w["lnf"])
+    lnf[c0] = 0x3F80  # bf16 1.0
+    head = w["lm_head"].copy()
+    head[list(TIE_POS), c0] = 0x3F80
+    head[list(TIE_NEG), c0] = 0xBF80  # bf16 -1.0
+    w["lnf"], w["lm_head"] = lnf, head
+    return w
+
+
+def _check_ties(lg, got, what):
+    # main.bend argmax: the first index of the largest value
+    for rows in (TIE_POS, TIE_NEG):
+        vals = lg[list(rows)]
+        assert np.all(vals == vals[0]), f"{what}: tied rows differ {vals}"
+    want = min(TIE_POS) if lg[TIE_POS[0]] > lg[TIE_NEG[0]] else min(TIE_NEG)
+    assert lg[want] == lg.max(), f"{what}: tie rows are not the maximum"
+    assert got == want, f"{what}: argmax {got}, the first of the tied maxima is {want}"
+    return want
+
+
+@pytest.mark.timeout(600)
+def test_lm_head_argmax_cross_block_ties():
+    lm = _lm()
+    cfg = configs.truncated(configs.LLAMA31_8B, 1)
+    w = _tie_weights(cfg)
+    om = oracle.Model(cfg, w, rows=1, max_seq=16, alloc_cache=False)
+    # batch 1 and 2 through lm_head_argmax (the GEMV with its block winners and the final reduce)
+    dec = lm.Decoder(cfg, w, rows=2, max_seq=16)
+    rng = np.random.default_rng(3)
+    hid = rng.standard_normal((2, cfg.dim)).astype(np.float32)
+    hid[1, 7] = -abs(hid[1, 7])
+    hid[0, 7] = abs(hid[0, 7])
+    logits = torch.empty((2, cfg.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(2, dtype=torch.int32, device="cuda")
+    dec.lm_head_argmax(torch.from_numpy(hid).cuda(), logits, am)
+    torch.cuda.synchronize()
+    wants = []
+    for b in range(2):
+        lg = logits[b].cpu().numpy()
+        wants.append(_check_ties(lg, int(am[b].item()), f"lm_head_argmax row {b}"))
+        rid, _ = om.lm_head(hid[b])
+        assert rid == wants[-1]
+    assert wants == [1000, 2000]
+    # argmax alone (no logits written)
+    dec.lm_head_argmax(torch.from_numpy(hid).cuda(), None, am)
+    torch.cuda.synchronize()
+    assert am.cpu().tolist() == wants
+    del dec
+    # 32 rows through a decode step (the batched matrix-core LM head and its per-row reduce)
+    B = 32
+    dec = lm.Decoder(cfg, w, rows=B, max_seq=16)
+    toks = synth.tokens(cfg, "ties", B)
+    logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    dec.decode(torch.from_numpy(toks).cuda(), [0] * B, logits, nxt)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    seen = set()
+    for b in range(B):
+        seen.add(_check_ties(got[b], int(nxt[b].item()), f"decode row {b}"))
+    log(f"cross-block ties: batch-32 winners {sorted(seen)}")

@@ -110,3 +110,35 @@ def test_prefill_4096_equals_decode_steps_8b():
         tol = 1.6e-2 * float(np.abs(ya).max())
         assert float(np.abs(xa - ya).max()) <= tol, nm
     log(f"prefill 4096 vs decode: max|d| {d:.3g} rel {rel:.3g}")
+
+
+@pytest.mark.timeout(1200)
+def test_prefill_4096_oracle_parity_8b_width():
+    """The 4096-position prompt of the long-context workload, at the full 8B width and in the benchmark's
+    launch configuration (one pass: max_prefill 4096, a MaxSeq-32768 cache row), on a 2-layer truncation
+    so the oracle finishes: last-position logits within 2e-2, the argmax outside near-ties and every
+    appended K/V slot of both layers (the second layer's slots depend on every position's first-layer
+    output) within bf16 rounding.  The oracle runs position after position (its prefill is sequential
+    decode), in pieces of 256 positions with a progress line after each."""
+    import llama_architecture_decoder_amd as lm
+    cfg = configs.truncated(configs.LLAMA31_8B_LONG, 2)
+    S, max_seq = cfg.prompt_len, cfg.max_seq
+    assert (S, max_seq) == (4096, 32768)
+    w = weights(cfg)
+    dec = lm.Decoder(cfg, w, rows=1, max_seq=max_seq, max_prefill=S)
+    toks = synth.tokens(cfg, "bench/prompt", S)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    dec.prefill(torch.from_numpy(toks).cuda(), pos0=0, logits=logits, next_tok=nxt)
+    torch.cuda.synchronize()
+    assert dec.status() == 0
+    got, gid = logits.cpu().numpy(), int(nxt.item())
+    om = oracle.Model(cfg, w, rows=1, max_seq=max_seq)
+    piece = 256
+    for p0 in range(0, S, piece):
+        rid, ref = om.prefill(toks[p0:p0 + piece], pos0=p0)
+        log(f"oracle prefill {p0 + piece}/{S}")
+    d, rel = check_logits(cfg, got, ref, "prefill 4096")
+    check_argmax(cfg, gid, ref, "prefill 4096")
+    _check_slots(cfg, dec, om, 0, S, "prefill 4096")
+    log(f"prefill 4096 (2 layers, 8B width) vs oracle: max|d| {d:.3g} rel {rel:.3g}")

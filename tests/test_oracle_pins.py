@@ -508,3 +508,44 @@ def test_oracle_matches_transformers(name, layers, n):
         top2 = np.sort(ref[p])[-2:]
         if top2[1] - top2[0] > 1e-4:
             assert r == int(np.argmax(ref[p]))
+
+
+@pytest.mark.parametrize("name,layers,vocab", [("tiny", None, None), ("smollm2_135m", 1, None),
+                                               ("llama31_8b", 1, 8192)])
+def test_lm_head_matches_decode_and_transformers(name, layers, vocab):
+    # main.bend "The model": head_of = the LM head (the embedding when tied, the separate head matrix of
+    # the nest card otherwise) over rmsnorm(x, final norm), then argmax.  The oracle's standalone head
+    # (the reference for the GPU lm_head_argmax) must give the decode's own logits bit for bit from the
+    # decode's hidden state, and match transformers' model.norm + lm_head on that state; the untied case
+    # uses a head matrix unlike the embedding, so a swapped head, the wrong gain or a skipped norm fails.
+    import torch
+    cfg = configs.get(name)
+    if layers:
+        cfg = configs.truncated(cfg, layers, **({"vocab": vocab} if vocab else {}))
+    cfg = cfg.replace(kvdtype="f32")
+    w = synth.make_weights(cfg)
+    if not cfg.tied:
+        assert not np.array_equal(w["lm_head"], w["emb"])
+    om = oracle.Model(cfg, w, max_seq=8)
+    toks = synth.tokens(cfg, "lmhead", 3)
+    m = hf_model(cfg, w)
+    for p, tk in enumerate(toks):
+        r, lg, _, hd = om.decode(int(tk), p, hidden=True)
+        r2, lg2 = om.lm_head(hd)
+        np.testing.assert_array_equal(lg2, lg)
+        assert r2 == r
+        with torch.no_grad():
+            h = torch.from_numpy(hd[None].copy())
+            ref = m.lm_head(m.model.norm(h))[0].numpy()
+        assert np.abs(lg2 - ref).max() <= 1e-5 * np.abs(ref).max(), p
+        top2 = np.sort(ref)[-2:]
+        if top2[1] - top2[0] > 1e-4:
+            assert r2 == int(np.argmax(ref))
+    # a hidden state that is not a decode's
+    rng = np.random.default_rng(5)
+    hid = rng.standard_normal(cfg.dim).astype(F32)
+    r3, lg3 = om.lm_head(hid)
+    with torch.no_grad():
+        ref = m.lm_head(m.model.norm(torch.from_numpy(hid[None].copy())))[0].numpy()
+    assert np.abs(lg3 - ref).max() <= 1e-5 * np.abs(ref).max()
+    del m
