@@ -65,6 +65,8 @@ def kernel_bytes(cfg, cls, t=None):
         return cfg.vocab * d * wb + d * wb + d * 4 + cfg.vocab * 4
     if cls == "attention":
         return 2 * kw * cfg.kvbytes * (t + 1) + (d + 2 * kw) * 4 + d * 4
+    if cls == "qkv_attention":  # the q/k/v product and the attention in one launch (+ its merge)
+        return kernel_bytes(cfg, "qkv", t) + 2 * kw * cfg.kvbytes * t + d * 4
     raise KeyError(cls)
 
 

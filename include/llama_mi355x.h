@@ -52,7 +52,8 @@ enum {
   LLAMA_E_HIP = -7,         /* a HIP runtime call or launch failed */
   LLAMA_E_UNSUPPORTED = -8, /* valid but not built: head not in {64,128}, g not in {1,2,3,4,8}, dim or f not a
                                multiple of 8 or too wide, max_seq > 131072 */
-  LLAMA_E_PAGE = -9         /* a page table entry outside the pool (sticky device flag, see llama_status) */
+  LLAMA_E_PAGE = -9,        /* a page table entry outside the pool (sticky device flag, see llama_status) */
+  LLAMA_E_WAIT = -10        /* a device-side wait of a decode step gave up (sticky device flag, see llama_status) */
 };
 
 /*
@@ -268,6 +269,7 @@ int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidd
  * with K2 = k rounded up to a power of two: 262144 at k = 256).  B = 0 returns LLAMA_OK.
  */
 int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k);
+
 int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
                  const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals, int32_t *topk_ids,
                  void *scratch, size_t scratch_bytes, void *stream);
@@ -281,13 +283,15 @@ int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float te
  */
 enum {
   LLAMA_K_EMBED = 0, LLAMA_K_QKV = 1, LLAMA_K_ATTN = 2, LLAMA_K_O = 3, LLAMA_K_GATE_UP = 4, LLAMA_K_DOWN = 5,
-  LLAMA_K_LM_HEAD = 6, LLAMA_K_SAMPLE = 7
+  LLAMA_K_LM_HEAD = 6, LLAMA_K_SAMPLE = 7, LLAMA_K_QKV_ATTN = 8
 };
 int llama_profile_enable(int on);
 int llama_profile_read(int kernel_class, int64_t *launches, double *total_ms);
 
-/* Synchronise `stream` and return the sticky device-side status (LLAMA_OK, LLAMA_E_TOKEN, or LLAMA_E_PAGE when
- * no token was out of range), then clear it. */
+/* Synchronise `stream` and return the sticky device-side status, then clear it: LLAMA_OK, else LLAMA_E_TOKEN
+ * (a token out of range), else LLAMA_E_PAGE (a page table entry outside the pool), else LLAMA_E_WAIT (an
+ * attention block of a batch-1 step stopped waiting for the step's queries: its outputs are NaN; not
+ * expected unless the GPU is shared with work that keeps the step's blocks from running). */
 int llama_status(const llama_ws *ws, void *stream);
 
 /* Static description of a return code. */

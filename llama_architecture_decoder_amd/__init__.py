@@ -18,9 +18,10 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "llama_mi355x.h")
 
 F32, BF16 = 0, 1
 OK = 0
-E_CONFIG, E_POS, E_TOKEN, E_SHAPE, E_NULL, E_WORKSPACE, E_HIP, E_UNSUPPORTED, E_PAGE = -1, -2, -3, -4, -5, -6, -7, -8, -9
+E_CONFIG, E_POS, E_TOKEN, E_SHAPE, E_NULL, E_WORKSPACE, E_HIP, E_UNSUPPORTED, E_PAGE, E_WAIT = range(-1, -11, -1)
 ERROR_NAMES = {0: "OK", -1: "E_CONFIG", -2: "E_POS", -3: "E_TOKEN", -4: "E_SHAPE", -5: "E_NULL",
-               -6: "E_WORKSPACE", -7: "E_HIP", -8: "E_UNSUPPORTED", -9: "E_PAGE"}
+               -6: "E_WORKSPACE", -7: "E_HIP", -8: "E_UNSUPPORTED", -9: "E_PAGE",
+               -10: "E_WAIT"}
 PAGE_SIZE = 64
 
 
@@ -337,9 +338,9 @@ class Decoder:
         return int(lib().llama_status(ctypes.byref(self.ws.rec), _stream_handle(stream)))
 
 
-K_EMBED, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LM_HEAD, K_SAMPLE = range(8)
+K_EMBED, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LM_HEAD, K_SAMPLE, K_QKV_ATTN = range(9)
 KERNEL_CLASSES = {"embed": K_EMBED, "qkv": K_QKV, "attention": K_ATTN, "o_proj": K_O, "gate_up": K_GATE_UP,
-                  "down": K_DOWN, "lm_head": K_LM_HEAD, "sample": K_SAMPLE}
+                  "down": K_DOWN, "lm_head": K_LM_HEAD, "sample": K_SAMPLE, "qkv_attention": K_QKV_ATTN}
 
 
 def sample_scratch_bytes(B: int, V: int, k: int) -> int:

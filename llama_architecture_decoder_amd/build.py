@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build", "llama_mi355x")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libllama_mi355x.so")
-SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "prefill.hip", "attention.hip", "misc.hip", "sample.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "prefill.hip", "attention.hip", "fused.hip", "misc.hip", "sample.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=on",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

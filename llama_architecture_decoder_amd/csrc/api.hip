@@ -24,6 +24,9 @@ using namespace lm;
 namespace {
 
 constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
+// polls before an attention block of the q/k/v + attention launch stops waiting for its queries (each
+// poll is a memory round trip of about a microsecond: ~0.1 s in all, against ~15 us for the product)
+constexpr int kSpinLimit = 1 << 16;
 
 // Caps on GEMV blocks per projection (blocks walk row groups with a grid stride).  Fewer blocks read
 // the input vector fewer times (each block loads all of it); more blocks keep more loads in flight.
@@ -109,9 +112,10 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, done, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
+  size_t status, done, epoch, tagged, group_done, part_t, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
       total;
-  int nch;
+  int nch;    // chunk slots per (row, kv head) of the attention partials
+  int nch_f;  // chunk slots of the one-row launch that runs the q/k/v product with the attention
   int lm_ld;  // per-row stride of the LM head's block winners
   int mpad;   // token rows of the split operands (max_batch rounded up to 16)
 };
@@ -147,6 +151,8 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   WsLayout L;
   const int chunk = attention_chunk(c->kv_dtype, (int)d.head, (int)d.g);
   L.nch = (int)((max_seq + chunk - 1) / chunk);
+  const int fchunk = qkv_attention_chunk(c->kv_dtype, (int)d.head, (int)d.g);
+  L.nch_f = fchunk > 0 ? (int)((max_seq + fchunk - 1) / fchunk) : 0;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -154,7 +160,12 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
     return at;
   };
   L.status = take(64);
-  L.done = take(sizeof(unsigned) * (size_t)max_batch * d.kv);  // zeroed with the status word at init
+  // zeroed with the status word at init: chunk counters, the step counter and the tagged words
+  L.done = take(sizeof(unsigned) * (size_t)max_batch * d.kv);
+  L.epoch = take(sizeof(unsigned));
+  L.tagged = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));
+  L.group_done = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));  // at most a group per row
+  L.part_t = take(sizeof(unsigned long long) * (size_t)L.nch_f * d.kv * (d.g * d.head + 2 * d.g + 1));
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * rows * d.dim);
@@ -164,8 +175,9 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   // the F32 MLP activations of the GEMV path (decode rows one at a time, and the trace); the prefill's
   // gate/up product writes the down product's operands instead
   L.m = take(sizeof(float) * (size_t)max_batch * d.f);
-  L.part_o = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * d.head);
-  L.part_ml = take(sizeof(float) * (size_t)max_batch * d.kv * L.nch * d.g * 2);
+  const size_t slots = std::max<size_t>((size_t)max_batch * L.nch, (size_t)L.nch_f);  // per kv head
+  L.part_o = take(sizeof(float) * slots * d.kv * d.g * d.head);
+  L.part_ml = take(sizeof(float) * slots * d.kv * d.g * 2);
   const bool rows_path = rows_ok(c, max_batch);
   L.lm_ld = kLmGridMax;
   if (rows_path && gemm_rows_blocks((int)d.vocab, false) > L.lm_ld) L.lm_ld = gemm_rows_blocks((int)d.vocab, false);
@@ -486,6 +498,11 @@ int run_step_rows(const Ctx &x, AttnArgs aa, RopeAppend ra, int tmax, int B, flo
   return LLAMA_OK;
 }
 
+// The matrix-core prefill's products whose activations go in as bf16 hi + lo (bit set: the F32 values to
+// ~2^-17) rather than as bf16 (the hi half alone, half the matrix-core work)
+enum { kProdQkv = 0, kProdO = 1, kProdGateUp = 2, kProdDown = 3 };
+constexpr unsigned kPrefillLo = 0xFu;
+
 // One piece of a packed pass: len consecutive positions pos0 .. of cache row `row` (paged: of table row
 // `row`); out >= 0 asks for the logits / next token after its last position at entry `out`.
 struct PackSeg {
@@ -514,7 +531,7 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
   int rc;
   {
     ProfScope ps(LLAMA_K_EMBED, x.s);
-    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, S, x.at<int>(x.L.status), x.s));
+    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, S, x.at<int>(x.L.status), nullptr, x.s));
   }
   if (rc) return rc;
   auto split = [&](const float *in, const void *gain, int K) {
@@ -531,8 +548,9 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
   };
   auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
-                  int ldy, const float *res, bool mlp_in) {
+                  int ldy, const float *res, bool mlp_in, int product) {
     GemmArgs ga = {};
+    ga.lo = (kPrefillLo >> product) & 1;
     ga.xhi = mlp_in ? mhi : xhi;  // the down product reads the operands the gate/up product wrote
     ga.xlo = mlp_in ? mlo : xlo;
     if (epi == EPI_SWIGLU) {
@@ -590,7 +608,8 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
       if ((rc = split(xs, lw.ln1, H))) return rc;
-      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, false)))
+      if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, false,
+                     kProdQkv)))
         return rc;
     }
     pa.kc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->k, l));
@@ -603,17 +622,18 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_O, x.s);
       if ((rc = split(att, nullptr, H))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, false))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, false, kProdO))) return rc;
     }
     {
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
       if ((rc = split(xs, lw.ln2, H))) return rc;
       // silu(gate) * up goes straight to the down product's operands (mhi / mlo), never to F32
-      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, nullptr, F, nullptr, false))) return rc;
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, nullptr, F, nullptr, false, kProdGateUp)))
+        return rc;
     }
     {
       ProfScope ps(LLAMA_K_DOWN, x.s);
-      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true))) return rc;
+      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true, kProdDown))) return rc;
     }
   }
   if (!logits && !next) return LLAMA_OK;
@@ -642,7 +662,8 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
   int rc;
   {
     ProfScope ps(LLAMA_K_EMBED, x.s);
-    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, B, x.at<int>(x.L.status), x.s));
+    rc = hip_rc(launch_embed(wdt, tokens, x.w->emb, H, (int)d.vocab, xs, B, x.at<int>(x.L.status),
+                             x.at<unsigned>(x.L.epoch), x.s));
   }
   if (rc) return rc;
 
@@ -691,11 +712,13 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
     return run_step_rows(x, aa, ra, tmax, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
+  // one token row (contiguous cache, no trace): the q/k/v product and the attention in one launch
+  bool fused = B == 1 && !trace && !x.table && x.L.nch_f > 0;
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
     aa.kc = ra.kc = layer_cache(x, x.kv->k, l);
     aa.vc = ra.vc = layer_cache(x, x.kv->v, l);
-    for (int b = 0; b < B; ++b) {
+    auto qkv_args = [&](int b) {
       GemvArgs a = {};
       a.ra = ra;
       a.ra.qrot = ra.qrot + (size_t)b * H;
@@ -715,10 +738,36 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.N = H + 2 * KW;
       a.K = H;
       a.y = qkv + (size_t)b * qkv_stride;
-      ProfScope ps(LLAMA_K_QKV, x.s);
-      if ((rc = hip_rc(launch_gemv(wdt, EPI_ROPE, true, a, tun().qkv, x.s)))) return rc;
+      return a;
+    };
+    bool done = false;
+    if (fused) {
+      GemvArgs a = qkv_args(0);
+      a.ra.tagged = x.at<unsigned long long>(x.L.tagged);
+      a.ra.group_done = x.at<unsigned long long>(x.L.group_done);
+      AttnArgs af = aa;
+      af.tagged = a.ra.tagged;
+      af.dim = H;
+      af.kvw = KW;
+      af.spin_limit = kSpinLimit;
+      af.nch = x.L.nch_f;
+      af.part_t = x.at<unsigned long long>(x.L.part_t);
+      ProfScope ps(LLAMA_K_QKV_ATTN, x.s);
+      const hipError_t e = launch_qkv_attention(wdt, x.c->kv_dtype, (int)d.head, (int)d.g, a, af, tmax,
+                                                x.at<unsigned>(x.L.epoch), (uint32_t)d.layers, (uint32_t)l + 1u, x.s);
+      if (e == hipSuccess)
+        done = true;
+      else if (e == hipErrorNotSupported)
+        fused = false;  // nothing was launched: the two launches below, for this and the later layers
+      else
+        return LLAMA_E_HIP;
     }
-    {
+    if (!done) {
+      for (int b = 0; b < B; ++b) {
+        GemvArgs a = qkv_args(b);
+        ProfScope ps(LLAMA_K_QKV, x.s);
+        if ((rc = hip_rc(launch_gemv(wdt, EPI_ROPE, true, a, tun().qkv, x.s)))) return rc;
+      }
       ProfScope ps(LLAMA_K_ATTN, x.s);
       if ((rc = hip_rc(launch_attention(x.c->kv_dtype, (int)d.head, (int)d.g, aa, B, tmax, x.s)))) return rc;
     }
@@ -826,6 +875,7 @@ const char *llama_strerror(int code) {
     case LLAMA_E_HIP: return "HIP runtime error";
     case LLAMA_E_UNSUPPORTED: return "not supported by this library";
     case LLAMA_E_PAGE: return "a page table entry outside the cache's page pool";
+    case LLAMA_E_WAIT: return "a device-side wait for the step's queries gave up (outputs are NaN)";
     default: return "unknown error";
   }
 }
@@ -1257,7 +1307,7 @@ int llama_status(const llama_ws *ws, void *stream) {
   if (hipMemcpy(&flag, ws->base, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LLAMA_E_HIP;
   if (flag) {
     if (launch_zero(ws->base, 64, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) return LLAMA_E_HIP;
-    return (flag & 1) ? LLAMA_E_TOKEN : LLAMA_E_PAGE;
+    return (flag & 1) ? LLAMA_E_TOKEN : (flag & 2) ? LLAMA_E_PAGE : LLAMA_E_WAIT;
   }
   return LLAMA_OK;
 }

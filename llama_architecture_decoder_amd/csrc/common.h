@@ -241,6 +241,13 @@ struct RopeAppend {
   const int32_t *table;
   int pages, npages;               // entries per table row, pages in the pool
   int *status;                     // sticky flag word: bit 1 = a table entry outside the pool
+  // nullable: each rotated query, and each key and value as the cache stores it, also goes to
+  // tagged[P] (token row 0 only) as one 64-bit word (the tag in the high half, the F32 bits in the
+  // low half), for attention blocks of the same launch (tagged_store / tagged_load)
+  unsigned long long *tagged;
+  // nullable (with tagged): one tagged word per row group of the product, written once the group's
+  // outputs are out, so a waiting attention block can poll one word per group instead of every output
+  unsigned long long *group_done;
 };
 
 // Paged caches: positions of a row lie in pages of kPageSize consecutive pool positions, page i of the
@@ -267,10 +274,23 @@ __device__ __forceinline__ int rope_row(int L, int qk_rows, int hshift) {
 // pair index i (cos/sin column) of logical row L of the q and k heads
 __device__ __forceinline__ int rope_pair_index(int L, int hshift) { return (L & ((2 << hshift) - 1)) >> 1; }
 
+// Tagged words: a value and the tag of the launch that wrote it, stored and loaded as one naturally
+// aligned 64-bit word with device-scope atomics (written through to memory; read past this XCD's L2).
+// A reader takes a word only when its tag is the current launch's, and the 64-bit access is single-copy
+// atomic, so the value it takes is the one stored with that tag: no fence or flag is needed.
+__device__ __forceinline__ void tagged_store(unsigned long long *p, float v, uint32_t tag) {
+  const unsigned long long w = ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long tagged_load(const unsigned long long *p) {
+  return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // the epilogue for one logical row L of token row t: val = its projection, pv = its pair partner's,
-// (c, s) = cos/sin of the token's position at the row's pair index (unused for value rows)
+// (c, s) = cos/sin of the token's position at the row's pair index (unused for value rows); `tag`
+// labels the tagged copies (ra.tagged set)
 __device__ __forceinline__ void rope_append(const RopeAppend &ra, float *y, int t, int L, float val, float pv, float c,
-                                            float s) {
+                                            float s, uint32_t tag = 0u) {
   const int dshift = ra.hshift + 1, D = 1 << dshift, qk = ra.dim + ra.kvw;
   const int p = ra.pos[t];
   int P = L;
@@ -283,7 +303,10 @@ __device__ __forceinline__ void rope_append(const RopeAppend &ra, float *y, int 
   }
   y[P] = val;
   if (P < ra.dim) {
-    ra.qrot[(size_t)t * ra.dim + P] = out;
+    if (ra.tagged)
+      tagged_store(ra.tagged + P, out, tag);
+    else
+      ra.qrot[(size_t)t * ra.dim + P] = out;
     return;
   }
   const bool is_k = P < qk;
@@ -297,10 +320,15 @@ __device__ __forceinline__ void rope_append(const RopeAppend &ra, float *y, int 
   }
   const size_t off = (((size_t)crow * (ra.kvw >> dshift) + j) * ra.max_seq + slot) * D + d;
   void *base = is_k ? ra.kc : ra.vc;
-  if (ra.kv_bf16)
-    reinterpret_cast<bf16_t *>(base)[off] = f32_to_bf16(out);
-  else
+  float stored = out;
+  if (ra.kv_bf16) {
+    const uint16_t hb = f32_to_bf16(out);
+    reinterpret_cast<bf16_t *>(base)[off] = hb;
+    stored = bf16_to_f32(hb);
+  } else {
     reinterpret_cast<float *>(base)[off] = out;
+  }
+  if (ra.tagged) tagged_store(ra.tagged + P, stored, tag);
 }
 
 struct GemvArgs {
@@ -352,6 +380,9 @@ struct GemmArgs {
   int ldo;
   // k_gemm_tiled: K slices (set by the launcher); more than one leaves partial sums in `part` for a reduce
   int kslices;
+  // k_gemm_tiled / k_gemm_big: 1 = multiply the operands' lo half too (F32 activations to ~2^-17),
+  // 0 = the activations as bf16 (the hi half alone)
+  int lo;
 };
 
 // x[t] += sum_s part[s][t][:], then the next product's operands from rmsnorm(x[t], gain)
@@ -388,6 +419,17 @@ struct AttnArgs {
   const int32_t *table;
   int pages, npages;
   int *status;
+  // a launch that also runs the q/k/v product (one token row, contiguous cache row row0): the queries,
+  // and the key and value at t, come from that product's tagged words (RopeAppend::tagged: query
+  // number n at n, key head j number d at dim + j*head + d, value at dim + kvw + j*head + d)
+  const unsigned long long *tagged;
+  const unsigned long long *group_done;  // nullable: the product's per-row-group words (RopeAppend)
+  int rows_per_group;                    // the product's rows per group (it divides head)
+  int dim, kvw;
+  int spin_limit;  // polls before a wait for them gives up (status bit 3; the outputs are then NaN)
+  // that launch's chunk partials as tagged words [kv][nch][g*head + 2g + 1] (the o sums, (m, l) per
+  // query head, a last word written after the others), merged by the head's chunk blocks (merge_tagged)
+  unsigned long long *part_t;
 };
 
 // Prefill of S positions of one cache row (bf16 cache): RoPE + append and causal attention
@@ -459,6 +501,16 @@ hipError_t launch_gemv(int wdtype, GemvEpi epi, bool norm, const GemvArgs &a, in
 int gemv_supported(int wdtype, int K);  // 1 if the chunk count per thread is instantiated
 // rows' positions in a.pos[0..B-1], tmax = their maximum
 hipError_t launch_attention(int kvdtype, int head, int g, const AttnArgs &a, int B, int tmax, hipStream_t s);
+// the separate merge of nch chunk partials of `chunk` positions per (row, kv head)
+hipError_t launch_attention_merge(int head, int g, const AttnArgs &a, int B, int nch, int chunk, hipStream_t s);
+// The q/k/v product (one token row: GEMV with the RoPE + append epilogue) and the attention of that row
+// in one launch (+ the merge of its chunks when that runs separately).  ga: the product's arguments
+// (ga.ra.tagged set); aa: the attention's (aa.tagged, aa.nch slots per kv head for this launch's chunks).
+// Each launch's tag is epoch[0] * tag_mul + tag_add (the step counter times the layers, plus the layer
+// + 1).  Returns hipErrorNotSupported, having launched nothing, for shapes without an instantiation.
+hipError_t launch_qkv_attention(int wdtype, int kvdtype, int head, int g, const GemvArgs &ga, const AttnArgs &aa,
+                                int tmax, const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add, hipStream_t s);
+int qkv_attention_chunk(int kvdtype, int head, int g);  // positions per attention block of that launch (0: none)
 int attention_supported(int head, int g);
 int attention_paged_supported(int kvdtype, int head, int g);  // the matrix-core kernel (whole pages per wave)
 int attention_chunk(int kvdtype, int head, int g);
@@ -493,8 +545,9 @@ hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, 
 // argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]
 hipError_t launch_argmax_final(const float *part_v, const int *part_i, int n, int ld, int rows, int32_t *next,
                                hipStream_t s);
+// embedding rows of B tokens; `epoch` (nullable) is the step counter, advanced by one per launch
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
-                        int *status, hipStream_t s);
+                        int *status, unsigned *epoch, hipStream_t s);
 
 // sampling (temperature, top-k, top-p): per-row candidate keys of the first pass in `cand`
 // [B][nchunk][K2]; the second pass selects from the nchunk*K2 <= kSampleCandMax keys of a row

@@ -12,10 +12,13 @@ namespace lm {
 
 template <typename WT>
 __global__ __launch_bounds__(kThreads) void k_embed(const int32_t *tokens, const WT *emb, int dim, int vocab,
-                                                    float *x, int *status) {
+                                                    float *x, int *status, unsigned *epoch) {
   // block (s, b): 16-byte slices s*256 + tid of row b (dim is a multiple of 8)
   constexpr int E = Vec16<WT>::E;
   const int b = blockIdx.y;
+  // the step counter (tags of the step's tagged words): the launch boundary publishes it to the
+  // step's later launches
+  if (epoch && blockIdx.x == 0 && b == 0 && threadIdx.x == 0) epoch[0] = epoch[0] + 1u;
   const int tok = tokens[b];
   const int ci = blockIdx.x * kThreads + threadIdx.x;
   if (ci * E >= dim) return;
@@ -37,15 +40,15 @@ __global__ void k_zero(uint32_t *p, size_t n) {
 }
 
 hipError_t launch_embed(int wdtype, const int32_t *tokens, const void *emb, int dim, int vocab, float *x, int B,
-                        int *status, hipStream_t s) {
+                        int *status, unsigned *epoch, hipStream_t s) {
   const int E = wdtype == LLAMA_BF16 ? 8 : 4;
   const dim3 grid((dim / E + kThreads - 1) / kThreads, B);
   if (wdtype == LLAMA_BF16)
     launch(k_embed<bf16_t>, grid, dim3(kThreads), s, true, true, tokens, reinterpret_cast<const bf16_t *>(emb), dim,
-           vocab, x, status);
+           vocab, x, status, epoch);
   else
     launch(k_embed<float>, grid, dim3(kThreads), s, true, true, tokens, reinterpret_cast<const float *>(emb), dim,
-           vocab, x, status);
+           vocab, x, status, epoch);
   return hipGetLastError();
 }
 

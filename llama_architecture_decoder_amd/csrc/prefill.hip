@@ -9,6 +9,8 @@
 //   * causal grouped-query attention over the cache, flash style: key tiles of 64 positions stream
 //     through LDS once per (32-position query tile, kv head) and serve the g query heads of the group;
 //     scores and probabilities stay in registers (softmax with a running maximum, base 2).
+#include <type_traits>
+
 #include "common.h"
 
 namespace lm {
@@ -48,10 +50,12 @@ __device__ __forceinline__ void swiglu_store(const GemmArgs &a, int t, int n, fl
   }
 }
 
-template <int EPI>
+// LO: the A operand's lo half is multiplied too (hi + lo carry the F32 activations to ~2^-17); without
+// it the product takes A as bf16 (hi, rounded to nearest even)
+template <int EPI, bool LO>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
   constexpr bool SW = EPI == EPI_SWIGLU;
-  constexpr int AC = 2 * kTM * (kTK / 8) / kThreads;  // 16-byte chunks of A (hi and lo) per thread per stage
+  constexpr int AC = (LO ? 2 : 1) * kTM * (kTK / 8) / kThreads;  // 16-byte chunks of A (hi, lo) per thread
   constexpr int BC = kTN * (kTK / 8) / kThreads;      // of B
   __shared__ __attribute__((aligned(16))) bf16_t s_a[2][2][kTM * kRowA];  // [buffer][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t s_b[2][kTN * kRowA];
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int row = wm * 64 + i * 32 + l32;
         ah[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][0][row * kRowA + ko]);
-        al[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][1][row * kRowA + ko]);
+        if (LO) al[i] = *reinterpret_cast<const u32x4 *>(&s_a[buf][1][row * kRowA + ko]);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
-          acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+          if (LO) acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
         }
     }
     if (s + 1 < nst) stash(buf ^ 1);
@@ -313,15 +317,17 @@ static BigPlan big_plan(int M, int N, int K, bool swiglu) {
 
 // NW waves: 8 (4 x 2 waves of 64 x 128, two per SIMD) or 4 (2 x 2 waves of 128 x 128, one per SIMD with
 // 256 accumulators, a quarter fewer operand reads per product)
-template <int EPI, int NW>
+// LO: as k_gemm_tiled (without it a stage holds [A hi | B] and each step does half the products)
+template <int EPI, int NW, bool LO>
 __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan plan) {
   constexpr bool SW = EPI == EPI_SWIGLU;
   constexpr int WM = NW / 2, TMW = kBM / WM, MI = TMW / 32;  // waves along M, rows per wave, 32-row tiles
-  constexpr int SPW = 16 / NW, LPW = 3 * SPW;                  // 1 KB segments per operand, loads per wave
-  // three stages, each [A hi | A lo | B]
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[3 * kBTile];
-  __shared__ __attribute__((aligned(1024))) bf16_t st1[3 * kBTile];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[3 * kBTile];
+  constexpr int NOP = LO ? 3 : 2;                              // operand tiles per stage
+  constexpr int SPW = 16 / NW, LPW = NOP * SPW;                // 1 KB segments per operand, loads per wave
+  // three stages, each [A hi | A lo | B] (or [A hi | B])
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[NOP * kBTile];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[NOP * kBTile];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NOP * kBTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -337,7 +343,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
   const int n0 = tnn * (SW ? kBN / 2 : kBN);
 
   // this thread's LPW 16-byte loads of a stage: wave segment g = part * NW + wave (1 KB = 16 rows) of
-  // operand o (0 A hi, 1 A lo, 2 B); lane -> row 16 g + lane / 4, stored position lane % 4
+  // operand o (0 A hi, 1 A lo, 2 B; without LO 0 A hi, 1 B); lane -> row 16 g + lane / 4, stored
+  // position lane % 4
   const bf16_t *gp[LPW];
   uint32_t lo[LPW];
 #pragma unroll
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
     const int o = i / SPW, g = (i % SPW) * NW + wave;
     const int row = g * 16 + (lane >> 2), c = (lane & 3) ^ bswz(row);
     lo[i] = (uint32_t)(o * kBTile + g * 512) * 2;  // byte offset of the wavefront's 1 KB within the stage
-    if (o < 2) {
+    if (o < NOP - 1) {
       const int t = min(m0 + row, a.M - 1);
       gp[i] = (o ? a.xlo : a.xhi) + (size_t)t * a.ldx + c * 8;
     } else if (SW) {
@@ -390,12 +397,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
       const int c = kk * 2 + hsel;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[kk][j] = *reinterpret_cast<const u32x4 *>(stage + 2 * kBTile + brow[j] * kBK + ((c ^ bswz(brow[j])) << 3));
+        bf[kk][j] = *reinterpret_cast<const u32x4 *>(stage + (NOP - 1) * kBTile + brow[j] * kBK +
+                                                     ((c ^ bswz(brow[j])) << 3));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int off = arow[i] * kBK + ((c ^ bswz(arow[i])) << 3);
         ah[kk][i] = *reinterpret_cast<const u32x4 *>(stage + off);
-        al[kk][i] = *reinterpret_cast<const u32x4 *>(stage + kBTile + off);
+        if (LO) al[kk][i] = *reinterpret_cast<const u32x4 *>(stage + kBTile + off);
       }
     }
 #pragma unroll
@@ -404,13 +412,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_big(GemmArgs a, BigPlan pla
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ah[kk][i], bf[kk][j], acc[i][j]);
+      if (LO) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(al[kk][i], bf[kk][j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(al[kk][i], bf[kk][j], acc[i][j]);
+      }
     }
     // schedule: the first half's reads, a quarter of the products, the second half's reads, the rest
-    constexpr int R = 2 * MI + 4, P = 8 * MI;
+    constexpr int R = (LO ? 2 : 1) * MI + 4, P = (LO ? 8 : 4) * MI;
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, P / 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
@@ -538,42 +548,38 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
     a.kslices = p.kslices;
     const int ks = a.kslices;
     const dim3 g(p.blocks, ks);
+    auto big = [&](auto epi_c) {
+      constexpr int E = decltype(epi_c)::value;
+      if (a.lo)
+        launch(k_gemm_big<E, kBWaves, true>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
+      else
+        launch(k_gemm_big<E, kBWaves, false>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
+      if (ks > 1) launch(k_tiled_reduce<E>, rg, dim3(kThreads), s, false, last, a, ks);
+    };
     switch (epi) {
-      case EPI_STORE:
-        launch(k_gemm_big<EPI_STORE, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
-        if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
-        break;
-      case EPI_RESID:
-        launch(k_gemm_big<EPI_RESID, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
-        if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
-        break;
-      case EPI_SWIGLU:
-        launch(k_gemm_big<EPI_SWIGLU, kBWaves>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
-        if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
-        break;
-      default:
-        return hipErrorInvalidValue;
+      case EPI_STORE: big(std::integral_constant<int, EPI_STORE>{}); break;
+      case EPI_RESID: big(std::integral_constant<int, EPI_RESID>{}); break;
+      case EPI_SWIGLU: big(std::integral_constant<int, EPI_SWIGLU>{}); break;
+      default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   a.kslices = a.part ? gemm_tiled_kslices(a.M, a.N, a.K, sw) : 1;
   const int ks = a.kslices;
+  auto tiled = [&](auto epi_c) {
+    constexpr int E = decltype(epi_c)::value;
+    const dim3 g(E == EPI_SWIGLU ? (a.N + kTN / 2 - 1) / (kTN / 2) : (a.N + kTN - 1) / kTN, mt, ks);
+    if (a.lo)
+      launch(k_gemm_tiled<E, true>, g, dim3(kThreads), s, first, last && ks == 1, a);
+    else
+      launch(k_gemm_tiled<E, false>, g, dim3(kThreads), s, first, last && ks == 1, a);
+    if (ks > 1) launch(k_tiled_reduce<E>, rg, dim3(kThreads), s, false, last, a, ks);
+  };
   switch (epi) {
-    case EPI_STORE:
-      launch(k_gemm_tiled<EPI_STORE>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, first, last && ks == 1, a);
-      if (ks > 1) launch(k_tiled_reduce<EPI_STORE>, rg, dim3(kThreads), s, false, last, a, ks);
-      break;
-    case EPI_RESID:
-      launch(k_gemm_tiled<EPI_RESID>, dim3((a.N + kTN - 1) / kTN, mt, ks), dim3(kThreads), s, first, last && ks == 1, a);
-      if (ks > 1) launch(k_tiled_reduce<EPI_RESID>, rg, dim3(kThreads), s, false, last, a, ks);
-      break;
-    case EPI_SWIGLU:
-      launch(k_gemm_tiled<EPI_SWIGLU>, dim3((a.N + kTN / 2 - 1) / (kTN / 2), mt, ks), dim3(kThreads), s, first,
-             last && ks == 1, a);
-      if (ks > 1) launch(k_tiled_reduce<EPI_SWIGLU>, rg, dim3(kThreads), s, false, last, a, ks);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case EPI_STORE: tiled(std::integral_constant<int, EPI_STORE>{}); break;
+    case EPI_RESID: tiled(std::integral_constant<int, EPI_RESID>{}); break;
+    case EPI_SWIGLU: tiled(std::integral_constant<int, EPI_SWIGLU>{}); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
