@@ -270,6 +270,19 @@ int lm_head_argmax(const llama_cfg *c, const llama_weights *w, const float *hidd
  */
 int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k);
 
+/*
+ * llama_sample without a scratch argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the candidate keys live
+ * in a static device array of the library (2 MiB on each GPU it runs on, held until the process
+ * ends; llama_sample_scratch_bytes(B, V, k) must not exceed it: 64 rows of the 128256-token vocabulary
+ * at k <= 256).  Same arguments, results and errors as llama_sample, plus E_UNSUPPORTED when the
+ * candidates would not fit and E_HIP when the array's address cannot be obtained.  Nothing is
+ * allocated.  Calls on one GPU share its array: two calls that overlap in time on one GPU (different
+ * streams, or threads) race; order them on one stream.  The stream must belong to the current device.
+ */
+int llama_sample_noalloc(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
+                         const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals,
+                         int32_t *topk_ids, void *stream);
 int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
                  const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals, int32_t *topk_ids,
                  void *scratch, size_t scratch_bytes, void *stream);

@@ -101,6 +101,8 @@ def lib():
     L.llama_sample_scratch_bytes.restype = i64
     L.llama_sample.argtypes = [vp, i64, i32, i32, ctypes.c_float, i32, ctypes.c_float, vp, ctypes.c_uint32, vp, vp,
                                vp, vp, vp, sz, vp]
+    L.llama_sample_noalloc.argtypes = [vp, i64, i32, i32, ctypes.c_float, i32, ctypes.c_float, vp, ctypes.c_uint32,
+                                       vp, vp, vp, vp, vp]
     L.llama_profile_enable.argtypes = [ctypes.c_int]
     L.llama_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
     _lib = L
@@ -368,6 +370,18 @@ def sample(logits, temp: float, k: int, p: float, seeds=None, draw: int = 0, u=N
                             _ptr(seeds), int(draw) & 0xFFFFFFFF, _ptr(u), ids.data_ptr(), _ptr(vals), _ptr(topk_ids),
                             scratch.data_ptr(), int(scratch.numel()), _stream_handle(stream))
     _check(rc, "llama_sample")
+    return ids
+
+
+def sample_noalloc(logits, temp: float, k: int, p: float, ids, seeds=None, draw: int = 0, u=None, vals=None,
+                   topk_ids=None, stream=None):
+    """As sample(), through llama_sample_noalloc: the candidates stay in the library's static device
+    buffer, so nothing is allocated here or in the library; `ids` (device int32 [B]) is required."""
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    rc = lib().llama_sample_noalloc(logits.data_ptr(), int(logits.stride(0)), B, V, float(temp), int(k), float(p),
+                                    _ptr(seeds), int(draw) & 0xFFFFFFFF, _ptr(u), ids.data_ptr(), _ptr(vals),
+                                    _ptr(topk_ids), _stream_handle(stream))
+    _check(rc, "llama_sample_noalloc")
     return ids
 
 

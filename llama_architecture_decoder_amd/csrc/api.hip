@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -1264,6 +1265,45 @@ int64_t llama_sample_scratch_bytes(int32_t B, int32_t V, int32_t k) {
   const int K2 = sample_k2(k);
   if (sample_candidates(V, K2) > kSampleCandMax) return LLAMA_E_UNSUPPORTED;
   return (int64_t)B * sample_chunks(V) * K2 * (int64_t)sizeof(uint64_t);
+}
+
+// The candidate keys of llama_sample_noalloc: a file-scope device array, one copy on each GPU the
+// library runs on (kept until the process ends).  Host code must not pass `scratch` itself to a kernel
+// (on the host it is only a stand-in for the device array): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept in `g_scratch`.
+constexpr int64_t kNoAllocKeys = 64 * 4096;  // 64 rows of 16 chunks x 256 keys: 2 MiB
+static __device__ __align__(256) uint64_t scratch[kNoAllocKeys];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// the device address of this GPU's array, or nullptr (HIP error)
+void *noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+int llama_sample_noalloc(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
+                         const uint32_t *seeds, uint32_t draw, const float *u, int32_t *ids, float *vals,
+                         int32_t *topk_ids, void *stream) {
+  const int64_t need = llama_sample_scratch_bytes(B, V, k);
+  if (need < 0) return (int)need;
+  if (need > kNoAllocKeys * (int64_t)sizeof(uint64_t)) return LLAMA_E_UNSUPPORTED;  // beyond the static buffer
+  if (B == 0) return llama_sample(logits, ld, B, V, temp, k, p, seeds, draw, u, ids, vals, topk_ids, nullptr, 0,
+                                  stream);
+  void *buf = noalloc_scratch();
+  if (!buf) return LLAMA_E_HIP;
+  return llama_sample(logits, ld, B, V, temp, k, p, seeds, draw, u, ids, vals, topk_ids, buf,
+                      (size_t)kNoAllocKeys * sizeof(uint64_t), stream);
 }
 
 int llama_sample(const float *logits, int64_t ld, int32_t B, int32_t V, float temp, int32_t k, float p,
