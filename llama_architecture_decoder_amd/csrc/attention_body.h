@@ -443,10 +443,13 @@ struct MfmaAttnShape {
 // kv head j): scores on the matrix cores from the query fragments (qhi, qlo) and the keys (getk(gi, kf)
 // supplies 16-key group gi in the B layout), the softmax pieces, the weighted V sum on the vector units,
 // then the NW waves combined in a fixed order into the chunk's partial (or, with one chunk, the output).
+// vt / vti (optional): this lane's value row vti is taken from vt (F32 values that are bf16 numbers)
+// instead of vr[vti], at its use, so a load still in flight into vr is not waited for earlier.
 template <int D, int G, int NPW, int NW, int MODE, typename GetK>
 __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int b, int t, int nact, int pw0,
                                             const u32x4 (&qhi)[D / 32], const u32x4 (&qlo)[D / 32], GetK getk,
-                                            const u32x4 (&vr)[NPW / (64 / (D / 8))], uint32_t tag = 0u) {
+                                            const u32x4 (&vr)[NPW / (64 / (D / 8))], uint32_t tag = 0u,
+                                            const float *vt = nullptr, int vti = -1) {
   using S = MfmaAttnShape<D, G, NPW, NW>;
   constexpr int CHUNK = S::CHUNK, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
   constexpr int GP = S::GP, NG = S::NG;
@@ -533,6 +536,7 @@ __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int
     }
     float vf[8];
     Vec16<bf16_t>::unpack(vr[i], vf);
+    if (vt && i == vti) load_f32<8>(vt + 8 * vl, vf);
 #pragma unroll
     for (int q = 0; q < G; ++q)
 #pragma unroll

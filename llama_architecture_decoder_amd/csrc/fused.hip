@@ -44,11 +44,15 @@ constexpr int kFusedNpw = 32;
 //  - the wait: poll one word per product row group first (group words), or the outputs themselves.
 //  For reference, the two launches without fusion: 505 us (8B), 295 us (1.7B).
 enum { kProductRoom = 0, kProductBalanced = 1, kProductAll = 2 };
+//  - the values' cache loads with the keys' (before the poll) or after the queries are seen (the scores
+//    and the softmax then run while they are in flight; matrix-core role only): after, 501-502 vs
+//    505-507 us at the 8B shape.
 template <typename KT>
 struct FusedPlan {
   static constexpr bool mfma = sizeof(KT) == 2;
   static constexpr int merge = mfma ? kMergePlain : kMergeTagged;
   static constexpr bool early_kv = mfma;
+  static constexpr bool late_v = mfma;
   static constexpr int product = mfma ? kProductRoom : kProductAll;
   static constexpr bool group_words = !mfma;
 };
@@ -164,13 +168,15 @@ __device__ __forceinline__ void attn_role_mfma(const AttnArgs &a, int c, int j, 
   const int qrow = lane & 15, qh8 = (lane >> 4) * 8;
   const int vl = lane % LPR, vg = lane / LPR;
   u32x4 kb[NGI][KS], vr[NV];
-  auto load_kv = [&]() {
+  auto load_k = [&]() {
 #pragma unroll
     for (int gi = 0; gi < NGI; ++gi) {
       const int p = min(pw0 + 16 * gi + qrow, tl);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kb[gi][ks] = load_stream16(Kh + (size_t)p * D + 32 * ks + qh8);
     }
+  };
+  auto load_v = [&]() {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int p = min(pw0 + PPI * i + vg, tl);
@@ -178,20 +184,27 @@ __device__ __forceinline__ void attn_role_mfma(const AttnArgs &a, int c, int j, 
     }
   };
   using P = FusedPlan<bf16_t>;
-  if (P::early_kv) load_kv();
+  if (P::early_kv) {
+    load_k();
+    if (!P::late_v) load_v();
+  }
   // (2) the queries (and the key and value at t) from the product
   if (P::group_words) wait_groups<G, D>(a, j, last, tag);
   poll_qkv<G, D>(a, j, last, tag, q_s, kt_s, vt_s);
-  if (!P::early_kv) load_kv();
+  if (!P::early_kv) load_k();
+  if (!P::early_kv || P::late_v) load_v();
   if (last) {
 #pragma unroll
     for (int gi = 0; gi < NGI; ++gi)
       if (pw0 + 16 * gi + qrow == t)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kb[gi][ks] = Vec16<bf16_t>::pack(&kt_s[32 * ks + qh8]);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (pw0 + PPI * i + vg == t) vr[i] = Vec16<bf16_t>::pack(&vt_s[8 * vl]);
+  }
+  // the lane's value row at t (if any) is taken from vt_s where it is used
+  int vti = -1;
+  if (last) {
+    const int dp = t - pw0 - vg;
+    if (dp >= 0 && dp % PPI == 0 && dp / PPI < NV) vti = dp / PPI;
   }
   float qf[KS][8];
 #pragma unroll
@@ -204,7 +217,7 @@ __device__ __forceinline__ void attn_role_mfma(const AttnArgs &a, int c, int j, 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = kb[gi][ks];
   };
-  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, tag);
+  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, tag, vt_s, vti);
 }
 
 // Vector-unit attention role (any cache type), as k_attn.
