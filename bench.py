@@ -330,7 +330,7 @@ def time_secondary(args, lm, synth, configs, c3=None):
     nxt = torch.empty(1, dtype=torch.int32, device="cuda")
     dec3.prefill(prompt, pos0=0, next_tok=nxt)
     torch.cuda.synchronize()
-    s3 = c3.decode_steps
+    s3 = min(c3.decode_steps, args.secondary_steps or c3.decode_steps)
     ev3, _, _ = time_decode(dec3, c3, c3.prompt_len, s3, args.warmup, int(nxt.item()))
     ms3 = ev3 / s3
     pev3, _, prof3 = time_decode(dec3, c3, c3.prompt_len, s3, 0, int(nxt.item()), profile=True)
@@ -539,6 +539,21 @@ def time_sample(lm, vocab, reps=200):
     return out
 
 
+def copy_probe():
+    """Three copies of a 1 GiB buffer (a plain copy kernel of known size, for calibrating HBM counters)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -558,6 +573,8 @@ def main():
                     help="time only the paged continuous-batching workload (for profiling its kernels)")
     ap.add_argument("--sample-only", action="store_true",
                     help="time only sampling over the 8B vocabulary (for profiling its kernels)")
+    ap.add_argument("--secondary-steps", type=int, default=0,
+                    help="decode steps of the F32 workloads (default: each workload's own count)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the decode steps, copy a 1 GiB buffer 3 times (counter calibration: a plain "
@@ -578,28 +595,32 @@ def main():
     p0 = cfg.kv_fill
     steps = max(1, min(args.steps, cfg.max_seq - p0))
     want_cpu = not args.no_cpu_baseline
+    def emit(d):
+        if args.copy_probe:
+            d["copy_probe_bytes"] = copy_probe()
+        print(json.dumps(d), flush=True)
+
     if args.secondary_only:
-        print(json.dumps({"secondary": time_secondary(args, lm, synth, configs)}), flush=True)
+        emit({"secondary": time_secondary(args, lm, synth, configs)})
         return
     if args.sample_only:
-        print(json.dumps({"sampling": time_sample(lm, cfg.vocab)}), flush=True)
+        emit({"sampling": time_sample(lm, cfg.vocab)})
         return
     if args.long_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
-        print(json.dumps({"long_context": time_long_context(cfg, lm, synth, dec.w)}), flush=True)
+        emit({"long_context": time_long_context(cfg, lm, synth, dec.w)})
         return
     if args.serving_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
-        print(json.dumps({"serving": time_serving(cfg, lm, synth, dec.w)}), flush=True)
+        emit({"serving": time_serving(cfg, lm, synth, dec.w)})
         return
     if args.prefill_only or args.batched_only:
         dec, _, _, _ = build_model(cfg, lm, synth, 16, 0, keep_host=False)
         c5 = configs.LLAMA31_8B_LONG
         if args.prefill_only:
-            print(json.dumps({"prefill": time_prefill(c5, lm, synth, dec.w, 2, 1)}), flush=True)
+            emit({"prefill": time_prefill(c5, lm, synth, dec.w, 2, 1)})
         else:
-            print(json.dumps({"batched": time_batched(c5, lm, synth, dec.w, min(args.steps, c5.decode_steps),
-                                                      args.warmup)}), flush=True)
+            emit({"batched": time_batched(c5, lm, synth, dec.w, min(args.steps, c5.decode_steps), args.warmup)})
         return
     dec, w, kc, vc = build_model(cfg, lm, synth, cfg.max_seq, p0, keep_host=want_cpu)
     first = int(synth.tokens(cfg, "bench/first", 1)[0])
@@ -662,16 +683,7 @@ def main():
     del dec
     torch.cuda.empty_cache()
     if args.copy_probe:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_probe_bytes"] = n
-        del src, dst
-        torch.cuda.empty_cache()
+        result["copy_probe_bytes"] = copy_probe()
 
     if want_cpu:
         log(f"cpu baseline: oracle on {cfg.name}, ~{args.cpu_seconds:.0f}s sample")

@@ -2,13 +2,14 @@
 
 Usage (from the repository root, after the rocprofv3 runs given in profiles/decode_8b_hbm_traffic.md):
 
-    python -m llama_architecture_decoder_amd.rocprof_summary traffic <fetch_dir> <write_dir> [out.json]
+    python -m llama_architecture_decoder_amd.rocprof_summary traffic <fetch_dir> <write_dir> [out.json] [workload]
 
 reads every ``*counter_collection.csv`` under the two directories (one FETCH_SIZE run, one WRITE_SIZE run of
 ``bench.py --copy-probe``), averages each counter per kernel over its dispatches, scales the counts by what
 they read for the 1 GiB plain copy (``__amd_rocclr_copyBuffer``: 1 GiB fetched, 1 GiB written) and writes
 the per-launch traffic of the decode kernels with the hash of the sources it was measured on (bench.py
-reports ``traffic`` only while that hash still matches).
+reports ``traffic`` only while that hash still matches).  workload: decode_8b (default), decode_1_7b
+(``bench.py --secondary-only``) or batched_8b (``bench.py --batched-only``, its attention).
 
     python -m llama_architecture_decoder_amd.rocprof_summary stats <kernel_stats.csv>
 
@@ -30,18 +31,30 @@ import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = ["llama_architecture_decoder_amd/csrc/gemv.hip", "llama_architecture_decoder_amd/csrc/common.h"]
+SOURCES = ["llama_architecture_decoder_amd/csrc/gemv.hip", "llama_architecture_decoder_amd/csrc/gemv_body.h",
+           "llama_architecture_decoder_amd/csrc/common.h"]
 COPY = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
-# decode kernels of the 8B shape (bf16 weights: k_gemv<unsigned short, KCH, EPI, NORM>)
+# decode kernels per workload (substrings of the kernel names; bf16 weights: unsigned short)
 KERNELS = {
-    "gate_up": "k_gemv<unsigned short, 2, 2, true>",
-    "down": "k_gemv<unsigned short, 7, 1, false>",
-    "qkv": "k_gemv<unsigned short, 2, 4, true>",
-    "o_proj": "k_gemv<unsigned short, 2, 1, false>",
-    "lm_head": "k_gemv<unsigned short, 2, 3, true>",
-    "attention": "k_attn_mfma<128, 4, 32, false, false, 8>",
+    "decode_8b": {
+        "gate_up": "k_gemv<unsigned short, 2, 2, true>",
+        "down": "k_gemv<unsigned short, 7, 1, false>",
+        "qkv_attention": "k_qkv_attn<unsigned short, 2, unsigned short, 128, 4>",
+        "o_proj": "k_gemv<unsigned short, 2, 1, false>",
+        "lm_head": "k_gemv<unsigned short, 2, 3, true>",
+    },
+    "decode_1_7b": {
+        "gate_up": "k_gemv<float, 2, 2, true>",
+        "down": "k_gemv<float, 8, 1, false>",
+        "qkv_attention": "k_qkv_attn<float, 2, float, 64, 1>",
+        "o_proj": "k_gemv<float, 2, 1, false>",
+        "lm_head": "k_gemv<float, 2, 3, true>",
+    },
+    "batched_8b": {
+        "attention": "k_attn_mfma<128, 4, 64, true, false, 4>",
+    },
 }
 
 
@@ -84,24 +97,39 @@ def find(means, sub):
     return hits[0][1]
 
 
-def traffic(fetch_dir: str, write_dir: str, out: str):
+def traffic(fetch_dir: str, write_dir: str, out: str, workload: str = "decode_8b"):
     sys.path.insert(0, ROOT)
     import bench
+    import synth
     from synth import configs
-    cfg = configs.LLAMA31_8B
     fm = counter_means(fetch_dir, "FETCH_SIZE", COPY)
     wm = counter_means(write_dir, "WRITE_SIZE", COPY)
     ff = COPY_BYTES / 1024 / find(fm, COPY)[1]
     wf = COPY_BYTES / 1024 / find(wm, COPY)[1]
-    t_mean = cfg.kv_fill + 4  # the mean position of the 8 profiled steps after one warm-up step
-    rec = {"kernel": "gate_up", "sources": SOURCES, "sources_sha256_16": sources_hash(),
+    if workload == "decode_8b":
+        cfg = configs.LLAMA31_8B
+        t_mean = cfg.kv_fill + 4  # the mean position of the 8 profiled steps after one warm-up step
+        alg = lambda cls: bench.kernel_bytes(cfg, cls, t_mean)
+    elif workload == "decode_1_7b":
+        # `bench.py --secondary-only --secondary-steps 16 --warmup 1`: the prompt's positions go through the
+        # decode kernels too (F32 models prefill one position after another), then one warm-up step and
+        # the timed and the profiled pass of 16 steps: the mean algorithmic bytes over those dispatches
+        cfg = configs.SMOLLM2_1_7B
+        P = cfg.prompt_len
+        ts = list(range(P)) + [P] + 2 * list(range(P, P + 16))
+        alg = lambda cls: int(round(sum(bench.kernel_bytes(cfg, cls, t) for t in ts) / len(ts)))
+    else:  # batched_8b: every row's K/V rows 0..t per layer launch, at the mean step (warm-up 1 + 4 steps)
+        cfg = configs.LLAMA31_8B_LONG
+        lens = synth.row_lengths(cfg).astype("int64") + 3
+        alg = lambda cls: int(sum(2 * cfg.kvw * cfg.kvbytes * (int(t) + 1) for t in lens))
+    rec = {"workload": workload, "kernel": "gate_up", "sources": SOURCES, "sources_sha256_16": sources_hash(),
            "fetch_factor": ff, "write_factor": wf, "per_launch": {}}
     rows = []
-    for cls, sub in KERNELS.items():
+    for cls, sub in KERNELS[workload].items():
         n, fk = find(fm, sub)
         _, wk = find(wm, sub)
         tb = (fk * ff + wk * wf) * 1024
-        ab = bench.kernel_bytes(cfg, cls, t_mean)
+        ab = alg(cls)
         rec["per_launch"][cls] = {"fetch_kib": fk, "write_kib": wk, "traffic_bytes": tb, "algorithmic_bytes": ab,
                                   "dispatches": n}
         rows.append(f"| {cls} (`{sub}`) | {n} | {fk:.1f} | {wk:.1f} | {tb:,.0f} | {ab:,} | {tb / ab:.3f} |")
@@ -152,7 +180,8 @@ def mfma(directory: str, clock_ghz: float = 2.4, simds: int = 1024):
 if __name__ == "__main__":
     if len(sys.argv) >= 4 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3],
-                sys.argv[4] if len(sys.argv) > 4 else os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json"))
+                sys.argv[4] if len(sys.argv) > 4 else os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json"),
+                sys.argv[5] if len(sys.argv) > 5 else "decode_8b")
     elif len(sys.argv) == 3 and sys.argv[1] == "stats":
         stats(sys.argv[2])
     elif len(sys.argv) == 3 and sys.argv[1] == "mfma":
