@@ -22,6 +22,7 @@
 // staged once per block in LDS.  Each wavefront keeps its scores in registers and forms its own
 // softmax pieces (max, exp-sum, exp-weighted V sum) with cross-lane permutes; the 4 wavefronts are
 // combined through LDS.
+#include <algorithm>
 #include <type_traits>
 
 #include "attention_body.h"
@@ -156,6 +157,298 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
   mfma_attend<D, G, NPW, NW, SELF ? kMergeSelf : kMergePlain>(a, c, j, b, t, nact, pw0, qhi, qlo, getk, vr);
 }
 
+// positions per wavefront of the matrix-core kernel: 64 (chunks of 256) measured faster than 32 or 128
+// for both one row at 8K positions and 32 rows at 8K..32K
+constexpr int kMfmaNpw = 64;
+
+// Streamed attention for long rows and many blocks (batched rows, long contexts).  The step's chunks
+// of 256 positions, in (row, kv head, chunk) order, are cut into sk_blocks equal runs (two blocks per
+// CU, all resident); block k takes run k, crossing from one (row, kv head) segment to the next, and
+// writes one partial per segment it touches (the merge combines a segment's partials in block order,
+// which is position order).  Each wavefront keeps a running softmax over its 64 positions of every
+// chunk (running maximum m and sum l per query head, its output slices rescaled by 2^(m_old - m_new)
+// when the maximum grows), so a segment's result is the same combination of the same terms as in the
+// one-chunk-per-block kernel.  The next chunk's keys are requested as soon as this chunk's scores are
+// formed (their registers are free), its values as soon as this chunk's weighted sum is done, so every
+// block keeps about a chunk of loads in flight from its first chunk to its last.  Against one block per
+// chunk (32 rows of 8K..32K positions): the chunk partials' stores (40 MB per layer, interleaved with
+// the cache stream) cost far more than their bytes (~39 us of a ~426 us launch), and spans of 4 or 8
+// chunks per block left the launch's last round ragged.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
+  using S = MfmaAttnShape<D, G, kMfmaNpw, 4>;
+  constexpr int NW = 4, NPW = S::NPW, CHUNK = S::CHUNK, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI;
+  constexpr int NV = S::NV, GP = S::GP, IPG = 16 / PPI;
+  const int nb = gridDim.x, T = a.sk_total;
+  const int g0 = (int)((long)blockIdx.x * T / nb), g1 = (int)((long)(blockIdx.x + 1) * T / nb);
+  if (g0 >= g1) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qrow = lane & 15, qh8 = (lane >> 4) * 8, qbase = 4 * (lane >> 4);
+  const int vl = lane % LPR, vg = lane / LPR;
+
+  __shared__ __attribute__((aligned(16))) bf16_t k_s[NW][16 * S::KROW];  // each wave's 16 keys in turn
+  __shared__ __attribute__((aligned(16))) u32x4 q_s[KS][2][64];            // query fragments (hi, lo) by lane
+  __shared__ __attribute__((aligned(16))) float p_s[NW][NPW][GP];          // each wave's weights
+  __shared__ float r_s[NW][G];                                              // each wave's rescale factors
+  __shared__ float m_s[NW][G], l_s[NW][G];
+  __shared__ __attribute__((aligned(16))) float o_w[NW][G][D];             // each wave's output slices
+
+  // the block whose run holds chunk g: the last k with k * T / nb <= g
+  auto blk = [&](int g) { return (int)(((long)(g + 1) * nb - 1) / T); };
+  // where the run starts: row b (the last whose first chunk is at or before g0), kv head j, chunk c
+  int b;
+  {
+    int lo = 0, hi = a.sk_rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.sk_prefix[mid] <= g0) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+  }
+  int t = a.pos[b];
+  int n = t / CHUNK + 1;  // chunks of each of row b's segments
+  int j = (g0 - a.sk_prefix[b]) / n, c = (g0 - a.sk_prefix[b]) % n;
+
+  const bf16_t *Kc = reinterpret_cast<const bf16_t *>(a.kc);
+  const bf16_t *Vc = reinterpret_cast<const bf16_t *>(a.vc);
+  auto seg_off = [&](int bb, int jj) { return ((size_t)(a.row0 + bb) * a.kv + jj) * (size_t)a.max_seq * D; };
+  // Requests go through buffer descriptors of the segment's rows 0..tt (scalar registers): lane l asks
+  // for 16 bytes at 8 (l%LPR) of row l/LPR of each PPI-row group of its 64 positions (whole rows per
+  // load), one 32-bit offset register per request; a row past tt is outside the descriptor, so the
+  // hardware returns zeros without a memory access (their scores are masked, their weights 0).  `rest`:
+  // the requests after the run's last chunk, all outside, fetch nothing.
+  u32x4 kr[NV], vr[NV];
+  auto rsrc = [&](const bf16_t *base, int tt) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), (short)0, (tt + 1) * D * 2, 0x00020000);
+  };
+  // (`rest` sets the offset's top bit, past any descriptor: arithmetic, not a branch around each request)
+  auto voff = [&](int cc, bool rest, int i) {
+    return (uint32_t)((cc * CHUNK + wave * NPW + PPI * i + vg) * D * 2 + 16 * vl) | ((uint32_t)rest << 31);
+  };
+  auto load_k = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
+  };
+  auto load_v = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
+  };
+  size_t off = seg_off(b, j);
+  __amdgpu_buffer_rsrc_t rk = rsrc(Kc + off, t), rv = rsrc(Vc + off, t);
+  load_k(rk, c, false);
+  load_v(rv, c, false);
+  // the segment's query fragments (the same for every wavefront) into LDS, read per key group: registers
+  // go to the loads of two chunks in flight.  The barrier also orders the previous segment's reads of
+  // the combine arrays before any later write.
+  auto load_q = [&]() {
+    if (wave == 0) {
+      const float *qp = a.q + (size_t)b * (a.kv * G * D) + ((size_t)j * G + min(qrow, G - 1)) * D;
+      float qf[KS][8];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) load_f32<8>(qp + 32 * ks + qh8, qf[ks]);
+      u32x4 qhi[KS], qlo[KS];
+      q_fragments<D, G>(qf, qrow, qhi, qlo);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        q_s[ks][0][lane] = qhi[ks];
+        q_s[ks][1][lane] = qlo[ks];
+      }
+    }
+    lds_barrier();
+  };
+  load_q();
+
+  // LDS operations of a wave complete in order; a wave barrier between its writes and its reads
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+  bf16_t *kw = k_s[wave];
+  const float scale2 = a.scale * 1.4426950408889634f;
+  float mrun[4], lrun[4];  // this lane's heads qbase + r: running maximum (base 2) and sum
+  float o[G][8];
+  auto reset = [&] {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mrun[r] = -INFINITY;
+      lrun[r] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] = 0.f;
+  };
+  reset();
+
+  for (int g = g0; g < g1; ++g) {
+    // the chunk after this one in the run
+    int b2 = b, j2 = j, c2 = c + 1;
+    if (c2 >= n) {
+      c2 = 0;
+      if (++j2 >= a.kv) {
+        j2 = 0;
+        ++b2;
+      }
+    }
+    const bool more = g + 1 < g1;
+    const int t2 = more ? a.pos[b2] : t;
+    const size_t off2 = more ? seg_off(b2, j2) : off;
+    const __amdgpu_buffer_rsrc_t rk2 = rsrc(Kc + off2, t2), rv2 = rsrc(Vc + off2, t2);
+
+    const int pw0 = c * CHUNK + wave * NPW;
+    const int p1 = min(c * CHUNK + CHUNK, t + 1);
+    // (1) scores, base 2, on the matrix cores: the 16 keys of group gi through the wave's LDS tile into
+    // the B layout (lane l: key l%16, numbers 32 ks + 8(l/16) .. +8)
+    float sc[NGI][4];
+#pragma unroll
+    for (int gi = 0; gi < NGI; ++gi) {
+#pragma unroll
+      for (int u = 0; u < IPG; ++u)
+        *reinterpret_cast<u32x4 *>(&kw[(PPI * u + vg) * S::KROW + 8 * vl]) = kr[gi * IPG + u];
+      wave_sync();
+      u32x4 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4 *>(&kw[qrow * S::KROW + 32 * ks + qh8]);
+      wave_sync();
+      af32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = mfma16(q_s[ks][0][lane], kf[ks], acc);
+        acc = mfma16(q_s[ks][1][lane], kf[ks], acc);
+      }
+      const int p = pw0 + 16 * gi + qrow;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[gi][r] = (p < p1) ? acc[r] * scale2 : -INFINITY;
+    }
+    // (2) the next chunk's keys go out now (their registers are free; the scheduling barriers keep the
+    // compiler from hoisting these requests above the use of the registers they refill, which would
+    // need a second set of registers)
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(rk2, c2, !more);
+    __builtin_amdgcn_sched_barrier(0);
+    // (3) per head: the new running maximum, the factor for what was summed so far, this chunk's
+    // weights 2^(s2 - max) and their sum (reference 0 while no position has been seen: every weight 0)
+    float fr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = sc[0][r];
+#pragma unroll
+      for (int gi = 1; gi < NGI; ++gi) m = fmaxf(m, sc[gi][r]);
+      const float mn = fmaxf(mrun[r], row16_max(m));
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      fr[r] = (mrun[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mref);
+      float l = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NGI; ++gi) {
+        const float w = __builtin_amdgcn_exp2f(sc[gi][r] - mref);
+        sc[gi][r] = w;
+        l += w;
+      }
+      lrun[r] = fmaf(lrun[r], fr[r], group_sum<16>(l));
+      mrun[r] = mn;
+    }
+    if (qbase < G) {
+#pragma unroll
+      for (int gi = 0; gi < NGI; ++gi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (qbase + r < GP) p_s[wave][16 * gi + qrow][qbase + r] = sc[gi][r];
+      if (qrow == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (qbase + r < G) r_s[wave][qbase + r] = fr[r];
+      }
+    }
+    wave_sync();
+    // (4) o[q][e] = f[q] * o[q][e] + sum over this lane's positions of w[q] * V[p][8 vl + e]
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const float f = r_s[wave][q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] *= f;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float w[GP];
+#pragma unroll
+      for (int k = 0; k < GP; k += 4) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(&p_s[wave][PPI * i + vg][k]);
+        w[k] = w4.x;
+        w[k + 1] = w4.y;
+        w[k + 2] = w4.z;
+        w[k + 3] = w4.w;
+      }
+      float vf[8];
+      Vec16<bf16_t>::unpack(vr[i], vf);
+#pragma unroll
+      for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] = fmaf(w[q], vf[e], o[q][e]);
+    }
+    wave_sync();  // this chunk's weights and factors are read before the next chunk writes them
+    // (5) the next chunk's values
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(rv2, c2, !more);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (!more || b2 != b || j2 != j) {
+      // (6) the segment's partial: the wave's lane groups summed (lanes that share lane % LPR hold the
+      // same numbers), the waves combined in a fixed order (factor 2^(m_w - M), 0 for a wave without
+      // positions); slot = this block's place among the blocks the segment's chunks fall in
+#pragma unroll
+      for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] = strided_sum<LPR>(o[q][e]);
+      if (vg == 0) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          *reinterpret_cast<float4 *>(&o_w[wave][q][8 * vl]) = make_float4(o[q][0], o[q][1], o[q][2], o[q][3]);
+          *reinterpret_cast<float4 *>(&o_w[wave][q][8 * vl + 4]) = make_float4(o[q][4], o[q][5], o[q][6], o[q][7]);
+        }
+      }
+      if (qbase < G && qrow == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (qbase + r < G) {
+            m_s[wave][qbase + r] = mrun[r];
+            l_s[wave][qbase + r] = lrun[r];
+          }
+      }
+      lds_barrier();
+      const int part = (int)blockIdx.x - blk(a.sk_prefix[b] + j * n);
+      const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
+      for (int idx = tid; idx < G * D; idx += NW * 64) {
+        const int q = idx / D, d = idx % D;
+        float M = m_s[0][q];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, m_s[w][q]);
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = (m_s[w][q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][q] - M);
+          acc = fmaf(f, o_w[w][q][d], acc);
+          L = fmaf(f, l_s[w][q], L);
+        }
+        emit_chunk<G, D, kMergePlain>(a, b, j, part, slot, idx, q, d, acc, M, L, 0u);
+      }
+      reset();
+      if (more) {
+        b = b2;
+        j = j2;
+        t = t2;
+        n = t / CHUNK + 1;
+        off = off2;
+        rk = rk2;
+        rv = rv2;
+        load_q();
+      }
+    }
+    c = c2;
+  }
+}
+
 // Merge of the chunk partials of one (row, kv head), in chunk order (a separate launch: the kernel
 // boundary makes the partials visible without cache-wide fences inside the attention kernel).
 // Block (og, j, b) produces 64 consecutive outputs of query head i = og*64/head of group j:
@@ -170,7 +463,13 @@ __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
   constexpr int MLR = (kAttnMaxChunks + NT - 1) / NT;
   const int og = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
-  const int nact = t / chunk + 1;
+  int nact = t / chunk + 1;
+  if (a.sk_total) {
+    // streamed attention: the segment's partials are those of the blocks its chunks fall in
+    const int nb = a.sk_blocks, T = a.sk_total, g = a.sk_prefix[b] + j * nact;
+    auto blk = [&](int x) { return (int)(((long)(x + 1) * nb - 1) / T); };
+    nact = blk(g + nact - 1) - blk(g) + 1;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = (og * 64) / D, d = (og * 64) % D + lane;
   __shared__ float w_s[kAttnMaxChunks];
@@ -249,9 +548,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
   }
 }
 
-// positions per wavefront of the matrix-core kernel: 64 (chunks of 256) measured faster than 32 or 128
-// for both one row at 8K positions and 32 rows at 8K..32K
-constexpr int kMfmaNpw = 64;
 template <typename KT, int D, int G>
 constexpr bool use_mfma() {
   return sizeof(KT) == 2 && MfmaAttnShape<D, G, kMfmaNpw>::LDS <= 64 * 1024;
@@ -329,6 +625,20 @@ hipError_t launch_attention_merge(int head, int g, const AttnArgs &a, int B, int
   return hipErrorInvalidValue;
 }
 
+// Blocks of the streamed attention: two per CU of the current device (its kernel fits two per CU), all
+// resident at once; 0 if the count cannot be read
+static int stream_blocks() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) return 0;
+    cached[dev] = 2 * cu;
+  }
+  return cached[dev];
+}
+
 // One attention launch (+ the merge when more than one chunk): chunks of `chunk` positions cover 0..tmax.
 template <typename KT, int D, int G>
 static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
@@ -348,7 +658,22 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
     // about one block per CU finishes sooner with the keys loaded straight in the MFMA layout, and with
     // 8 wavefronts of 32 positions rather than 4 of 64 (same chunk; one row at 8K: 14.4 vs 14.6 us per
     // layer with the merge)
-    const bool krows = (long)B * a.kv * nch_launch >= 4096;
+    const long nblk = (long)B * a.kv * nch_launch;
+    const bool krows = nblk >= 4096;
+    if (krows && !self && !a.table && stream_blocks() > 0) {
+      // the streamed kernel: equal runs of the step's chunks over a resident grid, then the merge
+      long total = 0;
+      for (int b = 0; b < B; ++b) {
+        a.sk_prefix[b] = (int)total;
+        total += (long)a.kv * (a.pos[b] / chunk + 1);
+      }
+      a.sk_total = (int)total;
+      a.sk_rows = B;
+      a.sk_blocks = (int)std::min<long>(stream_blocks(), total);
+      a.direct = 0;
+      launch(k_attn_stream<D, G>, dim3(a.sk_blocks), dim3(kThreads), s, true, false, a);
+      return merge_g<G, D>(a, B, nch_launch, chunk, s);
+    }
     if (krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, true, true>, grid, dim3(kThreads), s, true, true, a);
     if (krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, true, false>, grid, dim3(kThreads), s, true, !merge, a);
     if (!krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, false, true>, grid, dim3(kThreads), s, true, true, a);

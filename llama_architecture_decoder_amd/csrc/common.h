@@ -125,6 +125,8 @@ __device__ __forceinline__ u32x4 load_stream16(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// cache policy of a streaming buffer load (the non-temporal hint, as load_stream16)
+constexpr int kBufferNT = 2;
 
 // Block barrier that orders LDS only: waves publish LDS writes to each other, while global loads issued
 // before it stay in flight (a full __syncthreads() also waits for every outstanding global access).
@@ -430,6 +432,11 @@ struct AttnArgs {
   // that launch's chunk partials as tagged words [kv][nch][g*head + 2g + 1] (the o sums, (m, l) per
   // query head, a last word written after the others), merged by the head's chunk blocks (merge_tagged)
   unsigned long long *part_t;
+  // streamed attention (k_attn_stream; set by its launcher, sk_total = 0 otherwise): the step's chunks
+  // in (row, kv head, chunk) order, sk_total of them, row b's first at sk_prefix[b]; sk_blocks blocks
+  // take equal runs of them, and segment (b, j)'s partials are those of the blocks its chunks fall in
+  int sk_total, sk_blocks, sk_rows;
+  int sk_prefix[kMaxBatch];
 };
 
 // Prefill of S positions of one cache row (bf16 cache): RoPE + append and causal attention

@@ -32,8 +32,9 @@ CASES = [
     ("smollm2_135m_bf16", 3, 17, 512),
     ("llama31_8b", 2, 2, 256),           # matrix-core rows: one ragged 16-row tile
     ("llama31_8b", 2, 20, 512),          # two tiles, the second ragged
-    ("llama31_8b", 2, 33, 4096),         # three tiles, lengths across several attention chunks
+    ("llama31_8b", 2, 33, 4096),         # three tiles, lengths across several attention chunks (spans of 2)
     ("llama31_8b", 2, 64, 512),          # the largest batch: four full tiles
+    ("llama31_8b", 2, 40, 8192),         # attention in spans of 4 chunks, ragged last spans and chunks
 ]
 
 
