@@ -174,9 +174,13 @@ constexpr int kMfmaNpw = 64;
 // chunk (32 rows of 8K..32K positions): the chunk partials' stores (40 MB per layer, interleaved with
 // the cache stream) cost far more than their bytes (~39 us of a ~426 us launch), and spans of 4 or 8
 // chunks per block left the launch's last round ragged.
+#ifndef STREAM_NPW
+#define STREAM_NPW 64
+#endif
+constexpr int kStreamNpw = STREAM_NPW;  // positions per wavefront and chunk in the streamed kernel
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
-  using S = MfmaAttnShape<D, G, kMfmaNpw, 4>;
+  using S = MfmaAttnShape<D, G, kStreamNpw, 4>;
   constexpr int NW = 4, NPW = S::NPW, CHUNK = S::CHUNK, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI;
   constexpr int NV = S::NV, GP = S::GP, IPG = 16 / PPI;
   const int nb = gridDim.x, T = a.sk_total;
@@ -226,18 +230,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
   auto voff = [&](int cc, bool rest, int i) {
     return (uint32_t)((cc * CHUNK + wave * NPW + PPI * i + vg) * D * 2 + 16 * vl) | ((uint32_t)rest << 31);
   };
-  auto load_k = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest) {
+  // requests i0 .. i1-1 of a chunk's keys / values
+  auto load_k = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
+    for (int i = i0; i < i1; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
   };
-  auto load_v = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest) {
+  auto load_v = [&](__amdgpu_buffer_rsrc_t r, int cc, bool rest, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
+    for (int i = i0; i < i1; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff(cc, rest, i), 0, kBufferNT);
   };
   size_t off = seg_off(b, j);
   __amdgpu_buffer_rsrc_t rk = rsrc(Kc + off, t), rv = rsrc(Vc + off, t);
-  load_k(rk, c, false);
-  load_v(rv, c, false);
+  load_k(rk, c, false, 0, NV);
+  load_v(rv, c, false, 0, NV);
   // the segment's query fragments (the same for every wavefront) into LDS, read per key group: registers
   // go to the loads of two chunks in flight.  The barrier also orders the previous segment's reads of
   // the combine arrays before any later write.
@@ -321,13 +326,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
       const int p = pw0 + 16 * gi + qrow;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[gi][r] = (p < p1) ? acc[r] * scale2 : -INFINITY;
+      // (2) the next chunk's keys go out as their registers free up: the first half after the first
+      // half of the groups (the scheduling barriers keep the compiler from hoisting these requests above
+      // the use of the registers they refill, which would need a second set of registers)
+      if (gi == NGI / 2 - 1 || gi == NGI - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(rk2, c2, !more, gi == NGI - 1 ? NV / 2 : 0, gi == NGI - 1 ? NV : NV / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // (2) the next chunk's keys go out now (their registers are free; the scheduling barriers keep the
-    // compiler from hoisting these requests above the use of the registers they refill, which would
-    // need a second set of registers)
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(rk2, c2, !more);
-    __builtin_amdgcn_sched_barrier(0);
     // (3) per head: the new running maximum, the factor for what was summed so far, this chunk's
     // weights 2^(s2 - max) and their sum (reference 0 while no position has been seen: every weight 0)
     float fr[4];
@@ -386,12 +393,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
       for (int q = 0; q < G; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[q][e] = fmaf(w[q], vf[e], o[q][e]);
+      // (5) the next chunk's values, each half as its registers free up
+      if (i == NV - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(rv2, c2, !more, 0, NV);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wave_sync();  // this chunk's weights and factors are read before the next chunk writes them
-    // (5) the next chunk's values
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(rv2, c2, !more);
-    __builtin_amdgcn_sched_barrier(0);
 
     if (!more || b2 != b || j2 != j) {
       // (6) the segment's partial: the wave's lane groups summed (lanes that share lane % LPR hold the
@@ -662,17 +671,18 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
     const bool krows = nblk >= 4096;
     if (krows && !self && !a.table && stream_blocks() > 0) {
       // the streamed kernel: equal runs of the step's chunks over a resident grid, then the merge
+      constexpr int schunk = MfmaAttnShape<D, G, kStreamNpw, 4>::CHUNK;
       long total = 0;
       for (int b = 0; b < B; ++b) {
         a.sk_prefix[b] = (int)total;
-        total += (long)a.kv * (a.pos[b] / chunk + 1);
+        total += (long)a.kv * (a.pos[b] / schunk + 1);
       }
       a.sk_total = (int)total;
       a.sk_rows = B;
       a.sk_blocks = (int)std::min<long>(stream_blocks(), total);
       a.direct = 0;
       launch(k_attn_stream<D, G>, dim3(a.sk_blocks), dim3(kThreads), s, true, false, a);
-      return merge_g<G, D>(a, B, nch_launch, chunk, s);
+      return merge_g<G, D>(a, B, nch_launch, schunk, s);
     }
     if (krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, true, true>, grid, dim3(kThreads), s, true, true, a);
     if (krows && !self) launch(k_attn_mfma<D, G, kMfmaNpw, true, false>, grid, dim3(kThreads), s, true, !merge, a);

@@ -53,7 +53,7 @@ KERNELS = {
         "lm_head": "k_gemv<float, 2, 3, true>",
     },
     "batched_8b": {
-        "attention": "k_attn_mfma<128, 4, 64, true, false, 4>",
+        "attention": "k_attn_stream<128, 4>",
     },
 }
 
