@@ -565,6 +565,8 @@ def main():
                     help="time only the 4096-position prefill (for profiling its kernels)")
     ap.add_argument("--batched-only", action="store_true",
                     help="time only the batch-32 long-context decode (for profiling its kernels)")
+    ap.add_argument("--small-only", nargs="?", const="both", choices=["both", "135m", "360m"],
+                    help="only the small shapes (135M and 360M decode, or the one named)")
     ap.add_argument("--secondary-only", action="store_true",
                     help="time only the 1.7B-shaped decode (for profiling its kernels)")
     ap.add_argument("--long-only", action="store_true",
@@ -602,6 +604,11 @@ def main():
 
     if args.secondary_only:
         emit({"secondary": time_secondary(args, lm, synth, configs)})
+        return
+    if args.small_only:
+        shapes = {"135m": [configs.SMOLLM2_135M], "360m": [configs.SMOLLM2_360M],
+                  "both": [configs.SMOLLM2_135M, configs.SMOLLM2_360M]}[args.small_only]
+        emit({"small_shapes": [time_secondary(args, lm, synth, configs, c) for c in shapes]})
         return
     if args.sample_only:
         emit({"sampling": time_sample(lm, cfg.vocab)})
