@@ -113,7 +113,7 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, done, epoch, tagged, group_done, part_t, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
+  size_t status, done, epoch, tagged, group_done, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
       total;
   int nch;    // chunk slots per (row, kv head) of the attention partials
   int nch_f;  // chunk slots of the one-row launch that runs the q/k/v product with the attention
@@ -166,7 +166,6 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.epoch = take(sizeof(unsigned));
   L.tagged = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));
   L.group_done = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));  // at most a group per row
-  L.part_t = take(sizeof(unsigned long long) * (size_t)L.nch_f * d.kv * (d.g * d.head + 2 * d.g + 1));
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * rows * d.dim);
@@ -752,7 +751,6 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       af.kvw = KW;
       af.spin_limit = kSpinLimit;
       af.nch = x.L.nch_f;
-      af.part_t = x.at<unsigned long long>(x.L.part_t);
       ProfScope ps(LLAMA_K_QKV_ATTN, x.s);
       const hipError_t e = launch_qkv_attention(wdt, x.c->kv_dtype, (int)d.head, (int)d.g, a, af, tmax,
                                                 x.at<unsigned>(x.L.epoch), (uint32_t)d.layers, (uint32_t)l + 1u, x.s);

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
           acc = fmaf(f, o_w[w][q][d], acc);
           L = fmaf(f, l_s[w][q], L);
         }
-        emit_chunk<G, D, kMergePlain>(a, b, j, part, slot, idx, q, d, acc, M, L, 0u);
+        emit_chunk<G, D, kMergePlain>(a, b, j, part, slot, idx, q, d, acc, M, L);
       }
       reset();
       if (more) {

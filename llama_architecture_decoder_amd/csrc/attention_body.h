@@ -130,125 +130,16 @@ __device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, si
 }
 
 // How a chunk's result leaves the block when the positions take several chunks: plain stores of the
-// partial for a separate merge launch, device-scope stores and the merge in the last block of the kv
-// head (finish_chunk_merge), or tagged words merged by all of the head's chunk blocks (merge_tagged).
-enum { kMergePlain = 0, kMergeSelf = 1, kMergeTagged = 2 };
-
-// The merge of kv head j's nact chunk partials (tagged words of this launch, a.part_t), shared by the
-// head's chunk blocks: block c produces outputs [c*opb, (c+1)*opb) of the head's g*head, opb =
-// ceil(g*head / nact).  T threads per output (a power of two, at most a wavefront) take its chunks s,
-// s+T, ... in order and the T partial merges are combined by a butterfly in a fixed order:
-// (m1, l1, o1) + (m2, l2, o2) = (M, l1 w1 + l2 w2, o1 w1 + o2 w2), w = 2^(m - M), M = max (maxima in
-// base 2), and the output is o / l.  Each word is polled until it carries this launch's tag (the chunk
-// blocks of one head are resident together: they are dispatched in order after the product's blocks,
-// which never wait); a wait that outlasts a.spin_limit polls, or finds status bit 3 set, fills NaN.
-// words of one chunk's record in AttnArgs::part_t: g*head o sums, (m, l) per query head, and a last word
-// that the block writes once its other words are out (the merge waits on those first)
-template <int G, int D>
-constexpr int part_words() {
-  return G * D + 2 * G + 1;
-}
-
-template <int G, int D>
-__device__ void merge_tagged(const AttnArgs &a, int c, int j, int nact, uint32_t tag) {
-  constexpr int NO = G * D;                // outputs of a kv head
-  constexpr int W = part_words<G, D>();    // words per chunk record
-  constexpr int BATCH = 4;                 // chunks per thread whose words are requested together
-  const int opb = (NO + nact - 1) / nact;
-  const int o0 = c * opb;
-  if (o0 >= NO) return;  // uniform: this block has no outputs to merge
-  const unsigned long long *pj = a.part_t + (size_t)j * a.nch * W;
-  // (1) one wavefront polls the chunks' last words until every chunk of the head is out (a light poll:
-  // one word per chunk), the other wavefronts wait at the barrier
-  {
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-      int spins = 0;
-      for (;;) {
-        bool ok = true;
-        for (int cc = tid; cc < nact; cc += 64) ok &= (uint32_t)(tagged_load(pj + (size_t)cc * W + W - 1) >> 32) == tag;
-        if (__all(ok)) break;
-        if (++spins >= a.spin_limit ||
-            ((spins & 63) == 0 && (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 8)))
-          break;  // the word loop below gives up too
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    lds_barrier();
-  }
-  int T = 64;
-  while (T > 1 && T * opb > kThreads) T >>= 1;
-  const int tid = threadIdx.x;
-  const int k = tid / T, s = tid % T;
-  const int o = o0 + k;
-  const bool act = k < opb && o < NO;
-  const int oc = act ? o : NO - 1;  // idle threads read a valid word and discard it
-  const int q = oc / D;
-  float m = -INFINITY, l = 0.f, acc = 0.f;
-  bool give_up = false;
-  int spins = 0;
-  for (int cb = s; cb < nact; cb += BATCH * T) {
-    float mv[BATCH], lv[BATCH], ov[BATCH];
-    for (;;) {
-      bool ok = true;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int cc = min(cb + u * T, nact - 1);
-        const unsigned long long *pc = pj + (size_t)cc * W;
-        const unsigned long long wo = tagged_load(pc + oc), wm = tagged_load(pc + NO + 2 * q),
-                                 wl = tagged_load(pc + NO + 2 * q + 1);
-        const bool hit = (uint32_t)(wo >> 32) == tag && (uint32_t)(wm >> 32) == tag && (uint32_t)(wl >> 32) == tag;
-        ok &= hit;
-        ov[u] = hit ? __uint_as_float((uint32_t)wo) : __builtin_nanf("");
-        mv[u] = hit ? __uint_as_float((uint32_t)wm) : __builtin_nanf("");
-        lv[u] = hit ? __uint_as_float((uint32_t)wl) : __builtin_nanf("");
-      }
-      if (ok || give_up) break;
-      ++spins;
-      if (spins >= a.spin_limit ||
-          ((spins & 63) == 0 && (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 8))) {
-        give_up = true;  // one more pass, then NaN for what is still missing
-        atomicOr(a.status, 8);
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      if (cb + u * T >= nact) break;
-      const float M = fmaxf(m, mv[u]);
-      const float f1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      const float f2 = __builtin_amdgcn_exp2f(mv[u] - M);
-      l = l * f1 + lv[u] * f2;
-      acc = acc * f1 + ov[u] * f2;
-      m = M;
-    }
-  }
-  // the T threads of an output: a butterfly in a fixed order (lanes of one wavefront)
-  for (int off = 1; off < T; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off), a2 = __shfl_xor(acc, off);
-    const float M = fmaxf(m, m2);
-    const float f1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-    l = l * f1 + l2 * f2;
-    acc = acc * f1 + a2 * f2;
-    m = M;
-  }
-  if (act && s == 0) put_out(a, 0, j * NO + o, acc / l);
-}
+// partial for a separate merge launch, or device-scope stores and the merge in the last block of the kv
+// head (finish_chunk_merge).
+enum { kMergePlain = 0, kMergeSelf = 1 };
 
 // A chunk's result for output idx (query head q, number d) of (row b, kv head j) in the merge mode.
 template <int G, int D, int MODE>
 __device__ __forceinline__ void emit_chunk(const AttnArgs &a, int b, int j, int c, size_t slot, int idx, int q, int d,
-                                           float acc, float M, float L, uint32_t tag) {
+                                           float acc, float M, float L) {
   if (a.direct) {
     put_out(a, b, j * G * D + idx, acc / L);
-  } else if (MODE == kMergeTagged) {
-    unsigned long long *pc = a.part_t + (size_t)(j * a.nch + c) * part_words<G, D>();
-    tagged_store(pc + idx, acc, tag);
-    if (d == 0) {
-      tagged_store(pc + G * D + 2 * q, M, tag);
-      tagged_store(pc + G * D + 2 * q + 1, L, tag);
-    }
   } else if (MODE == kMergeSelf) {
     store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
     if (d == 0) {
@@ -266,17 +157,9 @@ __device__ __forceinline__ void emit_chunk(const AttnArgs &a, int b, int j, int 
 
 // after every output of the chunk is emitted: the merge, where this block takes part in it
 template <int G, int D, int MODE>
-__device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, int c, int nact, size_t slot,
-                                             uint32_t tag) {
+__device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, int nact, size_t slot) {
   if (a.direct) return;
   if (MODE == kMergeSelf) finish_chunk_merge<G, D>(a, b, j, nact, slot);
-  if (MODE == kMergeTagged) {
-    // the record's last word after the block's other words were issued
-    lds_barrier();
-    if (threadIdx.x == 0)
-      tagged_store(a.part_t + (size_t)(j * a.nch + c) * part_words<G, D>() + part_words<G, D>() - 1, 0.f, tag);
-    merge_tagged<G, D>(a, c, j, nact, tag);
-  }
 }
 
 // Everything after the loads of k_attn: this thread's slices of the group's query heads from q_s (LDS,
@@ -286,7 +169,7 @@ __device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, in
 template <typename KT, int D, int G, int MODE>
 __device__ __forceinline__ void valu_attend(const AttnArgs &a, int c, int j, int b, int t, int nact,
                                             const float (&q_s)[G][D], const u32x4 (&kraw)[AttnShape<KT, D>::NR],
-                                            const u32x4 (&vraw)[AttnShape<KT, D>::NR], uint32_t tag = 0u) {
+                                            const u32x4 (&vraw)[AttnShape<KT, D>::NR]) {
   using S = AttnShape<KT, D>;
   constexpr int E = S::E, LPR = S::LPR, PPR = S::PPR, NR = S::NR, CHUNK = S::CHUNK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -388,9 +271,9 @@ __device__ __forceinline__ void valu_attend(const AttnArgs &a, int c, int j, int
       acc = fmaf(f, ow, acc);
       L = fmaf(f, lsum, L);
     }
-    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, i, d, acc, M, L, tag);
+    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, i, d, acc, M, L);
   }
-  finish_chunk<G, D, MODE>(a, b, j, c, nact, slot, tag);
+  finish_chunk<G, D, MODE>(a, b, j, nact, slot);
 }
 
 // ------------------------------------------------------------------ matrix-core scores ----
@@ -448,7 +331,7 @@ struct MfmaAttnShape {
 template <int D, int G, int NPW, int NW, int MODE, typename GetK>
 __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int b, int t, int nact, int pw0,
                                             const u32x4 (&qhi)[D / 32], const u32x4 (&qlo)[D / 32], GetK getk,
-                                            const u32x4 (&vr)[NPW / (64 / (D / 8))], uint32_t tag = 0u,
+                                            const u32x4 (&vr)[NPW / (64 / (D / 8))],
                                             const float *vt = nullptr, int vti = -1) {
   using S = MfmaAttnShape<D, G, NPW, NW>;
   constexpr int CHUNK = S::CHUNK, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
@@ -515,7 +398,8 @@ __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int
         }
     }
   }
-  lds_barrier();
+  // the weights are read back by the wave that wrote them (m_s and l_s only after the barrier below)
+  wave_lds_barrier();
 
   // (5) o[q][e] = sum over this lane's positions of w[q] * V[p][8 vl + e]
   float o[G][8];
@@ -568,9 +452,9 @@ __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int
       acc = fmaf(f, ow, acc);
       L = fmaf(f, l_s[w][q], L);
     }
-    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, q, d, acc, M, L, tag);
+    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, q, d, acc, M, L);
   }
-  finish_chunk<G, D, MODE>(a, b, j, c, nact, slot, tag);
+  finish_chunk<G, D, MODE>(a, b, j, nact, slot);
 }
 
 // query fragments: lane l holds head l%16 (zero rows from G on), numbers 32 ks + 8(l/16) .. +8, as

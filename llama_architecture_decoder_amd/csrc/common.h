@@ -136,6 +136,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// the same for LDS data that one wavefront writes and reads itself
+__device__ __forceinline__ void wave_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
 // n (4 or 8) consecutive F32 from a 16-byte aligned address
 template <int n>
@@ -429,9 +435,6 @@ struct AttnArgs {
   int rows_per_group;                    // the product's rows per group (it divides head)
   int dim, kvw;
   int spin_limit;  // polls before a wait for them gives up (status bit 3; the outputs are then NaN)
-  // that launch's chunk partials as tagged words [kv][nch][g*head + 2g + 1] (the o sums, (m, l) per
-  // query head, a last word written after the others), merged by the head's chunk blocks (merge_tagged)
-  unsigned long long *part_t;
   // streamed attention (k_attn_stream; set by its launcher, sk_total = 0 otherwise): the step's chunks
   // in (row, kv head, chunk) order, sk_total of them, row b's first at sk_prefix[b]; sk_blocks blocks
   // take equal runs of them, and segment (b, j)'s partials are those of the blocks its chunks fall in

@@ -28,14 +28,15 @@
 
 namespace lm {
 
-// positions per wavefront of the matrix-core role: 32 (chunks of 128), so a block's registers fit
-// beside the product's and four blocks share a CU
+// positions per wavefront of the matrix-core role: 32 (chunks of 128)
 constexpr int kFusedNpw = 32;
 // Per cache type (measured, batch-1 decode with 4 full-width layers, us per step: 8B shape at
 // positions 7936.., 1.7B shape at 767..):
-//  - the merge: by a separate launch (kMergePlain) or by the chunk blocks themselves (kMergeTagged,
-//    merge_tagged).  bf16 / matrix cores: separate, 507 vs 514-532 us (the in-kernel merge waits for
-//    the head's slowest chunk and its polls slow the others); F32: in-kernel, 290-292 vs 293-296 us.
+//  - the merge: by a separate launch (kMergePlain), by the last chunk block of each kv head to finish
+//    (kMergeSelf, finish_chunk_merge), or by all of the head's chunk blocks, each polling for the
+//    others' partials as tagged words and merging a slice of the outputs.  bf16 / matrix cores:
+//    separate, 505-507 us (last block 529-530, all blocks 514-532: the merge of 64 chunks waits for the
+//    head's slowest one); F32: last block 289.6-289.8, all blocks 291.5-291.8, separate 293-296 us.
 //  - the attention's cache loads before the poll for the queries (early) or after it (the product's
 //    weight stream then has the memory to itself): bf16 early, F32 late.
 //  - product blocks: as many as fit beside the attention's (kProductRoom), that many with the row
@@ -50,7 +51,7 @@ enum { kProductRoom = 0, kProductBalanced = 1, kProductAll = 2 };
 template <typename KT>
 struct FusedPlan {
   static constexpr bool mfma = sizeof(KT) == 2;
-  static constexpr int merge = mfma ? kMergePlain : kMergeTagged;
+  static constexpr int merge = mfma ? kMergePlain : kMergeSelf;
   static constexpr bool early_kv = mfma;
   static constexpr bool late_v = mfma;
   static constexpr int product = mfma ? kProductRoom : kProductAll;
@@ -217,7 +218,7 @@ __device__ __forceinline__ void attn_role_mfma(const AttnArgs &a, int c, int j, 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = kb[gi][ks];
   };
-  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, tag, vt_s, vti);
+  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, vt_s, vti);
 }
 
 // Vector-unit attention role (any cache type), as k_attn.
@@ -259,7 +260,7 @@ __device__ __forceinline__ void attn_role_valu(const AttnArgs &a, int c, int j, 
         vraw[r] = Vec16<KT>::pack(&vt_s[li * E]);
       }
   }
-  valu_attend<KT, D, G, P::merge>(a, c, j, 0, t, nact, q_s, kraw, vraw, tag);
+  valu_attend<KT, D, G, P::merge>(a, c, j, 0, t, nact, q_s, kraw, vraw);
 }
 
 template <typename KT, int D, int G>
@@ -290,8 +291,10 @@ __global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, i
     attn_role_valu<KT, D, G>(a, c, j, nact, tag);
 }
 
-// product blocks: enough that the product streams at full rate, few enough that the product and the
-// attention blocks are resident together (four blocks of this kernel per CU)
+// Product blocks: enough that the product streams at full rate, and as many as fit beside the attention
+// blocks at four blocks per CU.  The matrix-core (bf16, 128-number heads) build needs 134 registers, so
+// three fit and the attention blocks that do not start as product blocks end; capping it at 128
+// registers for four per CU measured slower (507.8 against 505.8 us per 4-layer 8B step).
 constexpr int kFusedResident = 1024;
 constexpr int kFusedMinProduct = 256;
 
@@ -306,8 +309,9 @@ static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, int tmax, const unsigned *
   const int R = 16 / kch >= 8 ? 8 : 16 / kch >= 4 ? 4 : 16 / kch >= 2 ? 2 : 1;  // RowsPerGroup<kch, 1>
   ga.ngroups = (ga.N + R - 1) / R;
   const int na = nact * aa.kv;
-  // the chunk blocks of a kv head wait for each other (the merge): at most one resident round of them
-  // (product blocks never wait, so the attention blocks get every slot once they are done)
+  // attention blocks wait only for the product's blocks, which come first in the grid and never wait;
+  // beyond one resident round of attention blocks (F32 heads of 64 past ~4K positions) the two separate
+  // launches are used
   if (na > kFusedResident) return hipErrorNotSupported;
   // product blocks: the room left beside the attention blocks, the row groups spread evenly (a block
   // with one group more than the others finishes a group's round trip later)
