@@ -557,6 +557,54 @@ __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
   }
 }
 
+// Merge of the streamed kernel's partials when no segment has more than kFewParts of them (long rows
+// over a resident grid: 2-3 each): block = one (row, kv head) segment, each thread OPT of its g*head
+// outputs; every part's (m, l, o) requested before any is used (one memory round trip), then
+// M = max_c m_c, w_c = 2^(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L in part (= position) order.
+// Against the general merge (2048 blocks of 64 outputs at 32 rows x 8 kv heads): no LDS, no barriers.
+constexpr int kFewParts = 8;
+template <int G, int D>
+__global__ __launch_bounds__(kThreads) void k_attn_merge_few(AttnArgs a, int chunk) {
+  constexpr int NO = G * D, OPT = (NO + kThreads - 1) / kThreads;
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int n = a.pos[b] / chunk + 1;
+  const int nb = a.sk_blocks, T = a.sk_total, g = a.sk_prefix[b] + j * n;
+  auto blk = [&](int x) { return (int)(((long)(x + 1) * nb - 1) / T); };
+  const int nparts = blk(g + n - 1) - blk(g) + 1;  // <= kFewParts (checked by the launcher)
+  const size_t slot = ((size_t)b * a.kv + j) * (size_t)a.nch;
+  const float *pml = a.part_ml + slot * (size_t)(G * 2);
+  const float *po = a.part_o + slot * (size_t)NO;
+  float mv[OPT][kFewParts], lv[OPT][kFewParts], ov[OPT][kFewParts];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int idx = min(tid + i * kThreads, NO - 1), q = idx / D;
+#pragma unroll
+    for (int k = 0; k < kFewParts; ++k) {
+      const int cc = min(k, nparts - 1);  // unconditional (clamped): one wait for all of them
+      mv[i][k] = pml[(size_t)cc * G * 2 + 2 * q];
+      lv[i][k] = pml[(size_t)cc * G * 2 + 2 * q + 1];
+      ov[i][k] = po[(size_t)cc * NO + idx];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int idx = tid + i * kThreads;
+    float M = mv[i][0];
+#pragma unroll
+    for (int k = 1; k < kFewParts; ++k)
+      if (k < nparts) M = fmaxf(M, mv[i][k]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kFewParts; ++k)
+      if (k < nparts) {
+        const float w = __builtin_amdgcn_exp2f(mv[i][k] - M);  // maxima are in base 2
+        L = fmaf(w, lv[i][k], L);
+        acc = fmaf(w, ov[i][k], acc);
+      }
+    if (idx < NO) put_out(a, b, j * NO + idx, acc / L);
+  }
+}
+
 template <typename KT, int D, int G>
 constexpr bool use_mfma() {
   return sizeof(KT) == 2 && MfmaAttnShape<D, G, kMfmaNpw>::LDS <= 64 * 1024;
@@ -682,6 +730,20 @@ static hipError_t launch_g(AttnArgs a, int B, int tmax, hipStream_t s) {
       a.sk_blocks = (int)std::min<long>(stream_blocks(), total);
       a.direct = 0;
       launch(k_attn_stream<D, G>, dim3(a.sk_blocks), dim3(kThreads), s, true, false, a);
+      // the most parts a segment has: the blocks its chunks fall in
+      int most = 0;
+      for (int b = 0; b < B; ++b) {
+        const int n = a.pos[b] / schunk + 1;
+        for (int j = 0; j < a.kv; ++j) {
+          const long g = a.sk_prefix[b] + (long)j * n;
+          const long first = ((g + 1) * a.sk_blocks - 1) / total, last = ((g + n) * a.sk_blocks - 1) / total;
+          most = std::max(most, (int)(last - first + 1));
+        }
+      }
+      if (most <= kFewParts) {
+        launch(k_attn_merge_few<G, D>, dim3(a.kv, B), dim3(kThreads), s, false, true, a, schunk);
+        return hipGetLastError();
+      }
       return merge_g<G, D>(a, B, nch_launch, schunk, s);
     }
     if (krows && self) launch(k_attn_mfma<D, G, kMfmaNpw, true, true>, grid, dim3(kThreads), s, true, true, a);
