@@ -28,6 +28,11 @@ constexpr uint32_t kWsMagic = 0x4c4d5357u;  // "LMSW"
 // polls before an attention block of the q/k/v + attention launch stops waiting for its queries (each
 // poll is a memory round trip of about a microsecond: ~0.1 s in all, against ~15 us for the product)
 constexpr int kSpinLimit = 1 << 16;
+// The O product runs inside the q/k/v + attention launch (F32 caches, one row) up to this many weight
+// bytes.  Measured (us per step): SmolLM2-135M shape 633 -> 601, 360M 878 -> 858 (a launch boundary
+// costs more than the in-launch wait for the attention outputs); the 1.7B shape's 16.8 MB gained
+// nothing (290.4 vs 290.6 per 4-layer step: its weight stream competes with the attention's cache reads).
+constexpr size_t kFuseOMaxBytes = 8u << 20;
 
 // Caps on GEMV blocks per projection (blocks walk row groups with a grid stride).  Fewer blocks read
 // the input vector fewer times (each block loads all of it); more blocks keep more loads in flight.
@@ -48,6 +53,11 @@ const Tun &tun() {
   static const Tun t;
   return t;
 }
+// LM head blocks by the bytes of one row: the 8 KB rows of the 8B (bf16) and 1.7B (F32) shapes take
+// tun().lm; shorter rows put fewer bytes in flight per block, so they take more blocks (measured, us per
+// step: SmolLM2-360M's 3.75 KB rows 861 at 384 blocks, 852 at 768, 857 at 1536; SmolLM2-135M's 2.25 KB
+// rows 600 at 384, 587 at 768, 584 at 1536, 581 at 2048)
+int lm_grid_cap(int64_t row_bytes) { return row_bytes >= 8192 ? tun().lm : row_bytes >= 3072 ? 768 : kLmGridMax; }
 
 struct Dims {
   int64_t head, heads, dim, kvw, f, vocab, layers, kv, g, half;
@@ -118,7 +128,7 @@ uint32_t cfg_key(const llama_cfg *c) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, done, epoch, tagged, group_done, rope_cs, rope_sn, x, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
+  size_t status, done, epoch, tagged, group_done, att_t, rope_cs, rope_sn, x, x2, qkv, qrot, attn, m, part_o, part_ml, lm_v, lm_i, xhi, xlo, xhi2, xlo2, part,
       total;
   int nch;    // chunk slots per (row, kv head) of the attention partials
   int nch_f;  // chunk slots of the one-row launch that runs the q/k/v product with the attention
@@ -172,9 +182,11 @@ WsLayout ws_layout(const llama_cfg *c, int32_t max_batch, int32_t max_seq, int32
   L.epoch = take(sizeof(unsigned));
   L.tagged = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));
   L.group_done = take(sizeof(unsigned long long) * (size_t)(d.dim + 2 * d.kvw));  // at most a group per row
+  L.att_t = take(sizeof(unsigned long long) * (size_t)d.dim);  // one row's attention outputs, tagged
   L.rope_cs = take(sizeof(float) * (size_t)max_seq * d.half);
   L.rope_sn = take(sizeof(float) * (size_t)max_seq * d.half);
   L.x = take(sizeof(float) * rows * d.dim);
+  L.x2 = take(sizeof(float) * (size_t)d.dim);  // one row's residual stream after O (O in the fused launch)
   L.qkv = take(sizeof(float) * rows * (d.dim + 2 * d.kvw));
   L.qrot = take(sizeof(float) * (size_t)max_batch * d.dim);
   L.attn = take(sizeof(float) * rows * d.dim);
@@ -378,7 +390,7 @@ int run_lm_head(const Ctx &x, const float *h, int b, float *logits, int32_t *nex
   a.part_i = x.at<int>(x.L.lm_i) + (size_t)b * kLmGridMax;
   a.next = next;
   ProfScope ps(LLAMA_K_LM_HEAD, x.s);
-  return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, tun().lm, x.s));
+  return hip_rc(launch_gemv(x.c->weight_dtype, EPI_ARGMAX, true, a, lm_grid_cap(x.d.dim * x.d.wb), x.s));
 }
 
 // Several token rows with bf16 weights: each projection is one matrix-core product over all rows (the
@@ -721,8 +733,12 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
     return run_step_rows(x, aa, ra, tmax, B, logits, next, want_head);
 
   const int64_t tstride = 4 * d.dim + 2 * d.kvw + d.f;
-  // one token row (contiguous cache, no trace): the q/k/v product and the attention in one launch
+  // one token row (contiguous cache, no trace): the q/k/v product and the attention in one launch, and
+  // with F32 caches the O product too (its output goes to the second residual buffer x2, read by the
+  // gate/up product and the down product's residual, so no block of the launch writes what another reads)
   bool fused = B == 1 && !trace && !x.table && x.L.nch_f > 0;
+  const bool fuse_o = fused && qkv_attention_fuses_o(x.c->kv_dtype) && (size_t)H * H * d.wb <= kFuseOMaxBytes;
+  float *x2 = x.at<float>(x.L.x2);
   for (int l = 0; l < (int)d.layers; ++l) {
     const llama_layer_w &lw = x.w->layers[l];
     aa.kc = ra.kc = layer_cache(x, x.kv->k, l);
@@ -749,7 +765,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.y = qkv + (size_t)b * qkv_stride;
       return a;
     };
-    bool done = false;
+    bool done = false, o_done = false;
     if (fused) {
       GemvArgs a = qkv_args(0);
       a.ra.tagged = x.at<unsigned long long>(x.L.tagged);
@@ -760,11 +776,28 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       af.kvw = KW;
       af.spin_limit = kSpinLimit;
       af.nch = x.L.nch_f;
+      GemvArgs oa = {};
+      if (fuse_o) {
+        af.out_t = x.at<unsigned long long>(x.L.att_t);
+        oa.xt = af.out_t;
+        oa.spin_limit = kSpinLimit;
+        oa.status = x.at<int>(x.L.status);
+        oa.w[0] = lw.wo;
+        oa.rs[0] = 0;
+        oa.rs[1] = oa.rs[2] = oa.rs[3] = H;
+        oa.N = H;
+        oa.K = H;
+        oa.y = x2;
+        oa.res = xs;
+      }
       ProfScope ps(LLAMA_K_QKV_ATTN, x.s);
-      const hipError_t e = launch_qkv_attention(wdt, x.c->kv_dtype, (int)d.head, (int)d.g, a, af, tmax,
-                                                x.at<unsigned>(x.L.epoch), (uint32_t)d.layers, (uint32_t)l + 1u, x.s);
-      if (e == hipSuccess)
+      const hipError_t e = launch_qkv_attention(wdt, x.c->kv_dtype, (int)d.head, (int)d.g, a, af,
+                                                fuse_o ? &oa : nullptr, tmax, x.at<unsigned>(x.L.epoch),
+                                                (uint32_t)d.layers, (uint32_t)l + 1u, x.s);
+      if (e == hipSuccess) {
         done = true;
+        o_done = fuse_o;
+      }
       else if (e == hipErrorNotSupported)
         fused = false;  // nothing was launched: the two launches below, for this and the later layers
       else
@@ -785,7 +818,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       if ((rc = hip_rc(hipMemcpyAsync(tr + qkv_stride, att, sizeof(float) * H, hipMemcpyDeviceToDevice, x.s))))
         return rc;
     }
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B && !o_done; ++b) {
       GemvArgs a = {};
       a.x = att + (size_t)b * H;
       a.w[0] = lw.wo;
@@ -800,9 +833,11 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
     }
     if (tr && (rc = hip_rc(hipMemcpyAsync(tr + qkv_stride + H, xs, sizeof(float) * H, hipMemcpyDeviceToDevice, x.s))))
       return rc;
+    // the residual stream after O: x2 when the fused launch ran O (one row), else x in place
+    float *xm = o_done ? x2 : xs;
     for (int b = 0; b < B; ++b) {
       GemvArgs a = {};
-      a.x = xs + (size_t)b * H;
+      a.x = xm + (size_t)b * H;
       a.gain = lw.ln2;
       a.eps = x.c->eps;
       a.w[0] = lw.w_gate;
@@ -824,7 +859,7 @@ int run_step(const Ctx &x, const int32_t *tokens, const int32_t *pos, int B, int
       a.N = H;
       a.K = F;
       a.y = xs + (size_t)b * H;
-      a.res = xs + (size_t)b * H;
+      a.res = xm + (size_t)b * H;
       ProfScope ps(LLAMA_K_DOWN, x.s);
       if ((rc = hip_rc(launch_gemv(wdt, EPI_RESID, false, a, tun().down, x.s)))) return rc;
     }

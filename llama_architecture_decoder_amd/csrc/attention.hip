@@ -464,11 +464,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_stream(AttnArgs a) {
 // M = max_c m_c, w_c = exp(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L.  The NW waves are NW
 // chunk groups x 64 outputs (wave w takes chunks w, w + NW, ...); their sums are combined in a fixed
 // order.  Every load is issued before the first use: NW * PER chunks in one memory round trip (NW = 16
-// for one long row: 512 chunks took 34 us per layer in 8 rounds with 4 waves, 6.7 us in one with 16).
-template <int G, int D, int NW>
+// for one long row: 512 chunks took 34 us per layer in 8 rounds with 4 waves, 6.7 us in one with 16;
+// one row of 64 chunks: 16 waves of 4 chunks 0.33 us per layer faster than 4 of 16, 1 wave of 64 2.5 us
+// slower).
+template <int G, int D, int NW, int PER>
 __global__ __launch_bounds__(NW * 64) void k_attn_merge(AttnArgs a, int chunk) {
   constexpr int NT = NW * 64;
-  constexpr int PER = NW >= 16 ? 32 : 16;  // partials per thread loaded up front; more in a loop
   constexpr int MLR = (kAttnMaxChunks + NT - 1) / NT;
   const int og = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = a.pos[b];
@@ -658,10 +659,13 @@ static hipError_t merge_g(const AttnArgs &a, int B, int nch_launch, int chunk, h
   // 16 waves only when the merge has fewer blocks than the chip has CUs (one row): at 32 rows (2048
   // blocks of ~125 chunks) the 4-wave blocks were faster (11.8 vs 30.4 us per layer)
   const dim3 mg(G * D / 64, a.kv, B);
-  if (nch_launch > 64 && (long)mg.x * mg.y * mg.z < 256)
-    launch(k_attn_merge<G, D, 16>, mg, dim3(16 * 64), s, false, true, a, chunk);
+  const bool one_round = (long)mg.x * mg.y * mg.z < 256;
+  if (one_round && nch_launch > 64)
+    launch(k_attn_merge<G, D, 16, 32>, mg, dim3(16 * 64), s, false, true, a, chunk);
+  else if (one_round)
+    launch(k_attn_merge<G, D, 16, 4>, mg, dim3(16 * 64), s, false, true, a, chunk);
   else
-    launch(k_attn_merge<G, D, 4>, mg, dim3(kThreads), s, false, true, a, chunk);
+    launch(k_attn_merge<G, D, 4, 16>, mg, dim3(kThreads), s, false, true, a, chunk);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@ namespace lm {
 // One normalised output o of row b at column col (of the row's dim outputs), and, when asked, its
 // operand split for the batched O product (the bits k_split would give: hi = bf16(o) to nearest even,
 // lo = bf16(o - hi))
-__device__ __forceinline__ void put_out(const AttnArgs &a, int b, int col, float v) {
+__device__ __forceinline__ void put_out(const AttnArgs &a, int b, int col, float v, uint32_t tag = 0u) {
   a.out[(size_t)b * a.out_stride + col] = v;
+  if (a.out_t) tagged_store(a.out_t + col, v, tag);
   if (a.ohi) {
     const __bf16 h = (__bf16)v;
     const __bf16 l = (__bf16)(v - (float)h);
@@ -36,7 +37,7 @@ struct AttnShape {
 // M = max_c m_c, w_c = 2^(m_c - M), L = sum_c w_c l_c, o = (sum_c w_c o_c) / L (maxima are base 2),
 // reading the partials with device-scope loads, then clears the count for the next launch.
 template <int G, int D>
-__device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, size_t slot) {
+__device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, size_t slot, uint32_t tag = 0u) {
   constexpr int OPT = (G * D + kThreads - 1) / kThreads;  // outputs per thread
   constexpr int CB = 16;                                    // chunks per batch of loads
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,7 +124,7 @@ __device__ void finish_chunk_merge(const AttnArgs &a, int b, int j, int nact, si
     if (idx < G * D) {
       const int q = idx / D;
       const float L = (red_l[0][q] + red_l[1][q]) + (red_l[2][q] + red_l[3][q]);
-      put_out(a, b, j * G * D + idx, acc[i] / L);
+      put_out(a, b, j * G * D + idx, acc[i] / L, tag);
     }
   }
   if (tid == 0) __hip_atomic_store(&a.done[b * a.kv + j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -137,9 +138,9 @@ enum { kMergePlain = 0, kMergeSelf = 1 };
 // A chunk's result for output idx (query head q, number d) of (row b, kv head j) in the merge mode.
 template <int G, int D, int MODE>
 __device__ __forceinline__ void emit_chunk(const AttnArgs &a, int b, int j, int c, size_t slot, int idx, int q, int d,
-                                           float acc, float M, float L) {
+                                           float acc, float M, float L, uint32_t tag = 0u) {
   if (a.direct) {
-    put_out(a, b, j * G * D + idx, acc / L);
+    put_out(a, b, j * G * D + idx, acc / L, tag);
   } else if (MODE == kMergeSelf) {
     store_dev(&a.part_o[(slot + c) * (size_t)(G * D) + idx], acc);
     if (d == 0) {
@@ -157,9 +158,10 @@ __device__ __forceinline__ void emit_chunk(const AttnArgs &a, int b, int j, int 
 
 // after every output of the chunk is emitted: the merge, where this block takes part in it
 template <int G, int D, int MODE>
-__device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, int nact, size_t slot) {
+__device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, int nact, size_t slot,
+                                             uint32_t tag = 0u) {
   if (a.direct) return;
-  if (MODE == kMergeSelf) finish_chunk_merge<G, D>(a, b, j, nact, slot);
+  if (MODE == kMergeSelf) finish_chunk_merge<G, D>(a, b, j, nact, slot, tag);
 }
 
 // Everything after the loads of k_attn: this thread's slices of the group's query heads from q_s (LDS,
@@ -169,7 +171,7 @@ __device__ __forceinline__ void finish_chunk(const AttnArgs &a, int b, int j, in
 template <typename KT, int D, int G, int MODE>
 __device__ __forceinline__ void valu_attend(const AttnArgs &a, int c, int j, int b, int t, int nact,
                                             const float (&q_s)[G][D], const u32x4 (&kraw)[AttnShape<KT, D>::NR],
-                                            const u32x4 (&vraw)[AttnShape<KT, D>::NR]) {
+                                            const u32x4 (&vraw)[AttnShape<KT, D>::NR], uint32_t tag = 0u) {
   using S = AttnShape<KT, D>;
   constexpr int E = S::E, LPR = S::LPR, PPR = S::PPR, NR = S::NR, CHUNK = S::CHUNK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -271,9 +273,9 @@ __device__ __forceinline__ void valu_attend(const AttnArgs &a, int c, int j, int
       acc = fmaf(f, ow, acc);
       L = fmaf(f, lsum, L);
     }
-    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, i, d, acc, M, L);
+    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, i, d, acc, M, L, tag);
   }
-  finish_chunk<G, D, MODE>(a, b, j, nact, slot);
+  finish_chunk<G, D, MODE>(a, b, j, nact, slot, tag);
 }
 
 // ------------------------------------------------------------------ matrix-core scores ----
@@ -332,7 +334,7 @@ template <int D, int G, int NPW, int NW, int MODE, typename GetK>
 __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int b, int t, int nact, int pw0,
                                             const u32x4 (&qhi)[D / 32], const u32x4 (&qlo)[D / 32], GetK getk,
                                             const u32x4 (&vr)[NPW / (64 / (D / 8))],
-                                            const float *vt = nullptr, int vti = -1) {
+                                            const float *vt = nullptr, int vti = -1, uint32_t tag = 0u) {
   using S = MfmaAttnShape<D, G, NPW, NW>;
   constexpr int CHUNK = S::CHUNK, NGI = S::NGI, KS = S::KS, LPR = S::LPR, PPI = S::PPI, NV = S::NV;
   constexpr int GP = S::GP, NG = S::NG;
@@ -452,9 +454,9 @@ __device__ __forceinline__ void mfma_attend(const AttnArgs &a, int c, int j, int
       acc = fmaf(f, ow, acc);
       L = fmaf(f, l_s[w][q], L);
     }
-    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, q, d, acc, M, L);
+    emit_chunk<G, D, MODE>(a, b, j, c, slot, idx, q, d, acc, M, L, tag);
   }
-  finish_chunk<G, D, MODE>(a, b, j, nact, slot);
+  finish_chunk<G, D, MODE>(a, b, j, nact, slot, tag);
 }
 
 // query fragments: lane l holds head l%16 (zero rows from G on), numbers 32 ks + 8(l/16) .. +8, as

@@ -354,6 +354,12 @@ struct GemvArgs {
   int *part_i;
   int32_t *next;       // nullable: argmax written by a one-block reduce
   RopeAppend ra;       // EPI_ROPE
+  // nullable: the input as tagged words [K] written by another role of the same launch (the attention
+  // outputs, for the O product in the launch that runs the q/k/v product with the attention); a wait
+  // past spin_limit polls gives up with NaN inputs and status bit 3
+  const unsigned long long *xt;
+  int spin_limit;
+  int *status;
 };
 
 // several token rows at once (matrix cores): operands split into bf16 hi/lo by k_split
@@ -435,6 +441,8 @@ struct AttnArgs {
   int rows_per_group;                    // the product's rows per group (it divides head)
   int dim, kvw;
   int spin_limit;  // polls before a wait for them gives up (status bit 3; the outputs are then NaN)
+  // nullable (one token row): the outputs also as tagged words [dim], for an O product in the same launch
+  unsigned long long *out_t;
   // streamed attention (k_attn_stream; set by its launcher, sk_total = 0 otherwise): the step's chunks
   // in (row, kv head, chunk) order, sk_total of them, row b's first at sk_prefix[b]; sk_blocks blocks
   // take equal runs of them, and segment (b, j)'s partials are those of the blocks its chunks fall in
@@ -519,7 +527,11 @@ hipError_t launch_attention_merge(int head, int g, const AttnArgs &a, int B, int
 // Each launch's tag is epoch[0] * tag_mul + tag_add (the step counter times the layers, plus the layer
 // + 1).  Returns hipErrorNotSupported, having launched nothing, for shapes without an instantiation.
 hipError_t launch_qkv_attention(int wdtype, int kvdtype, int head, int g, const GemvArgs &ga, const AttnArgs &aa,
-                                int tmax, const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add, hipStream_t s);
+                                const GemvArgs *oa, int tmax, const unsigned *epoch, uint32_t tag_mul,
+                                uint32_t tag_add, hipStream_t s);
+// whether that launch can also run the O product (oa non-null): its attention outputs are final in the
+// launch (merged there), so the O blocks can poll them as tagged words
+int qkv_attention_fuses_o(int kvdtype);
 int qkv_attention_chunk(int kvdtype, int head, int g);  // positions per attention block of that launch (0: none)
 int attention_supported(int head, int g);
 int attention_paged_supported(int kvdtype, int head, int g);  // the matrix-core kernel (whole pages per wave)

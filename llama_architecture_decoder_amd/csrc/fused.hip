@@ -218,7 +218,7 @@ __device__ __forceinline__ void attn_role_mfma(const AttnArgs &a, int c, int j, 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = kb[gi][ks];
   };
-  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, vt_s, vti);
+  mfma_attend<D, G, NPW, NW, P::merge>(a, c, j, 0, t, nact, pw0, qhi, qlo, getk, vr, vt_s, vti, tag);
 }
 
 // Vector-unit attention role (any cache type), as k_attn.
@@ -260,7 +260,7 @@ __device__ __forceinline__ void attn_role_valu(const AttnArgs &a, int c, int j, 
         vraw[r] = Vec16<KT>::pack(&vt_s[li * E]);
       }
   }
-  valu_attend<KT, D, G, P::merge>(a, c, j, 0, t, nact, q_s, kraw, vraw);
+  valu_attend<KT, D, G, P::merge>(a, c, j, 0, t, nact, q_s, kraw, vraw, tag);
 }
 
 template <typename KT, int D, int G>
@@ -276,11 +276,18 @@ constexpr int fused_chunk() {
 }
 
 template <typename WT, int KCH, typename KT, int D, int G>
-__global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, int nq, int nact,
+__global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, GemvArgs o, int nq, int nact, int na,
                                                        const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add) {
   const uint32_t tag = epoch[0] * tag_mul + tag_add;
   if ((int)blockIdx.x < nq) {
     gemv_body<WT, KCH, EPI_ROPE, true>(g, blockIdx.x, nq, tag);
+    return;
+  }
+  if ((int)blockIdx.x >= nq + na) {
+    // the O product + residual (F32 plan): its weights stream while the attention finishes; its input
+    // is the attention's outputs as tagged words (K = dim, as the q/k/v product's, so the same KCH)
+    const int ob = blockIdx.x - nq - na;
+    gemv_body<WT, KCH, EPI_RESID, false, true>(o, ob, gridDim.x - nq - na, tag);
     return;
   }
   const int ab = blockIdx.x - nq;
@@ -299,8 +306,8 @@ constexpr int kFusedResident = 1024;
 constexpr int kFusedMinProduct = 256;
 
 template <typename T, int D, int G>
-static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, int tmax, const unsigned *epoch, uint32_t tag_mul,
-                            uint32_t tag_add, hipStream_t s) {
+static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, const GemvArgs *oa, int tmax, const unsigned *epoch,
+                            uint32_t tag_mul, uint32_t tag_add, hipStream_t s) {
   constexpr int chunk = fused_chunk<T, D, G>();
   const int nact = tmax / chunk + 1;
   if (nact > aa.nch || nact > kAttnMaxChunks) return hipErrorNotSupported;
@@ -331,15 +338,26 @@ static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, int tmax, const unsigned *
   }
   aa.direct = nact == 1;
   const bool merge_launch = !aa.direct && P::merge == kMergePlain;
-  const dim3 grid(nq + na);
+  // the O product in the same launch: only where the attention's outputs are final in this launch
+  GemvArgs go = {};
+  int no = 0;
+  if (oa) {
+    if (merge_launch || !aa.out_t || oa->K != ga.K || !oa->xt) return hipErrorNotSupported;
+    go = *oa;
+    go.ngroups = (go.N + R - 1) / R;  // K = dim: the q/k/v product's rows per group
+    no = go.ngroups;
+  } else {
+    aa.out_t = nullptr;
+  }
+  const dim3 grid(nq + na + no);
   switch (kch) {
     case 1:
-      launch(k_qkv_attn<T, 1, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, nq, nact, epoch,
-             tag_mul, tag_add);
+      launch(k_qkv_attn<T, 1, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, go, nq, nact, na,
+             epoch, tag_mul, tag_add);
       break;
     case 2:
-      launch(k_qkv_attn<T, 2, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, nq, nact, epoch,
-             tag_mul, tag_add);
+      launch(k_qkv_attn<T, 2, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, go, nq, nact, na,
+             epoch, tag_mul, tag_add);
       break;
     default:
       return hipErrorNotSupported;
@@ -350,28 +368,31 @@ static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, int tmax, const unsigned *
 }
 
 template <typename T, int D>
-static hipError_t launch_d(int g, const GemvArgs &ga, const AttnArgs &aa, int tmax, const unsigned *epoch,
-                           uint32_t tag_mul, uint32_t tag_add, hipStream_t s) {
+static hipError_t launch_d(int g, const GemvArgs &ga, const AttnArgs &aa, const GemvArgs *oa, int tmax,
+                           const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add, hipStream_t s) {
   switch (g) {
-    case 1: return launch_dg<T, D, 1>(ga, aa, tmax, epoch, tag_mul, tag_add, s);
-    case 3: return launch_dg<T, D, 3>(ga, aa, tmax, epoch, tag_mul, tag_add, s);
-    case 4: return launch_dg<T, D, 4>(ga, aa, tmax, epoch, tag_mul, tag_add, s);
+    case 1: return launch_dg<T, D, 1>(ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
+    case 3: return launch_dg<T, D, 3>(ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
+    case 4: return launch_dg<T, D, 4>(ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
   }
   return hipErrorNotSupported;
 }
 
 hipError_t launch_qkv_attention(int wdtype, int kvdtype, int head, int g, const GemvArgs &ga, const AttnArgs &aa,
-                                int tmax, const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add, hipStream_t s) {
+                                const GemvArgs *oa, int tmax, const unsigned *epoch, uint32_t tag_mul,
+                                uint32_t tag_add, hipStream_t s) {
   if (wdtype != kvdtype || !ga.ra.tagged || !aa.tagged || ga.ra.table || aa.table) return hipErrorNotSupported;
   if (wdtype == LLAMA_BF16) {
-    if (head == 64) return launch_d<bf16_t, 64>(g, ga, aa, tmax, epoch, tag_mul, tag_add, s);
-    if (head == 128) return launch_d<bf16_t, 128>(g, ga, aa, tmax, epoch, tag_mul, tag_add, s);
+    if (head == 64) return launch_d<bf16_t, 64>(g, ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
+    if (head == 128) return launch_d<bf16_t, 128>(g, ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
   } else {
-    if (head == 64) return launch_d<float, 64>(g, ga, aa, tmax, epoch, tag_mul, tag_add, s);
-    if (head == 128) return launch_d<float, 128>(g, ga, aa, tmax, epoch, tag_mul, tag_add, s);
+    if (head == 64) return launch_d<float, 64>(g, ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
+    if (head == 128) return launch_d<float, 128>(g, ga, aa, oa, tmax, epoch, tag_mul, tag_add, s);
   }
   return hipErrorNotSupported;
 }
+
+int qkv_attention_fuses_o(int kvdtype) { return FusedPlan<float>::merge != kMergePlain && kvdtype == LLAMA_F32; }
 
 int qkv_attention_chunk(int kvdtype, int head, int g) {
   if (g != 1 && g != 3 && g != 4) return 0;

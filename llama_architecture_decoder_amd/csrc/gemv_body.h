@@ -62,6 +62,53 @@ __device__ __forceinline__ void wave_transpose_sum<1>(float (&v)[1], int lane) {
   v[0] = wave_sum(v[0]);
 }
 
+// The input slice of this thread (chunks j*256 + tid, E numbers each) from tagged words a.xt written by
+// another role of the same launch, polled until every word carries this launch's tag.  A wait past
+// spin_limit polls (at once when status bit 3 is already set) gives up: the missing inputs are NaN and
+// bit 3 is set.
+template <int KCH, int E>
+__device__ void poll_tagged_input(const GemvArgs &a, float (&xr)[KCH][E], int nchunk, uint32_t tag) {
+  __shared__ int ok_s[kThreads / 64];
+  __shared__ int stop_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool give_up = false;
+  for (int it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int ci = min(j * kThreads + tid, nchunk - 1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long w = tagged_load(a.xt + (size_t)ci * E + e);
+        const bool hit = (uint32_t)(w >> 32) == tag;
+        if (hit)
+          xr[j][e] = __uint_as_float((uint32_t)w);
+        else if (give_up)
+          xr[j][e] = __builtin_nanf("");
+        ok &= hit;
+      }
+    }
+    const int wave_ok = __all(ok);
+    if (lane == 0) ok_s[wave] = wave_ok;
+    if (tid == 0)
+      stop_s = it >= a.spin_limit ||
+               (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 8) != 0;
+    lds_barrier();
+    int all = 1;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) all &= ok_s[w];
+    const bool stop = stop_s != 0;
+    lds_barrier();  // ok_s and stop_s are read by every wave before they are written again
+    if (all) return;
+    if (give_up) {
+      if (tid == 0) atomicOr(a.status, 8);
+      return;
+    }
+    give_up = stop;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 template <typename WT>
 __device__ __forceinline__ const WT *row_ptr(const GemvArgs &a, int r) {
   int blk = (r >= a.rs[1]) + (r >= a.rs[2]);
@@ -69,8 +116,10 @@ __device__ __forceinline__ const WT *row_ptr(const GemvArgs &a, int r) {
 }
 
 // One block's share of a product: row groups bid, bid + nblk, ...  `tag` labels the tagged copies the
-// q/k/v epilogue writes when a.ra.tagged is set (a launch that also runs the attention).
-template <typename WT, int KCH, int EPI, bool NORM>
+// q/k/v epilogue writes when a.ra.tagged is set (a launch that also runs the attention), and, with XT,
+// the tagged input words this launch's other role writes (a.xt): the first group's weights are then
+// requested before the wait for the input.
+template <typename WT, int KCH, int EPI, bool NORM, bool XT = false>
 __device__ __forceinline__ void gemv_body(const GemvArgs &a, int bid, int nblk, uint32_t tag) {
   constexpr int E = Vec16<WT>::E;
   constexpr int PAIRS = (EPI == EPI_SWIGLU) ? 2 : 1;
@@ -98,9 +147,10 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int bid, int nblk, 
 
   // ---- the input slice of this thread: chunks j*256 + tid (a chunk past K reads the last chunk and is
   // zeroed)
+  static_assert(!XT || !NORM, "a tagged input is not normalised");
   float xr[KCH][E];
 #pragma unroll
-  for (int j = 0; j < KCH; ++j) {
+  for (int j = 0; j < KCH && !XT; ++j) {
     const int ci = min(j * kThreads + tid, nchunk - 1);
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
@@ -144,6 +194,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int bid, int nblk, 
   u32x4 wv[NV][KCH];
   int grp = bid;
   load_group(min(grp, a.ngroups - 1), wv);  // the launch has at most one block per group
+  if (XT) poll_tagged_input<KCH, E>(a, xr, nchunk, tag);
 #pragma unroll
   for (int j = 0; j < KCH; ++j)
     if (j * kThreads + tid >= nchunk)
