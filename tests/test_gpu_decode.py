@@ -234,6 +234,41 @@ def test_token_out_of_range_sets_status():
     assert dec.status() == 0
 
 
+def _set_status(dec, value):
+    """Write the workspace's status word from the host (it is the first word of the workspace)."""
+    base = dec.ws.mem.data_ptr()
+    off = (-base) % 256
+    dec.ws.mem[off:off + 4].copy_(torch.tensor(np.array([value], dtype=np.int32).view(np.uint8)))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,fill", [("smollm2_135m", 300), ("smollm2_1_7b", 600), ("llama31_8b", 1000)])
+def test_wait_give_up_ends_the_step(name, fill):
+    """A device-side wait that gives up (status bit 3, forced here from the host before the step: with the
+    bit set every wait of the launch that runs the q/k/v product with the attention ends at its first
+    unsuccessful poll) still lets every launch of the step finish; llama_status reports LLAMA_E_WAIT once
+    and clears it, and the same step run again equals the oracle.  Covers the query wait, the in-launch
+    merge (F32 caches) and the O role's input wait (SmolLM2-135M shape)."""
+    cfg = configs.truncated(configs.get(name), 2)
+    lm = _lm()
+    om, dec = _pair(cfg, fill + 8)
+    fill_random(cfg, om, dec, [0], fill)
+    tok = int(synth.tokens(cfg, f"first/{fill}", 1)[0])
+    logits = torch.empty((1, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    _set_status(dec, 8)
+    dec.decode(_dev_tok(tok), [fill], logits, nxt)
+    torch.cuda.synchronize()
+    assert 0 <= int(nxt.item()) < cfg.vocab
+    assert dec.status() == lm.E_WAIT
+    assert dec.status() == 0  # cleared by the read
+    r, ref, gid, got = _step(cfg, om, dec, tok, fill)  # the same position again: it rewrites slot fill
+    check_logits(cfg, got, ref, "after a wait that gave up")
+    check_argmax(cfg, gid, ref, "after a wait that gave up")
+    assert dec.status() == 0
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["smollm2_135m", "llama31_8b"])
 def test_lm_head_argmax(name):
