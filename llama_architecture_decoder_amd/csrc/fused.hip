@@ -275,19 +275,11 @@ constexpr int fused_chunk() {
     return AttnShape<KT, D>::CHUNK;
 }
 
+// the product and attention roles (blocks [0, nq) and [nq, nq + nact * kv))
 template <typename WT, int KCH, typename KT, int D, int G>
-__global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, GemvArgs o, int nq, int nact, int na,
-                                                       const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add) {
-  const uint32_t tag = epoch[0] * tag_mul + tag_add;
+__device__ __forceinline__ void qkv_attn_roles(const GemvArgs &g, const AttnArgs &a, int nq, int nact, uint32_t tag) {
   if ((int)blockIdx.x < nq) {
     gemv_body<WT, KCH, EPI_ROPE, true>(g, blockIdx.x, nq, tag);
-    return;
-  }
-  if ((int)blockIdx.x >= nq + na) {
-    // the O product + residual (F32 plan): its weights stream while the attention finishes; its input
-    // is the attention's outputs as tagged words (K = dim, as the q/k/v product's, so the same KCH)
-    const int ob = blockIdx.x - nq - na;
-    gemv_body<WT, KCH, EPI_RESID, false, true>(o, ob, gridDim.x - nq - na, tag);
     return;
   }
   const int ab = blockIdx.x - nq;
@@ -298,12 +290,37 @@ __global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, G
     attn_role_valu<KT, D, G>(a, c, j, nact, tag);
 }
 
+template <typename WT, int KCH, typename KT, int D, int G>
+__global__ __launch_bounds__(kThreads) void k_qkv_attn(GemvArgs g, AttnArgs a, int nq, int nact, const unsigned *epoch,
+                                                       uint32_t tag_mul, uint32_t tag_add) {
+  qkv_attn_roles<WT, KCH, KT, D, G>(g, a, nq, nact, epoch[0] * tag_mul + tag_add);
+}
+
+// The same with the O product + residual as a third role (blocks from nq + na on; F32 plan): its weights
+// stream while the attention finishes, and its input is the attention's outputs as tagged words (K = dim,
+// as the q/k/v product's, so the same KCH).  A separate kernel, so that the launches without it keep the
+// smaller argument block (measured: 4 us per step at the 1.7B shape with the O arguments always passed).
+template <typename WT, int KCH, typename KT, int D, int G>
+__global__ __launch_bounds__(kThreads) void k_qkv_attn_o(GemvArgs g, AttnArgs a, GemvArgs o, int nq, int nact, int na,
+                                                         const unsigned *epoch, uint32_t tag_mul, uint32_t tag_add) {
+  const uint32_t tag = epoch[0] * tag_mul + tag_add;
+  if ((int)blockIdx.x >= nq + na) {
+    gemv_body<WT, KCH, EPI_RESID, false, true>(o, blockIdx.x - nq - na, gridDim.x - nq - na, tag);
+    return;
+  }
+  qkv_attn_roles<WT, KCH, KT, D, G>(g, a, nq, nact, tag);
+}
+
 // Product blocks: enough that the product streams at full rate, and as many as fit beside the attention
 // blocks at four blocks per CU.  The matrix-core (bf16, 128-number heads) build needs 134 registers, so
 // three fit and the attention blocks that do not start as product blocks end; capping it at 128
 // registers for four per CU measured slower (507.8 against 505.8 us per 4-layer 8B step).
 constexpr int kFusedResident = 1024;
 constexpr int kFusedMinProduct = 256;
+// Product blocks of the matrix-core build (three blocks per CU fit, 768 on the chip): measured at the 8B
+// shape's 768 row groups, us per 4-layer step: 256 blocks 512.5, 384 505.8, 512 505.8-506.3, 576 505.3,
+// 640 502.8-504.0, 704 505.0, 768 503.4-505.3
+constexpr int kFusedProductMfma = 640;
 
 template <typename T, int D, int G>
 static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, const GemvArgs *oa, int tmax, const unsigned *epoch,
@@ -320,15 +337,16 @@ static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, const GemvArgs *oa, int tm
   // beyond one resident round of attention blocks (F32 heads of 64 past ~4K positions) the two separate
   // launches are used
   if (na > kFusedResident) return hipErrorNotSupported;
-  // product blocks: the room left beside the attention blocks, the row groups spread evenly (a block
-  // with one group more than the others finishes a group's round trip later)
+  // product blocks: one per row group (F32), or, matrix-core build, kFusedProductMfma (measured), or the
+  // room left beside the attention blocks, or that many with the row groups spread evenly (a block with
+  // one group more than the others finishes a group's round trip later)
   int room = kFusedResident - na;
   if (room < kFusedMinProduct) room = kFusedMinProduct;
   const int per = (ga.ngroups + room - 1) / room;
   using P = FusedPlan<T>;
   const int nq = P::product == kProductAll        ? ga.ngroups
                  : P::product == kProductBalanced ? (ga.ngroups + per - 1) / per
-                                                  : std::min(room, ga.ngroups);
+                                                  : std::min(P::mfma ? kFusedProductMfma : room, ga.ngroups);
   if (P::group_words) {
     if (!ga.ra.group_done || D % R) return hipErrorNotSupported;
     aa.group_done = ga.ra.group_done;
@@ -350,17 +368,26 @@ static hipError_t launch_dg(GemvArgs ga, AttnArgs aa, const GemvArgs *oa, int tm
     aa.out_t = nullptr;
   }
   const dim3 grid(nq + na + no);
-  switch (kch) {
-    case 1:
-      launch(k_qkv_attn<T, 1, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, go, nq, nact, na,
-             epoch, tag_mul, tag_add);
-      break;
-    case 2:
-      launch(k_qkv_attn<T, 2, T, D, G>, grid, dim3(kThreads), s, true, !merge_launch, ga, aa, go, nq, nact, na,
-             epoch, tag_mul, tag_add);
-      break;
-    default:
-      return hipErrorNotSupported;
+  const bool last = !merge_launch;
+  if (no > 0) {
+    if constexpr (P::mfma) {
+      return hipErrorNotSupported;  // the matrix-core plan merges in a separate launch
+    } else {
+      if (kch == 1)
+        launch(k_qkv_attn_o<T, 1, T, D, G>, grid, dim3(kThreads), s, true, last, ga, aa, go, nq, nact, na, epoch,
+               tag_mul, tag_add);
+      else if (kch == 2)
+        launch(k_qkv_attn_o<T, 2, T, D, G>, grid, dim3(kThreads), s, true, last, ga, aa, go, nq, nact, na, epoch,
+               tag_mul, tag_add);
+      else
+        return hipErrorNotSupported;
+    }
+  } else if (kch == 1) {
+    launch(k_qkv_attn<T, 1, T, D, G>, grid, dim3(kThreads), s, true, last, ga, aa, nq, nact, epoch, tag_mul, tag_add);
+  } else if (kch == 2) {
+    launch(k_qkv_attn<T, 2, T, D, G>, grid, dim3(kThreads), s, true, last, ga, aa, nq, nact, epoch, tag_mul, tag_add);
+  } else {
+    return hipErrorNotSupported;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge_launch) return e;
