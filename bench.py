@@ -70,6 +70,17 @@ def kernel_bytes(cfg, cls, t=None):
     raise KeyError(cls)
 
 
+def class_bytes(cfg, name, t, prof):
+    """Algorithmic bytes of one launch of a profiled kernel class; the q/k/v + attention launch also carries
+    the O product's bytes where the step launched no separate O product (small F32 shapes)."""
+    if name == "embed":
+        return None
+    b = kernel_bytes(cfg, name, t)
+    if name == "qkv_attention" and prof.get("o_proj", (0, 0.0))[0] == 0:
+        b += kernel_bytes(cfg, "o_proj", t)
+    return b
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_hbm_traffic.json")
 
 
@@ -341,7 +352,7 @@ def time_secondary(args, lm, synth, configs, c3=None):
     for name, (n, kms) in prof3.items():
         if n:
             per = kms / n
-            kb = kernel_bytes(c3, name, mean3) if name != "embed" else None
+            kb = class_bytes(c3, name, mean3, prof3)
             k3[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(kms / ksum3, 4),
                         "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
     res3 = {"workload": f"{c3.name}-shaped decode, batch 1, F32, {c3.prompt_len}-token prompt "
@@ -649,7 +660,7 @@ def main():
         if n == 0:
             continue
         per = ms / n
-        kb = kernel_bytes(cfg, name, int(mean_t)) if name != "embed" else None
+        kb = class_bytes(cfg, name, int(mean_t), prof)
         kernels[name] = {"launches": n, "avg_us": round(per * 1e3, 3), "share": round(ms / ksum, 4),
                          "GBps": round(kb / (per * 1e-3) / 1e9, 1) if kb else None}
     dom = "gate_up"
