@@ -568,8 +568,10 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     sa.ldx = K;
     return hip_rc(launch_split(wdt, gain != nullptr, sa, mpad, x.s));
   };
+  // nn: for a residual product, the next product's RMSNorm gain (the reduce of a K-sliced product then
+  // writes that product's operands itself; nn->done says so)
   auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
-                  int ldy, const float *res, bool mlp_in, int product) {
+                  int ldy, const float *res, bool mlp_in, int product, bool first, NormNext *nn = nullptr) {
     GemmArgs ga = {};
     ga.lo = (kPrefillLo >> product) & 1;
     ga.xhi = mlp_in ? mhi : xhi;  // the down product reads the operands the gate/up product wrote
@@ -595,8 +597,21 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     ga.res = res;
     ga.ldres = ldy;
     ga.part = x.at<float>(x.L.part);  // short chunks split K (sized for every chunk up to max_prefill)
-    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true, mlp_in));  // the down product opens its scope
+    // `first`: no operand split before it in its timing scope (the down product, or a product whose operands
+    // the previous reduce wrote)
+    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true, first, nn));
   };
+  auto norm_next = [&](const void *gain) {
+    NormNext nn = {};
+    nn.gain = gain;
+    nn.gdtype = wdt;
+    nn.eps = x.c->eps;
+    nn.xhi = xhi;
+    nn.xlo = xlo;
+    nn.ldo = H;
+    return nn;
+  };
+  bool x_split = false;  // the operands of rmsnorm(x, ln1) of the next layer are already written
   PrefillArgs pa = {};
   pa.qkv = qkv;
   pa.qkv_stride = qkv_stride;
@@ -628,9 +643,9 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     const llama_layer_w &lw = x.w->layers[l];
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
-      if ((rc = split(xs, lw.ln1, H))) return rc;
+      if (!x_split && (rc = split(xs, lw.ln1, H))) return rc;
       if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, false,
-                     kProdQkv)))
+                     kProdQkv, x_split)))
         return rc;
     }
     pa.kc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->k, l));
@@ -643,18 +658,25 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_O, x.s);
       if ((rc = split(att, nullptr, H))) return rc;
-      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, false, kProdO))) return rc;
+      NormNext nn = norm_next(lw.ln2);
+      if ((rc = gemm(EPI_RESID, lw.wo, lw.wo, lw.wo, H, H, H, H, xs, H, xs, false, kProdO, false, &nn))) return rc;
+      x_split = nn.done;
     }
     {
       ProfScope ps(LLAMA_K_GATE_UP, x.s);
-      if ((rc = split(xs, lw.ln2, H))) return rc;
+      if (!x_split && (rc = split(xs, lw.ln2, H))) return rc;
       // silu(gate) * up goes straight to the down product's operands (mhi / mlo), never to F32
-      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, nullptr, F, nullptr, false, kProdGateUp)))
+      if ((rc = gemm(EPI_SWIGLU, lw.w_gate, lw.w_up, lw.w_up, F, F, F, H, nullptr, F, nullptr, false, kProdGateUp,
+                     x_split)))
         return rc;
     }
     {
       ProfScope ps(LLAMA_K_DOWN, x.s);
-      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true, kProdDown))) return rc;
+      NormNext nn = norm_next(l + 1 < (int)d.layers ? x.w->layers[l + 1].ln1 : nullptr);
+      if ((rc = gemm(EPI_RESID, lw.w_down, lw.w_down, lw.w_down, H, H, H, F, xs, H, xs, true, kProdDown, true,
+                     l + 1 < (int)d.layers ? &nn : nullptr)))
+        return rc;
+      x_split = l + 1 < (int)d.layers && nn.done;
     }
   }
   if (!logits && !next) return LLAMA_OK;

@@ -560,8 +560,20 @@ int gemm_tiled_rows(int M);
 // the partial-sum floats they need in GemmArgs::part (0 for one slice)
 int gemm_tiled_kslices(int M, int N, int K, bool swiglu);
 size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu);
+// For a residual product (y == res) that runs in K slices: the reduce also normalises the updated rows
+// (RMSNorm with `gain`, of type gdtype) and writes them as the next product's bf16 hi/lo operands
+// (k_rows_reduce_norm); `done` reports whether it did (else the caller splits them itself)
+struct NormNext {
+  const void *gain;
+  int gdtype;
+  float eps;
+  bf16_t *xhi, *xlo;
+  int ldo;
+  bool done;
+};
 // first: the product's launch starts the profiling scope (no operand split launched before it)
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last, bool first = false);
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last, bool first = false,
+                             NormNext *nn = nullptr);
 hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 // argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]

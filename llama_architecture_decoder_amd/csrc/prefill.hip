@@ -536,12 +536,34 @@ size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu) {
   return ks > 1 ? (size_t)ks * M * (swiglu ? 2 * (size_t)N : (size_t)N) : 0;
 }
 
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last, bool first) {
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last, bool first, NormNext *nn) {
   if (a0.K % kTK != 0 || a0.M <= 0) return hipErrorInvalidValue;
   GemmArgs a = a0;
+  if (nn) nn->done = false;
+  // the K slices' reduce: plain, or (residual in place) with the RMSNorm + operand split of the next product
+  auto reduce = [&](auto epi_c, int ks) {
+    constexpr int E = decltype(epi_c)::value;
+    if (E == EPI_RESID && nn && a.y == a.res && a.ldy == a.ldres && a.N % 4 == 0) {
+      RowsNormArgs r = {};
+      r.part = a.part;
+      r.S = ks;
+      r.M = a.M;
+      r.N = a.N;
+      r.x = a.y;
+      r.ldx = a.ldy;
+      r.gain = nn->gain;
+      r.eps = nn->eps;
+      r.xhi = nn->xhi;
+      r.xlo = nn->xlo;
+      r.ldo = nn->ldo;
+      nn->done = launch_rows_reduce_norm(nn->gdtype, r, s, last) == hipSuccess;
+      return;
+    }
+    const dim3 rg((a.N / 2 + kThreads - 1) / kThreads, a.M);
+    launch(k_tiled_reduce<E>, rg, dim3(kThreads), s, false, last, a, ks);
+  };
   const int mt = (a.M + kTM - 1) / kTM;
   const bool sw = epi == EPI_SWIGLU;
-  const dim3 rg((a.N / 2 + kThreads - 1) / kThreads, a.M);
   if (use_big(a.M, a.N, a.K, sw)) {
     BigPlan p = big_plan(a.M, a.N, a.K, sw);
     if (!a.part) p.kslices = 1;
@@ -554,7 +576,7 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
         launch(k_gemm_big<E, kBWaves, true>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
       else
         launch(k_gemm_big<E, kBWaves, false>, g, dim3(kBWaves * 64), s, first, last && ks == 1, a, p);
-      if (ks > 1) launch(k_tiled_reduce<E>, rg, dim3(kThreads), s, false, last, a, ks);
+      if (ks > 1) reduce(epi_c, ks);
     };
     switch (epi) {
       case EPI_STORE: big(std::integral_constant<int, EPI_STORE>{}); break;
@@ -573,7 +595,7 @@ hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, boo
       launch(k_gemm_tiled<E, true>, g, dim3(kThreads), s, first, last && ks == 1, a);
     else
       launch(k_gemm_tiled<E, false>, g, dim3(kThreads), s, first, last && ks == 1, a);
-    if (ks > 1) launch(k_tiled_reduce<E>, rg, dim3(kThreads), s, false, last, a, ks);
+    if (ks > 1) reduce(epi_c, ks);
   };
   switch (epi) {
     case EPI_STORE: tiled(std::integral_constant<int, EPI_STORE>{}); break;
