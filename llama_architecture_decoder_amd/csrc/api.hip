@@ -571,7 +571,8 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
   // nn: for a residual product, the next product's RMSNorm gain (the reduce of a K-sliced product then
   // writes that product's operands itself; nn->done says so)
   auto gemm = [&](GemvEpi epi, const void *w0, const void *w1, const void *w2, int r1, int r2, int N, int K, float *y,
-                  int ldy, const float *res, bool mlp_in, int product, bool first, NormNext *nn = nullptr) {
+                  int ldy, const float *res, bool mlp_in, int product, bool first, NormNext *nn = nullptr,
+                  int *defer_ks = nullptr) {
     GemmArgs ga = {};
     ga.lo = (kPrefillLo >> product) & 1;
     ga.xhi = mlp_in ? mhi : xhi;  // the down product reads the operands the gate/up product wrote
@@ -599,7 +600,7 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     ga.part = x.at<float>(x.L.part);  // short chunks split K (sized for every chunk up to max_prefill)
     // `first`: no operand split before it in its timing scope (the down product, or a product whose operands
     // the previous reduce wrote)
-    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true, first, nn));
+    return hip_rc(launch_gemm_tiled(epi, ga, x.s, true, first, nn, defer_ks));
   };
   auto norm_next = [&](const void *gain) {
     NormNext nn = {};
@@ -644,9 +645,11 @@ int run_prefill_pass(const Ctx &x, const int32_t *tokens, const PackSeg *segs, i
     {
       ProfScope ps(LLAMA_K_QKV, x.s);
       if (!x_split && (rc = split(xs, lw.ln1, H))) return rc;
+      // in K slices: the RoPE + append launch adds the partial sums itself (no reduce launch)
       if ((rc = gemm(EPI_STORE, lw.wq, lw.wk, lw.wv, H, H + KW, H + 2 * KW, H, qkv, qkv_stride, nullptr, false,
-                     kProdQkv, x_split)))
+                     kProdQkv, x_split, nullptr, &pa.ks)))
         return rc;
+      pa.part = pa.ks > 1 ? x.at<float>(x.L.part) : nullptr;
     }
     pa.kc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->k, l));
     pa.vc = reinterpret_cast<bf16_t *>(layer_cache(x, x.kv->v, l));

@@ -476,6 +476,11 @@ struct PrefillArgs {
   int seg_tile[kMaxSegments + 1];   // first query tile of each segment; seg_tile[nseg] = all tiles
   int seg_pos0[kMaxSegments];
   int seg_row[kMaxSegments];
+  // nullable: the q|k|v rows are still the product's K-slice partial sums, part[z][i][n] for z < ks
+  // (rows of qkv_stride numbers); the RoPE + append launch adds them in slice order first (the reduce the
+  // product would otherwise launch), writing only the rotated queries back to qkv
+  const float *part;
+  int ks;
 };
 
 // the segment holding packed index i of a sorted start list (start[0] = 0, n >= 1 entries)
@@ -571,9 +576,11 @@ struct NormNext {
   int ldo;
   bool done;
 };
-// first: the product's launch starts the profiling scope (no operand split launched before it)
+// first: the product's launch starts the profiling scope (no operand split launched before it).
+// defer_ks (EPI_STORE): when non-null and the product runs in K slices, no reduce is launched; *defer_ks
+// is the slice count (else 0) and the caller adds the partial sums itself (PrefillArgs::part)
 hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a, hipStream_t s, bool last, bool first = false,
-                             NormNext *nn = nullptr);
+                             NormNext *nn = nullptr, int *defer_ks = nullptr);
 hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last);
 // argmax of `rows` rows of per-block winners ([rows][ld], n valid per row) into next[rows]

@@ -536,13 +536,19 @@ size_t gemm_tiled_part_floats(int M, int N, int K, bool swiglu) {
   return ks > 1 ? (size_t)ks * M * (swiglu ? 2 * (size_t)N : (size_t)N) : 0;
 }
 
-hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last, bool first, NormNext *nn) {
+hipError_t launch_gemm_tiled(GemvEpi epi, const GemmArgs &a0, hipStream_t s, bool last, bool first, NormNext *nn,
+                             int *defer_ks) {
   if (a0.K % kTK != 0 || a0.M <= 0) return hipErrorInvalidValue;
   GemmArgs a = a0;
   if (nn) nn->done = false;
+  if (defer_ks) *defer_ks = 0;
   // the K slices' reduce: plain, or (residual in place) with the RMSNorm + operand split of the next product
   auto reduce = [&](auto epi_c, int ks) {
     constexpr int E = decltype(epi_c)::value;
+    if (E == EPI_STORE && defer_ks) {
+      *defer_ks = ks;
+      return;
+    }
     if (E == EPI_RESID && nn && a.y == a.res && a.ldy == a.ldres && a.N % 4 == 0) {
       RowsNormArgs r = {};
       r.part = a.part;
@@ -621,14 +627,25 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
   // outside the pool writes no key or value
   const int slot = a.table ? page_slot(a.table + (size_t)a.seg_row[sg] * a.pages, p, a.npages, a.status) : p;
   float *row = a.qkv + (size_t)i * a.qkv_stride;
+  // number n of this row: the product's output, or its K slices added in slice order (0 + p0 + p1 ...,
+  // the order k_tiled_reduce adds them in)
+  const size_t zs = (size_t)a.S * a.qkv_stride;
+  auto val = [&](int n) {
+    if (!a.part) return row[n];
+    const float *pp = a.part + (size_t)i * a.qkv_stride + n;
+    float v = 0.f;
+    for (int z = 0; z < a.ks; ++z) v += pp[z * zs];
+    return v;
+  };
   const float *cs = a.rope_cs + (size_t)p * half, *sn = a.rope_sn + (size_t)p * half;
   const int nq = a.heads * half, nk = a.kv * half;
   for (int k = threadIdx.x; k < nq + nk; k += kThreads) {
     const bool isq = k < nq;
     const int kk = isq ? k : k - nq;
     const int h = kk / half, d = kk - h * half;
-    float *src = isq ? row + h * D : row + a.heads * D + h * D;
-    const float lo = src[d], hi = src[d + half], c = cs[d], s = sn[d];
+    const int base = isq ? h * D : a.heads * D + h * D;
+    float *src = row + base;
+    const float lo = val(base + d), hi = val(base + d + half), c = cs[d], s = sn[d];
     const float nlo = rope_pair(lo, -hi, c, s), nhi = rope_pair(hi, lo, c, s);
     if (isq) {
       src[d] = nlo;
@@ -640,10 +657,10 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
     }
   }
   if (slot < 0) return;
-  const float *v = row + a.heads * D + a.kv * D;
+  const int v0 = a.heads * D + a.kv * D;
   for (int k = threadIdx.x; k < a.kv * D; k += kThreads) {
     const int h = k / D, d = k - h * D;
-    a.vc[((size_t)(crow * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(v[k]);
+    a.vc[((size_t)(crow * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(val(v0 + k));
   }
 }
 
