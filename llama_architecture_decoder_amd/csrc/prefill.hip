@@ -623,40 +623,61 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
   // outside the pool writes no key or value
   const int slot = a.table ? page_slot(a.table + (size_t)a.seg_row[sg] * a.pages, p, a.npages, a.status) : p;
   float *row = a.qkv + (size_t)i * a.qkv_stride;
-  // number n of this row: the product's output, or its K slices added in slice order (0 + p0 + p1 ...,
-  // the order k_tiled_reduce adds them in)
+  // numbers n .. n+3 of this row: the product's outputs, or its K slices added in slice order (0 + p0 +
+  // p1 ..., the order k_tiled_reduce adds them in)
   const size_t zs = (size_t)a.S * a.qkv_stride;
-  auto val = [&](int n) {
-    if (!a.part) return row[n];
+  auto val4 = [&](int n) {
+    if (!a.part) return *reinterpret_cast<const float4 *>(row + n);
     const float *pp = a.part + (size_t)i * a.qkv_stride + n;
-    float v = 0.f;
-    for (int z = 0; z < a.ks; ++z) v += pp[z * zs];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < a.ks; ++z) {
+      const float4 q = *reinterpret_cast<const float4 *>(pp + z * zs);
+      v.x += q.x;
+      v.y += q.y;
+      v.z += q.z;
+      v.w += q.w;
+    }
     return v;
   };
   const float *cs = a.rope_cs + (size_t)p * half, *sn = a.rope_sn + (size_t)p * half;
-  const int nq = a.heads * half, nk = a.kv * half;
+  // four pairs (d .. d+3 with d+half .. d+half+3) per thread: half is a multiple of 4
+  const int hq = half / 4, nq = a.heads * hq, nk = a.kv * hq;
   for (int k = threadIdx.x; k < nq + nk; k += kThreads) {
     const bool isq = k < nq;
     const int kk = isq ? k : k - nq;
-    const int h = kk / half, d = kk - h * half;
+    const int h = kk / hq, d = (kk - h * hq) * 4;
     const int base = isq ? h * D : a.heads * D + h * D;
-    float *src = row + base;
-    const float lo = val(base + d), hi = val(base + d + half), c = cs[d], s = sn[d];
-    const float nlo = rope_pair(lo, -hi, c, s), nhi = rope_pair(hi, lo, c, s);
+    const float4 lo4 = val4(base + d), hi4 = val4(base + d + half);
+    const float4 c4 = *reinterpret_cast<const float4 *>(cs + d), s4 = *reinterpret_cast<const float4 *>(sn + d);
+    const float lo[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, hi[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+    float nlo[4], nhi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nlo[e] = rope_pair(lo[e], -hi[e], c[e], sv[e]);
+      nhi[e] = rope_pair(hi[e], lo[e], c[e], sv[e]);
+    }
     if (isq) {
-      src[d] = nlo;
-      src[d + half] = nhi;
+      *reinterpret_cast<float4 *>(row + base + d) = make_float4(nlo[0], nlo[1], nlo[2], nlo[3]);
+      *reinterpret_cast<float4 *>(row + base + d + half) = make_float4(nhi[0], nhi[1], nhi[2], nhi[3]);
     } else if (slot >= 0) {
       bf16_t *kd = a.kc + ((size_t)(crow * a.kv + h) * a.max_seq + slot) * D;
-      kd[d] = f32_to_bf16(nlo);
-      kd[d + half] = f32_to_bf16(nhi);
+      *reinterpret_cast<uint2 *>(kd + d) =
+          make_uint2(f32_to_bf16(nlo[0]) | ((uint32_t)f32_to_bf16(nlo[1]) << 16),
+                     f32_to_bf16(nlo[2]) | ((uint32_t)f32_to_bf16(nlo[3]) << 16));
+      *reinterpret_cast<uint2 *>(kd + d + half) =
+          make_uint2(f32_to_bf16(nhi[0]) | ((uint32_t)f32_to_bf16(nhi[1]) << 16),
+                     f32_to_bf16(nhi[2]) | ((uint32_t)f32_to_bf16(nhi[3]) << 16));
     }
   }
   if (slot < 0) return;
   const int v0 = a.heads * D + a.kv * D;
-  for (int k = threadIdx.x; k < a.kv * D; k += kThreads) {
+  for (int k = 4 * threadIdx.x; k < a.kv * D; k += 4 * kThreads) {
     const int h = k / D, d = k - h * D;
-    a.vc[((size_t)(crow * a.kv + h) * a.max_seq + slot) * D + d] = f32_to_bf16(val(v0 + k));
+    const float4 v = val4(v0 + k);
+    *reinterpret_cast<uint2 *>(a.vc + ((size_t)(crow * a.kv + h) * a.max_seq + slot) * D + d) =
+        make_uint2(f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                   f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
   }
 }
 
