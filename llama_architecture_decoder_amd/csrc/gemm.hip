@@ -60,7 +60,23 @@ __global__ __launch_bounds__(kThreads) void k_split(SplitArgs a) {
     r = 1.0f / sqrtf(tot / (float)a.K + a.eps);
   }
   const GT *g = reinterpret_cast<const GT *>(a.gain);
-  // pairs of numbers (K is even): one packed conversion per pair
+  // four numbers per thread when K allows (16-byte loads), else pairs (K is even): one packed conversion
+  // per pair
+  if (a.K % 4 == 0 && a.ldin % 4 == 0 && a.ldx % 4 == 0) {
+    for (int k = 4 * tid; k < a.K; k += 4 * kThreads) {
+      const float4 v = *reinterpret_cast<const float4 *>(x + k);
+      float f[4] = {v.x, v.y, v.z, v.w};
+      if (NORM)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = load_scalar<GT>(g, k + e) * (f[e] * r);
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(f[0], f[1], h0, l0);
+      split_bf16x2(f[2], f[3], h1, l1);
+      *reinterpret_cast<uint2 *>(hi + k) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(lo + k) = make_uint2(l0, l1);
+    }
+    return;
+  }
   for (int k = 2 * tid; k < a.K; k += 2 * kThreads) {
     const float v0 = NORM ? load_scalar<GT>(g, k) * (x[k] * r) : x[k];
     const float v1 = NORM ? load_scalar<GT>(g, k + 1) * (x[k + 1] * r) : x[k + 1];
