@@ -728,6 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   const int q_row = r0 + min(q_i, len - 1);           // its packed row (tail lanes repeat the last)
   const int q_pos = pos0 + min(q_i, len - 1);         // its cache position
   const int last_pos = pos0 + min(qt * kQT + kQT - 1, len - 1);
+  const int first_pos = pos0 + qt * kQT;              // every lane's query is at or after it
   const bf16_t *Kh = a.kc + (size_t)(crow * a.kv + j) * a.max_seq * D;
   const bf16_t *Vh = a.vc + (size_t)(crow * a.kv + j) * a.max_seq * D;
 
@@ -831,34 +832,49 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
         }
       }
       float mt_max = -INFINITY;
+      // the causal mask only where the tile reaches past the block's first query
+      if (k0 + kKT - 1 <= first_pos) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
-          const float v = key <= q_pos ? s[mt][r] * sc : -INFINITY;
-          s[mt][r] = v;
-          mt_max = fmaxf(mt_max, v);
-        }
+          for (int r = 0; r < 16; ++r) {
+            s[mt][r] *= sc;
+            mt_max = fmaxf(mt_max, s[mt][r]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+            const float v = key <= q_pos ? s[mt][r] * sc : -INFINITY;
+            s[mt][r] = v;
+            mt_max = fmaxf(mt_max, v);
+          }
+      }
       mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32));
       const float m_new = fmaxf(m_run, mt_max);  // finite: key 0 is visible to every query
-      const float alpha = exp2f(m_run - m_new);
+      // 2^x as the hardware's exponential (results below 2^-126 flush to zero: against a sum >= 1)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float lsum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = exp2f(s[mt][r] - m_new);
+          const float pr = __builtin_amdgcn_exp2f(s[mt][r] - m_new);
           s[mt][r] = pr;
           lsum += pr;
         }
       lsum += __shfl_xor(lsum, 32);
       l_run = l_run * alpha + lsum;
+      // the accumulators change only where the maximum grew (elsewhere alpha is exactly 1)
+      if (!__all(m_new == m_run)) {
+#pragma unroll
+        for (int t = 0; t < F::DT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
       m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < F::DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
       // O^T += V^T P^T over the tile's 4 groups of 16 keys
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
