@@ -821,15 +821,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
       // scores S^T for keys k0 + 32 mt + (8(r/4) + 4 hsel + r%4), query q_i
       f32x16 s[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < F::KS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4 *>(&s_k[buf][(mt * 32 + l32) * F::KROW + ks * 16 + hsel * 8]);
-          s[mt] = mfma32(kf, qh[ks], s[mt]);
-          s[mt] = mfma32(kf, ql[ks], s[mt]);
-        }
+      for (int ks = 0; ks < F::KS; ++ks) {
+        u32x4 kf[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          kf[mt] = *reinterpret_cast<const u32x4 *>(&s_k[buf][(mt * 32 + l32) * F::KROW + ks * 16 + hsel * 8]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(kf[mt], qh[ks], s[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(kf[mt], ql[ks], s[mt]);
       }
       float mt_max = -INFINITY;
       // the causal mask only where the tile reaches past the block's first query
@@ -885,15 +889,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
         const u32x4 pfh = u32x4{ph[0], ph[1], ph[2], ph[3]}, pfl = u32x4{pl[0], pl[1], pl[2], pl[3]};
         // keys of slot e of half hsel within the 16-group: 8(e/4) + 4 hsel + e%4
         const int kb = kk * 16 + 4 * hsel;
+        u32x4 vf[F::DT];
 #pragma unroll
         for (int t = 0; t < F::DT; ++t) {
           const bf16_t *vr = &s_vt[buf][(t * 32 + l32) * F::VROW + kb];
           const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(vr);
           const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(vr + 8);
-          const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
-          o[t] = mfma32(vf, pfh, o[t]);
-          o[t] = mfma32(vf, pfl, o[t]);
+          vf[t] = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
         }
+#pragma unroll
+        for (int t = 0; t < F::DT; ++t) o[t] = mfma32(vf[t], pfh, o[t]);
+#pragma unroll
+        for (int t = 0; t < F::DT; ++t) o[t] = mfma32(vf[t], pfl, o[t]);
       }
     }
     // the other buffer was last read in the previous tile, before the previous barrier
