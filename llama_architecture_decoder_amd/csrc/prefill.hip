@@ -765,6 +765,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   constexpr int KPT = (KCH + kThreads - 1) / kThreads;
   constexpr int VCH = (kKT / 4) * (D / 8);    // (4 keys x 8 numbers) pieces of the V tile
   u32x4 kreg[KPT], vreg[4];
+  // the V piece of this thread: 8 lanes read 128 contiguous bytes of a key row, and a wavefront covers 8
+  // d-chunks x 8 key quads, so the stash's transposed 8-byte writes of one instruction fall in 16
+  // distinct bank pairs (conflict-free)
+  const int v_dc = lane % 8 + 8 * (wave % (D / 64)), v_kq = lane / 8 + 8 * (wave / (D / 64));
+  static_assert(VCH == kKT / 4 * D / 8 && D % 64 == 0, "8 x 8 pieces per wavefront");
   // paged cache: a tile's positions k0 .. k0+63 (k0 a multiple of the page size, clamped to last_pos)
   // lie in one page
   static_assert(kKT == kPageSize, "a key tile is one page");
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
       }
     }
     if (tid < VCH) {
-      const int dc = tid % (D / 8), kq = tid / (D / 8);
+      const int dc = v_dc, kq = v_kq;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         vreg[u] = load16(Vh + (size_t)(base + min(k0 + 4 * kq + u, last_pos) - k0) * D + dc * 8);
@@ -800,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
     }
     // V: this thread's 4 consecutive keys x 8 consecutive numbers go to 8 rows of 4 keys of V^T
     if (tid < VCH) {
-      const int dc = tid % (D / 8), kq = tid / (D / 8);
+      const int dc = v_dc, kq = v_kq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1, sh = (e & 1) * 16;
