@@ -808,10 +808,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
       const int dc = v_dc, kq = v_kq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        const uint32_t b0 = (vreg[0][w] >> sh) & 0xffffu, b1 = (vreg[1][w] >> sh) & 0xffffu;
-        const uint32_t b2 = (vreg[2][w] >> sh) & 0xffffu, b3 = (vreg[3][w] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2 *>(&s_vt[buf][(dc * 8 + e) * F::VROW + 4 * kq]) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+        // number e of keys 0 and 1 (2 and 3) as one word: bytes 0-1 or 2-3 of each (v_perm_b32)
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t p01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
+        *reinterpret_cast<u32x2 *>(&s_vt[buf][(dc * 8 + e) * F::VROW + 4 * kq]) = u32x2{p01, p23};
       }
     }
   };
