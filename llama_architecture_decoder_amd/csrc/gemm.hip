@@ -407,7 +407,11 @@ __global__ __launch_bounds__(kNormThreads) void k_rows_reduce_norm(RowsNormArgs 
   for (int n = 4 * tid; n < a.N; n += 4 * kNormThreads) {
     const float4 r = *reinterpret_cast<const float4 *>(x + n);  // the residual stream
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < a.S; s0 += 8) {
+    if (a.S == 2) {  // the usual split: both partials, no clamped repeats
+      const float4 p0 = *reinterpret_cast<const float4 *>(pp + n), p1 = *reinterpret_cast<const float4 *>(pp + sstride + n);
+      acc = make_float4((acc.x + p0.x) + p1.x, (acc.y + p0.y) + p1.y, (acc.z + p0.z) + p1.z, (acc.w + p0.w) + p1.w);
+    }
+    for (int s0 = 0; s0 < a.S && a.S != 2; s0 += 8) {
       float4 p[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
