@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
 // 64 positions:
 //   S^T[key][q] = K Q^T (K from LDS as the A operand, the wave's rotated queries as bf16 hi + lo B
 //   fragments held in registers), so each lane owns one query column: 32 of the tile's 64 scores, the
-//   other 32 in lane ^ 32.  Softmax with a running maximum in base 2 (scores times scale * log2(e)).
+//   other 32 in lane ^ 32.  Softmax with a running maximum in base 2 (the queries carry scale * log2(e)).
 //   O^T[d][q] += V^T P^T: P^T is the score accumulator itself, split into bf16 hi + lo; the 16 keys a
 //   B fragment covers are taken in the order the accumulator holds them (a sum does not care), and
 //   V^T fragments are read from an LDS copy of V stored transposed, in the same key order.
@@ -732,6 +732,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   const bf16_t *Kh = a.kc + (size_t)(crow * a.kv + j) * a.max_seq * D;
   const bf16_t *Vh = a.vc + (size_t)(crow * a.kv + j) * a.max_seq * D;
 
+  const float sc = a.scale * 1.4426950408889634f;
   // the wave's rotated queries as B fragments: lane holds q[q_i][16 ks + 8 hsel .. +8], hi and lo
   u32x4 qh[F::KS], ql[F::KS];
   {
@@ -740,7 +741,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
     for (int ks = 0; ks < F::KS; ++ks) {
       const float4 v0 = *reinterpret_cast<const float4 *>(q + ks * 16 + hsel * 8);
       const float4 v1 = *reinterpret_cast<const float4 *>(q + ks * 16 + hsel * 8 + 4);
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      // the query times scale * log2(e), so the products are the base-2 softmax's exponents
+      const float f[8] = {v0.x * sc, v0.y * sc, v0.z * sc, v0.w * sc, v1.x * sc, v1.y * sc, v1.z * sc, v1.w * sc};
       uint32_t h4[4], l4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) split_bf16x2(f[2 * e], f[2 * e + 1], h4[e], l4[e]);
@@ -755,7 +757,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float sc = a.scale * 1.4426950408889634f;
 
   const int ntiles = last_pos / kKT + 1;
   // K (row-major) and V (transposed) of positions k0 .. k0+63 (past last_pos: clamped, masked): the next
@@ -849,7 +850,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            s[mt][r] *= sc;
             mt_max = fmaxf(mt_max, s[mt][r]);
           }
       } else {
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
-            const float v = key <= q_pos ? s[mt][r] * sc : -INFINITY;
+            const float v = key <= q_pos ? s[mt][r] : -INFINITY;
             s[mt][r] = v;
             mt_max = fmaxf(mt_max, v);
           }
