@@ -828,6 +828,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
     if (active) {
       // scores S^T for keys k0 + 32 mt + (8(r/4) + 4 hsel + r%4), query q_i
       f32x16 s[2];
+      // the matrix-core phases at a raised wave priority, so the other block's wavefront on this SIMD
+      // fills the softmax phases (8-layer 4096-position prefill 27.42 -> 27.21 ms)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -843,6 +846,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(kf[mt], ql[ks], s[mt]);
       }
+      __builtin_amdgcn_s_setprio(0);
       float mt_max = -INFINITY;
       // the causal mask only where the tile reaches past the block's first query
       if (k0 + kKT - 1 <= first_pos) {
@@ -887,6 +891,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
       }
       m_run = m_new;
       // O^T += V^T P^T over the tile's 4 groups of 16 keys
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int mt = kk >> 1, r0 = (kk & 1) * 8;
@@ -911,6 +916,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
       }
     }
     // the other buffer was last read in the previous tile, before the previous barrier
+    __builtin_amdgcn_s_setprio(0);
     if (tile + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
   }
