@@ -713,14 +713,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // query tile: the tiles of the segments in order (each segment's own tiles of kQT positions, the last
   // one ragged), taken from the end so that the longest tiles start first
-  const int tile_id = (int)gridDim.x - 1 - (int)blockIdx.x;
+  // block b: kv head b % kv, head quarter and query tile from b / kv.  Consecutive blocks go to
+  // consecutive XCDs, so with 8 kv heads each XCD runs one head's tiles and its L2 keeps that head's keys
+  // and values
+  const int zq = (a.g + 3) / 4, nq_tiles = a.seg_tile[a.nseg];
+  const int j = (int)blockIdx.x % a.kv, rest = (int)blockIdx.x / a.kv;
+  const int zz = rest % zq;
+  const int tile_id = nq_tiles - 1 - rest / zq;
   const int sg = segment_of(a.seg_tile, a.nseg, tile_id);
   const int qt = tile_id - a.seg_tile[sg];
   const int r0 = a.seg_start[sg], len = a.seg_start[sg + 1] - r0, pos0 = a.seg_pos0[sg];
   const int crow = a.table ? 0 : a.seg_row[sg];
   const int32_t *tr = a.table ? a.table + (size_t)a.seg_row[sg] * a.pages : nullptr;
-  const int j = blockIdx.y;
-  const int hi_in_group = blockIdx.z * 4 + wave;
+  const int hi_in_group = zz * 4 + wave;
   const bool active = hi_in_group < a.g;
   const int head = j * a.g + (active ? hi_in_group : 0);
   const int l32 = lane & 31, hsel = lane >> 5;
@@ -939,7 +944,7 @@ hipError_t launch_rope_rows(const PrefillArgs &a, hipStream_t s, bool first, boo
 
 hipError_t launch_attn_prefill(const PrefillArgs &a, hipStream_t s, bool first, bool last) {
   if (a.nseg < 1 || a.nseg > kMaxSegments || a.seg_start[a.nseg] != a.S) return hipErrorInvalidValue;
-  const dim3 g(a.seg_tile[a.nseg], a.kv, (a.g + 3) / 4);
+  const dim3 g(a.seg_tile[a.nseg] * a.kv * ((a.g + 3) / 4));
   if (a.half == 64)
     launch(k_attn_prefill<128>, g, dim3(kThreads), s, first, last, a);
   else if (a.half == 32)
