@@ -682,7 +682,8 @@ __global__ __launch_bounds__(kThreads) void k_rope_rows(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ causal attention ----
-// Block (query tile of 32 consecutive positions of one segment, kv head j, head quarter z): wave w takes
+// Block (query tile of 32 consecutive positions of one segment, kv head j, head quarter z; the order is
+// below): wave w takes
 // query head j*g + 4z + w (idle when that is >= g; it still helps stage the tiles); the keys are the
 // segment's request's positions 0 .. the query's own, from its cache row or its pages.  Per key tile of
 // 64 positions:
@@ -711,11 +712,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_prefill(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t s_k[2][kKT * F::KROW];   // double buffered
   __shared__ __attribute__((aligned(16))) bf16_t s_vt[2][D * F::VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // query tile: the tiles of the segments in order (each segment's own tiles of kQT positions, the last
-  // one ragged), taken from the end so that the longest tiles start first
-  // block b: kv head b % kv, head quarter and query tile from b / kv.  Consecutive blocks go to
-  // consecutive XCDs, so with 8 kv heads each XCD runs one head's tiles and its L2 keeps that head's keys
-  // and values
+  // block b: kv head b % kv, then head quarter and query tile from b / kv.  Query tiles are the
+  // segments' own tiles of kQT positions in order (the last of each ragged), taken from the end so that
+  // the longest start first.  Consecutive blocks go to consecutive XCDs, so with 8 kv heads each XCD runs
+  // one head's tiles and its L2 keeps that head's keys and values.
   const int zq = (a.g + 3) / 4, nq_tiles = a.seg_tile[a.nseg];
   const int j = (int)blockIdx.x % a.kv, rest = (int)blockIdx.x / a.kv;
   const int zz = rest % zq;
